@@ -1,0 +1,212 @@
+"""Throughput of blockwise causal GQA attention (forward + backward) on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+the device promise check, the forward kernel (O, LSE), then the backward
+(promise check, dO.O pre-pass, dK/dV with the first contribution stored, dQ).
+Default workload: one context-parallel rank's share at B64/S8192/Hq32/Hkv8/D256,
+chunks 0 and 15 of 16 per sequence (65536 query rows against 524288 K/V rows).
+
+Prints one JSON line.  `value` is causal TFLOP/s with FLOP = 14 * D per visible
+(query, key) pair per query head (forward 4D, backward 10D), inputs resident in
+HBM.  `roofline` reports the dominant kernel, timed with HIP events on the
+stream it runs on; `cpu_baseline` times the FP64 oracle on a bounded sample of
+the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention fwd+bwd TFLOP/s (causal) and % of BF16 MFMA peak, 1 MI355X"
+
+
+def visible_pairs(seq_lens, chunks, causal) -> int:
+    """Visible (query, key) pairs per query head (closed form per chunk)."""
+    tot = 0
+    for s, _, p0, n in chunks:
+        L = int(seq_lens[s])
+        p0, n = int(p0), int(n)
+        if causal:
+            # sum over p in [p0, p0+n) of min(p+1, L); p < L always holds
+            tot += n * (p0 + 1) + n * (n - 1) // 2
+        else:
+            tot += n * L
+    return tot
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, do, bias, budget_s):
+    """The FP64 oracle, as it stands, on whole (sequence, KV-head group) samples."""
+    import oracle
+    import workloads as W
+    from threadpoolctl import threadpool_info
+    import torch
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    G = w.hq // w.hkv
+    order = [(b, g) for b in range(w.num_seqs) for g in range(w.hkv)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    done_flop, t_used, samples = 0, 0.0, []
+    for b, g in order:
+        sub, qi, ki = W.subset(w, seqs={b})
+        tq = torch.from_numpy(qi).cuda()
+        tk = torch.from_numpy(ki).cuda()
+        f64 = lambda t, idx: t.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+        qs, dos = f64(q, tq), f64(do, tq)
+        ks, vs = f64(k, tk), f64(v, tk)
+        bs = None if bias is None else bias.cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.attention(qs, ks, vs, sub.seq_offsets, sub.seq_lens, sub.chunks, w.causal, w.scale,
+                         bias=bs, do=dos, select=(None, {g}))
+        t_used += time.perf_counter() - t0
+        done_flop += visible_pairs(sub.seq_lens, sub.chunks, w.causal) * G * 14 * w.head_dim
+        samples.append((b, g))
+        if t_used >= budget_s:
+            break
+    return {
+        "value": done_flop / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"FP64 NumPy oracle fwd+bwd on {len(samples)} (sequence, KV-head group) pairs "
+                  f"{samples[:4]}{'...' if len(samples) > 4 else ''}: {done_flop:.3e} FLOP in {t_used:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is designed, not built)"}))
+        sys.exit(2)
+    import torch
+    import context_causal_gqa_cpattn_amd as cp
+    import workloads as W
+
+    cp.load()
+    w = W.make_config(args.config, materialize=False)
+    q, k, v, do, bias = W.draw_on_device(w, 2000 + args.config)
+    lay = cp.make_layout(w.seq_offsets, w.seq_lens, w.chunks, "cuda",
+                         max_chunk_len=w.max_chunk_len, max_kv_len=w.max_kv_len)
+    prob = cp.problem(lay, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal, w.scale,
+                      w.bias_len)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.q_rows), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dbias = torch.empty_like(bias) if bias is not None else None
+    ws = torch.empty(max(cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
+    delta = ws[: w.hq * w.q_rows * 4].view(torch.float32)
+    err = cp.new_dev_err()
+
+    names = ["fwd", "validate", "prepass", "dkdv", "dq"] + (["dbias"] if bias is not None else [])
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        cp.fwd(q, k, v, lay, causal=w.causal, scale=w.scale, bias=bias, o=o, lse=lse, dev_err=err)
+        mark(1)
+        cp.validate(prob, lay, err)
+        mark(2)
+        cp.bwd_prepass(prob, lay, o, do, delta, err)
+        mark(3)
+        cp.bwd_dkdv(prob, lay, q, k, v, bias, lse, do, delta, dk, dv, False, err)
+        mark(4)
+        cp.bwd_dq(prob, lay, q, k, v, bias, lse, do, delta, dq, err)
+        mark(5)
+        if bias is not None:
+            cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, dbias, ws, err)
+            mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cp.check(err)
+
+    n_ev = len(names) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cp.check(err)
+    per_kernel = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
+                                     for i in range(args.steps)])) for j, n in enumerate(names)}
+    ms = wall * 1e3 / args.steps
+
+    pairs = visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq
+    D = w.head_dim
+    flop = pairs * 14 * D
+    tflops = flop / (ms * 1e-3) / 1e12
+    fwd_tflops = pairs * 4 * D / (per_kernel["fwd"] * 1e-3) / 1e12
+    bwd_ms = sum(per_kernel[n] for n in names[1:])
+    bwd_tflops = pairs * 10 * D / (bwd_ms * 1e-3) / 1e12
+    # dominant kernel: the longest one; its algorithmic FLOP per launch
+    algo = {"fwd": 4 * D, "dkdv": 8 * D, "dq": 2 * D}
+    dom = max((n for n in per_kernel if n in algo), key=lambda n: per_kernel[n])
+    dom_flop = pairs * algo[dom]
+    achieved = dom_flop / (per_kernel[dom] * 1e-3) / 1e12
+    pre_bytes = 2 * w.q_valid_rows().sum() * w.hq * D * 2 + 4 * w.q_valid_rows().sum() * w.hq
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) BF16 drawn on the device, seeded",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "seq_len": int(w.seq_lens.max()),
+                   "q_rows": w.q_rows, "kv_rows": w.kv_rows, "hq": w.hq, "hkv": w.hkv,
+                   "head_dim": D, "causal": bool(w.causal), "chunks": w.num_chunks,
+                   "flop_per_step": flop, "parallelism": "none (one GPU: one rank's share)"},
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "kernel_ms": {n: round(x, 4) for n, x in per_kernel.items()},
+        "prepass_gbs": round(pre_bytes / (per_kernel["prepass"] * 1e-3) / 1e9, 1),
+        "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": dom_flop},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, do, bias, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

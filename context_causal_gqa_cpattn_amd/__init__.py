@@ -1,0 +1,339 @@
+"""Python binding of the cpattn C-ABI (libcpattn.so, gfx950).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind include/cpattn.h.  PyTorch provides device memory and the current
+stream.  There is no fallback: if the library or a GPU is missing, calls raise.
+
+Names follow the C entry points: fwd, bwd, bwd_prepass, bwd_dkdv, bwd_dq,
+bwd_dbias, validate, pack, unpack.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcpattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+OP_FWD, OP_BWD = 0, 1
+DEV_ERR_BITS = {
+    0x01: "ESEQ_LEN", 0x02: "ESEQ_RANGE", 0x04: "ECHUNK_SEQ", 0x08: "ECHUNK_ROWS",
+    0x10: "ECHUNK_POS", 0x20: "EBIAS", 0x40: "ELAYOUT",
+}
+EXPORTS = [
+    "cpattn_status_str", "cpattn_last_error", "cpattn_version", "cpattn_workspace_size",
+    "cpattn_validate", "cpattn_fwd", "cpattn_bwd", "cpattn_bwd_prepass", "cpattn_bwd_dkdv",
+    "cpattn_bwd_dq", "cpattn_bwd_dbias", "cpattn_pack", "cpattn_unpack",
+]
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class DeviceError(RuntimeError):
+    def __init__(self, bits: int):
+        names = [n for b, n in DEV_ERR_BITS.items() if bits & b]
+        super().__init__(f"device promise check failed: 0x{bits:x} {names}")
+        self.bits = bits
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64),
+        ("num_chunks", ctypes.c_int32), ("max_chunk_len", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("bias_len", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libcpattn.so (built in-tree by build.py).  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(f"{p} not found: build it with `python -m context_causal_gqa_cpattn_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.cpattn_status_str.restype = ctypes.c_char_p
+    lib.cpattn_status_str.argtypes = [ctypes.c_int]
+    lib.cpattn_last_error.restype = ctypes.c_char_p
+    lib.cpattn_last_error.argtypes = []
+    lib.cpattn_version.restype = ctypes.c_int
+    lib.cpattn_workspace_size.restype = ctypes.c_size_t
+    lib.cpattn_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.c_int]
+    P = ctypes.POINTER(Problem)
+    i64, i32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sigs = {
+        "cpattn_validate": [P, _vp, _vp, _vp, _vp, _vp],
+        "cpattn_fwd": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
+        "cpattn_bwd": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                       ctypes.c_int, _vp, sz, _vp, _vp],
+        "cpattn_bwd_prepass": [P, _vp, _vp, _vp, _vp, _vp, _vp],
+        "cpattn_bwd_dkdv": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            ctypes.c_int, _vp, _vp],
+        "cpattn_bwd_dq": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+        "cpattn_bwd_dbias": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
+        "cpattn_pack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
+        "cpattn_unpack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
+    }
+    for name, args in sigs.items():
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != OK:
+        lib = load()
+        raise CpattnError(status, f"{lib.cpattn_status_str(status).decode()}: "
+                                  f"{lib.cpattn_last_error().decode()}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtype, shape=None):
+    torch = _torch()
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+@dataclasses.dataclass
+class Layout:
+    """Sequence and chunk descriptors on the device plus their host-side bounds."""
+    seq_offsets: object   # int32 [B] on the GPU
+    seq_lens: object      # int32 [B]
+    chunks: object        # int32 [C, 4]
+    num_seqs: int
+    num_chunks: int
+    max_chunk_len: int
+    max_kv_len: int
+
+
+def make_layout(seq_offsets: Sequence[int], seq_lens: Sequence[int], chunks, device="cuda",
+                max_chunk_len: Optional[int] = None, max_kv_len: Optional[int] = None) -> Layout:
+    torch = _torch()
+    so = np.ascontiguousarray(seq_offsets, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    ch = np.ascontiguousarray(chunks, dtype=np.int32).reshape(-1, 4)
+    mcl = int(ch[:, 3].max()) if len(ch) and max_chunk_len is None else (max_chunk_len or 0)
+    mkl = int(sl.max()) if len(sl) and max_kv_len is None else (max_kv_len or 0)
+    return Layout(torch.from_numpy(so).to(device), torch.from_numpy(sl).to(device),
+                  torch.from_numpy(ch).to(device), len(so), len(ch), max(mcl, 0), max(mkl, 0))
+
+
+def problem(layout: Layout, q_rows: int, kv_rows: int, hq: int, hkv: int, head_dim: int,
+            causal: bool = True, scale: Optional[float] = None, bias_len: int = 0) -> Problem:
+    return Problem(layout.num_seqs, hq, hkv, head_dim, q_rows, kv_rows, layout.num_chunks,
+                   layout.max_chunk_len, layout.max_kv_len, 1 if causal else 0,
+                   (1.0 / math.sqrt(head_dim)) if scale is None else float(scale), bias_len)
+
+
+def new_dev_err(device="cuda"):
+    return _torch().zeros(1, dtype=_torch().int32, device=device)
+
+
+def check(dev_err) -> None:
+    """Synchronize on the error word and raise DeviceError if a promise was broken."""
+    bits = int(dev_err.item())
+    if bits:
+        raise DeviceError(bits)
+
+
+def workspace_size(prob: Problem, op: int) -> int:
+    return int(load().cpattn_workspace_size(ctypes.byref(prob), op))
+
+
+def _shapes(q, k, v):
+    q_rows, hq, D = q.shape
+    kv_rows, hkv, D2 = k.shape
+    if D2 != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q/k/v head dims or k/v shapes disagree")
+    return q_rows, hq, kv_rows, hkv, D
+
+
+def _prob_for(q, k, v, layout, causal, scale, bias):
+    torch = _torch()
+    q_rows, hq, kv_rows, hkv, D = _shapes(q, k, v)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, n, torch.bfloat16)
+    bias_len = 0
+    if bias is not None:
+        _need(bias, "bias", torch.float32)
+        if bias.dim() != 3 or bias.shape[0] != hq or bias.shape[1] != bias.shape[2]:
+            raise ValueError("bias must be [hq, bias_len, bias_len]")
+        bias_len = int(bias.shape[1])
+    return problem(layout, q_rows, kv_rows, hq, hkv, D, causal, scale, bias_len)
+
+
+def validate(prob: Problem, layout: Layout, dev_err, stream=None):
+    lib = load()
+    _check(lib.cpattn_validate(ctypes.byref(prob), _ptr(layout.seq_offsets), _ptr(layout.seq_lens),
+                               _ptr(layout.chunks), _ptr(dev_err), _stream(stream)))
+
+
+def fwd(q, k, v, layout: Layout, causal: bool = True, scale: Optional[float] = None, bias=None,
+        o=None, lse=None, dev_err=None, stream=None):
+    """O [q_rows, hq, D] bf16 and LSE [hq, q_rows] fp32 (chunk rows written only)."""
+    torch = _torch()
+    lib = load()
+    prob = _prob_for(q, k, v, layout, causal, scale, bias)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((prob.hq, prob.q_rows), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (prob.hq, prob.q_rows))
+    if dev_err is None:
+        dev_err = new_dev_err(q.device)
+    _check(lib.cpattn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                          _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(o), _ptr(lse),
+                          None, 0, _ptr(dev_err), _stream(stream)))
+    return o, lse, dev_err
+
+
+def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optional[float] = None,
+        bias=None, dq=None, dk=None, dv=None, dkv_accumulate: bool = False, want_dbias: bool = True,
+        dbias=None, ws=None, dev_err=None, stream=None):
+    """dQ, dK, dV (bf16) and dBias (fp32, when a bias is given)."""
+    torch = _torch()
+    lib = load()
+    prob = _prob_for(q, k, v, layout, causal, scale, bias)
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(do, "do", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (prob.hq, prob.q_rows))
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        if dkv_accumulate:
+            raise ValueError("dkv_accumulate needs existing dk/dv")
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _need(t, n, torch.bfloat16, ref.shape)
+    if bias is not None and want_dbias and dbias is None:
+        dbias = torch.empty_like(bias)
+    need = workspace_size(prob, OP_BWD)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if dev_err is None:
+        dev_err = new_dev_err(q.device)
+    _check(lib.cpattn_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                          _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(o), _ptr(lse),
+                          _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
+                          1 if dkv_accumulate else 0, _ptr(ws), ws.numel(), _ptr(dev_err),
+                          _stream(stream)))
+    return dq, dk, dv, dbias, dev_err
+
+
+def bwd_prepass(prob: Problem, layout: Layout, o, do, delta, dev_err, stream=None):
+    lib = load()
+    _check(lib.cpattn_bwd_prepass(ctypes.byref(prob), _ptr(layout.chunks), _ptr(o), _ptr(do),
+                                  _ptr(delta), _ptr(dev_err), _stream(stream)))
+
+
+def bwd_dkdv(prob: Problem, layout: Layout, q, k, v, bias, lse, do, delta, dk, dv,
+             dkv_accumulate: bool, dev_err, stream=None):
+    lib = load()
+    _check(lib.cpattn_bwd_dkdv(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                               _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
+                               _ptr(do), _ptr(delta), _ptr(dk), _ptr(dv), 1 if dkv_accumulate else 0,
+                               _ptr(dev_err), _stream(stream)))
+
+
+def bwd_dq(prob: Problem, layout: Layout, q, k, v, bias, lse, do, delta, dq, dev_err, stream=None):
+    lib = load()
+    _check(lib.cpattn_bwd_dq(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                             _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
+                             _ptr(do), _ptr(delta), _ptr(dq), _ptr(dev_err), _stream(stream)))
+
+
+def bwd_dbias(prob: Problem, layout: Layout, q, k, v, bias, lse, do, dbias, ws, dev_err, stream=None):
+    lib = load()
+    _check(lib.cpattn_bwd_dbias(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                                _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
+                                _ptr(do), _ptr(dbias), _ptr(ws), ws.numel(), _ptr(dev_err),
+                                _stream(stream)))
+
+
+def pack(bhsd, seq_offsets, seq_lens, thd_rows: int, thd=None, dev_err=None, stream=None):
+    """THD [thd_rows, H, D] from BHSD [B, H, S_pitch, D]; only valid rows are written."""
+    torch = _torch()
+    lib = load()
+    _need(bhsd, "bhsd", torch.bfloat16)
+    B, H, S, D = bhsd.shape
+    if thd is None:
+        thd = torch.empty((thd_rows, H, D), dtype=torch.bfloat16, device=bhsd.device)
+    _need(thd, "thd", torch.bfloat16, (thd_rows, H, D))
+    if dev_err is None:
+        dev_err = new_dev_err(bhsd.device)
+    _check(lib.cpattn_pack(_ptr(bhsd), _ptr(thd), B, H, S, D, thd_rows, _ptr(seq_offsets),
+                           _ptr(seq_lens), _ptr(dev_err), _stream(stream)))
+    return thd, dev_err
+
+
+def unpack(thd, seq_offsets, seq_lens, B: int, S_pitch: int, bhsd=None, dev_err=None, stream=None):
+    """BHSD [B, H, S_pitch, D] from THD [thd_rows, H, D]; only valid rows are written."""
+    torch = _torch()
+    lib = load()
+    _need(thd, "thd", torch.bfloat16)
+    thd_rows, H, D = thd.shape
+    if bhsd is None:
+        bhsd = torch.empty((B, H, S_pitch, D), dtype=torch.bfloat16, device=thd.device)
+    _need(bhsd, "bhsd", torch.bfloat16, (B, H, S_pitch, D))
+    if dev_err is None:
+        dev_err = new_dev_err(thd.device)
+    _check(lib.cpattn_unpack(_ptr(thd), _ptr(bhsd), B, H, S_pitch, D, thd_rows, _ptr(seq_offsets),
+                             _ptr(seq_lens), _ptr(dev_err), _stream(stream)))
+    return bhsd, dev_err
+
+
+# ---------------------------------------------------------------- host <-> device helpers
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    """BF16 bit patterns (uint16 numpy) -> torch.bfloat16 device tensor, bit-exact."""
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_host_bits(t) -> np.ndarray:
+    """torch.bfloat16 tensor -> uint16 numpy bit patterns."""
+    torch = _torch()
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,559 @@
+// C-ABI of the cpattn library: host-side argument checks, the pointer-alias audit,
+// grid sizing and kernel dispatch.  Every entry point enqueues on the caller's stream
+// and returns without synchronizing.
+//
+// Page "Optimize context parallel attention layouts and gradient accumulation":
+// "Changes" (promise checked on the device, explicit contract instead of private
+// switches as asked under "Remaining before ready"), "CP8 AllGather: composition
+// with first-gradient reuse" (pointer-alias audits outside the timed region).
+// Page on the ws2 tensor/sequence/context-parallel block ("Scope / Known
+// limitations"): unsupported shapes and dtypes raise instead of falling back.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/cpattn.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace cpattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CPATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return CPATTN_OK;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+  bool output;
+};
+
+// Every output range must be disjoint from every other range.
+int alias_audit(const std::vector<Range>& rs) {
+  for (size_t i = 0; i < rs.size(); ++i) {
+    if (!rs[i].output || rs[i].lo == rs[i].hi) continue;
+    for (size_t j = 0; j < rs.size(); ++j) {
+      if (i == j || rs[j].lo == rs[j].hi) continue;
+      if (rs[j].output && j < i) continue;  // output pairs checked once
+      if (rs[i].lo < rs[j].hi && rs[j].lo < rs[i].hi)
+        return fail(CPATTN_EINVAL, "pointer alias: output %s overlaps %s %s", rs[i].name,
+                    rs[j].output ? "output" : "input", rs[j].name);
+    }
+  }
+  return CPATTN_OK;
+}
+
+Range rng(const char* name, const void* p, uint64_t bytes, bool out) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + bytes : lo, out};
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_ptr(const void* p, uint64_t bytes, size_t align, const char* name) {
+  if (bytes == 0) return CPATTN_OK;
+  if (!p) return fail(CPATTN_EINVAL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(CPATTN_EINVAL, "%s is not %zu-byte aligned", name, align);
+  return CPATTN_OK;
+}
+
+constexpr int64_t kGridMax = 0x7fffffff;
+
+struct Plan {
+  int D, G, hpw;
+  bool bias;
+  int64_t q_bytes, kv_bytes, stat_bytes, bias_bytes;
+  int64_t delta_bytes;  // rounded to 256
+  int parts;            // dBias partitions
+  int64_t partial_bytes;
+  dim3 grid_fwd, grid_prepass, grid_dkdv, grid_dbias;
+  int bpc_fwd, bpc_prepass, kv_tiles;
+};
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int make_plan(const cpattn_problem* p, Plan& pl) {
+  if (!p) return fail(CPATTN_EINVAL, "problem is NULL");
+  if (p->num_seqs < 0 || p->num_chunks < 0 || p->q_rows < 0 || p->kv_rows < 0 ||
+      p->max_chunk_len < 0 || p->max_kv_len < 0 || p->bias_len < 0)
+    return fail(CPATTN_EINVAL, "negative size in problem");
+  if (p->hq <= 0 || p->hkv <= 0) return fail(CPATTN_EINVAL, "hq and hkv must be positive");
+  if (p->hq % p->hkv) return fail(CPATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", p->hq, p->hkv);
+  if (!std::isfinite(p->scale)) return fail(CPATTN_EINVAL, "scale is not finite");
+  if (p->causal != 0 && p->causal != 1) return fail(CPATTN_EINVAL, "causal must be 0 or 1");
+  const int D = p->head_dim;
+  pl.bias = p->bias_len > 0;
+  if (pl.bias) {
+    if (p->causal) return fail(CPATTN_EUNSUPPORTED, "a pair bias is supported without causal masking only");
+    if (D != 32 && D != 64 && D != 128)
+      return fail(CPATTN_EUNSUPPORTED, "head_dim %d unsupported with a bias (32, 64, 128)", D);
+  } else if (D != 32 && D != 64 && D != 128 && D != 256) {
+    return fail(CPATTN_EUNSUPPORTED, "head_dim %d unsupported (32, 64, 128, 256)", D);
+  }
+  if (p->max_chunk_len > (1 << 30) || p->max_kv_len > (1 << 30) || p->bias_len > (1 << 20))
+    return fail(CPATTN_EUNSUPPORTED, "length bound too large");
+  if (p->q_rows > (int64_t(1) << 31) || p->kv_rows > (int64_t(1) << 31))
+    return fail(CPATTN_EUNSUPPORTED, "row count exceeds 2^31 (chunk map rows are int32)");
+  pl.D = D;
+  pl.G = p->hq / p->hkv;
+  pl.hpw = (pl.G % 4 == 0) ? 4 : (pl.G % 2 == 0) ? 2 : 1;
+  pl.q_bytes = p->q_rows * p->hq * (int64_t)D * 2;
+  pl.kv_bytes = p->kv_rows * p->hkv * (int64_t)D * 2;
+  pl.stat_bytes = (int64_t)p->hq * p->q_rows * 4;
+  pl.bias_bytes = pl.bias ? (int64_t)p->hq * p->bias_len * p->bias_len * 4 : 0;
+  pl.delta_bytes = round256(pl.stat_bytes);
+
+  const int64_t pos_per_wg = 32 * (4 / pl.hpw);
+  pl.bpc_fwd = (int)cdiv(p->max_chunk_len, pos_per_wg);
+  pl.bpc_prepass = (int)cdiv(p->max_chunk_len, kPrepassRows);
+  pl.kv_tiles = (int)cdiv(p->max_kv_len, kDkdvKeys);
+  const int64_t gx_fwd = (int64_t)p->num_chunks * pl.bpc_fwd;
+  const int64_t gx_pre = (int64_t)p->num_chunks * pl.bpc_prepass;
+  const int64_t gx_kv = (int64_t)p->num_seqs * pl.kv_tiles;
+  if (gx_fwd > kGridMax || gx_pre > kGridMax || gx_kv > kGridMax || p->hq / pl.hpw > 65535 ||
+      p->hkv > 65535)
+    return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
+  pl.grid_fwd = dim3((unsigned)gx_fwd, (unsigned)(p->hq / pl.hpw));
+  pl.grid_prepass = dim3((unsigned)gx_pre);
+  pl.grid_dkdv = dim3((unsigned)gx_kv, (unsigned)p->hkv);
+
+  pl.parts = 1;
+  pl.partial_bytes = 0;
+  if (pl.bias) {
+    const int64_t tiles = cdiv(p->bias_len, kDbiasKeys) * cdiv(p->bias_len, kDbiasPos) * p->hq;
+    int64_t parts = cdiv(2048, tiles);
+    parts = std::max<int64_t>(1, std::min<int64_t>({parts, 16, std::max(1, p->num_chunks)}));
+    if ((int64_t)p->hq * parts > 65535) parts = std::max<int64_t>(1, 65535 / p->hq);
+    pl.parts = (int)parts;
+    if (pl.parts > 1) pl.partial_bytes = round256((int64_t)pl.parts * pl.bias_bytes);
+    pl.grid_dbias = dim3((unsigned)cdiv(p->bias_len, kDbiasKeys), (unsigned)cdiv(p->bias_len, kDbiasPos),
+                         (unsigned)(p->hq * pl.parts));
+  }
+  return CPATTN_OK;
+}
+
+AttnArgs base_args(const cpattn_problem* p, const Plan& pl) {
+  AttnArgs a{};
+  a.q_rows = p->q_rows;
+  a.num_seqs = p->num_seqs;
+  a.num_chunks = p->num_chunks;
+  a.hq = p->hq;
+  a.hkv = p->hkv;
+  a.group = pl.G;
+  a.hpw = pl.hpw;
+  a.kv_tiles = pl.kv_tiles;
+  a.bias_len = p->bias_len;
+  a.parts = pl.parts;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * kLog2e;
+  return a;
+}
+
+int check_descriptors(const cpattn_problem* p, const int32_t* so, const int32_t* sl, const int32_t* cm,
+                      const int32_t* dev_err) {
+  int r;
+  if ((r = check_ptr(so, (uint64_t)p->num_seqs * 4, 4, "seq_offsets"))) return r;
+  if ((r = check_ptr(sl, (uint64_t)p->num_seqs * 4, 4, "seq_lens"))) return r;
+  if ((r = check_ptr(cm, (uint64_t)p->num_chunks * 16, 16, "q_chunk_map"))) return r;
+  if ((r = check_ptr(dev_err, 4, 4, "dev_err"))) return r;
+  return CPATTN_OK;
+}
+
+void add_descriptor_ranges(std::vector<Range>& rs, const cpattn_problem* p, const int32_t* so,
+                           const int32_t* sl, const int32_t* cm, const int32_t* dev_err,
+                           bool dev_err_written) {
+  rs.push_back(rng("seq_offsets", so, (uint64_t)p->num_seqs * 4, false));
+  rs.push_back(rng("seq_lens", sl, (uint64_t)p->num_seqs * 4, false));
+  rs.push_back(rng("q_chunk_map", cm, (uint64_t)p->num_chunks * 16, false));
+  rs.push_back(rng("dev_err", dev_err, 4, dev_err_written));
+}
+
+int run_validate(const cpattn_problem* p, const int32_t* so, const int32_t* sl, const int32_t* cm,
+                 int32_t* dev_err, hipStream_t s) {
+  ValidateArgs v{};
+  v.seq_offsets = so;
+  v.seq_lens = sl;
+  v.chunks = cm;
+  v.dev_err = dev_err;
+  v.rows = p->kv_rows;
+  v.q_rows = p->q_rows;
+  v.num_seqs = p->num_seqs;
+  v.num_chunks = p->num_chunks;
+  v.max_chunk_len = p->max_chunk_len;
+  v.max_kv_len = p->max_kv_len;
+  v.bias_len = p->bias_len;
+  v.s_pitch = 0;
+  return hip_check(launch_validate(v, s), "validate launch");
+}
+
+bool empty(dim3 g) { return g.x == 0 || g.y == 0 || g.z == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* cpattn_status_str(int status) {
+  switch (status) {
+    case CPATTN_OK: return "CPATTN_OK";
+    case CPATTN_EINVAL: return "CPATTN_EINVAL: invalid argument";
+    case CPATTN_EUNSUPPORTED: return "CPATTN_EUNSUPPORTED: unsupported problem";
+    case CPATTN_EHIP: return "CPATTN_EHIP: HIP runtime error";
+    default: return "unknown cpattn status";
+  }
+}
+
+const char* cpattn_last_error(void) { return g_last_error.c_str(); }
+
+int cpattn_version(void) { return 10000; }
+
+size_t cpattn_workspace_size(const cpattn_problem* p, int op) {
+  Plan pl;
+  if (make_plan(p, pl)) return 0;
+  if (op == CPATTN_OP_FWD) return 0;
+  if (op == CPATTN_OP_BWD) return (size_t)(pl.delta_bytes + pl.partial_bytes);
+  return 0;
+}
+
+int cpattn_validate(const cpattn_problem* p, const int32_t* seq_offsets, const int32_t* seq_lens,
+                    const int32_t* q_chunk_map, int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = check_descriptors(p, seq_offsets, seq_lens, q_chunk_map, dev_err))) return r;
+  std::vector<Range> rs;
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, true);
+  if ((r = alias_audit(rs))) return r;
+  return run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, (hipStream_t)stream);
+}
+
+int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
+               const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
+               const float* bias, void* o, float* lse, void* ws, size_t ws_bytes,
+               int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = check_ptr(q, pl.q_bytes, 16, "q")) || (r = check_ptr(k, pl.kv_bytes, 16, "k")) ||
+      (r = check_ptr(v, pl.kv_bytes, 16, "v")) || (r = check_ptr(o, pl.q_bytes, 16, "o")) ||
+      (r = check_ptr(lse, pl.stat_bytes, 4, "lse")) ||
+      (r = check_ptr(bias, pl.bias_bytes, 16, "bias")))
+    return r;
+  if (!pl.bias && bias) return fail(CPATTN_EINVAL, "bias given but bias_len is 0");
+  if ((r = check_descriptors(p, seq_offsets, seq_lens, q_chunk_map, dev_err))) return r;
+  (void)ws;
+  (void)ws_bytes;
+  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false), rng("k", k, pl.kv_bytes, false),
+                           rng("v", v, pl.kv_bytes, false), rng("bias", bias, pl.bias_bytes, false),
+                           rng("o", o, pl.q_bytes, true), rng("lse", lse, pl.stat_bytes, true)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, true);
+  if ((r = alias_audit(rs))) return r;
+
+  hipStream_t s = (hipStream_t)stream;
+  if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
+  if (empty(pl.grid_fwd)) return CPATTN_OK;
+  AttnArgs a = base_args(p, pl);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.bias = bias;
+  a.o_out = (uint16_t*)o;
+  a.lse_out = lse;
+  a.seq_offsets = seq_offsets;
+  a.seq_lens = seq_lens;
+  a.chunks = q_chunk_map;
+  a.dev_err = dev_err;
+  a.blocks_per_chunk = pl.bpc_fwd;
+  return hip_check(launch_fwd(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd, s), "forward launch");
+}
+
+// ---------------------------------------------------------------- backward steps
+
+namespace {
+
+int bwd_common_checks(const cpattn_problem* p, const Plan& pl, const void* q, const void* k,
+                      const void* v, const float* bias, const float* lse, const void* dout,
+                      const int32_t* so, const int32_t* sl, const int32_t* cm, const int32_t* dev_err) {
+  int r;
+  if ((r = check_ptr(q, pl.q_bytes, 16, "q")) || (r = check_ptr(k, pl.kv_bytes, 16, "k")) ||
+      (r = check_ptr(v, pl.kv_bytes, 16, "v")) || (r = check_ptr(lse, pl.stat_bytes, 4, "lse")) ||
+      (r = check_ptr(dout, pl.q_bytes, 16, "dout")) ||
+      (r = check_ptr(bias, pl.bias_bytes, 16, "bias")))
+    return r;
+  if (!pl.bias && bias) return fail(CPATTN_EINVAL, "bias given but bias_len is 0");
+  return check_descriptors(p, so, sl, cm, dev_err);
+}
+
+AttnArgs bwd_args(const cpattn_problem* p, const Plan& pl, const void* q, const void* k, const void* v,
+                  const int32_t* so, const int32_t* sl, const int32_t* cm, const float* bias,
+                  const float* lse, const void* dout, const float* delta, const int32_t* dev_err) {
+  AttnArgs a = base_args(p, pl);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.bias = bias;
+  a.lse = lse;
+  a.dout = (const uint16_t*)dout;
+  a.delta = delta;
+  a.seq_offsets = so;
+  a.seq_lens = sl;
+  a.chunks = cm;
+  a.dev_err = dev_err;
+  return a;
+}
+
+int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, const void* o,
+                    const void* dout, float* delta, const int32_t* dev_err, hipStream_t s) {
+  if (empty(pl.grid_prepass)) return CPATTN_OK;
+  AttnArgs a = base_args(p, pl);
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)dout;
+  a.delta_out = delta;
+  a.chunks = cm;
+  a.dev_err = dev_err;
+  a.blocks_per_chunk = pl.bpc_prepass;
+  return hip_check(launch_prepass(a, pl.D, pl.grid_prepass, s), "pre-pass launch");
+}
+
+int enqueue_dkdv(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dk, void* dv, int acc,
+                 hipStream_t s) {
+  if (empty(pl.grid_dkdv)) return CPATTN_OK;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.accumulate = acc ? 1 : 0;
+  return hip_check(launch_dkdv(a, pl.D, p->causal != 0, pl.bias, pl.grid_dkdv, s), "dK/dV launch");
+}
+
+int enqueue_dq(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dq, hipStream_t s) {
+  if (empty(pl.grid_fwd)) return CPATTN_OK;
+  a.dq = (uint16_t*)dq;
+  a.blocks_per_chunk = pl.bpc_fwd;
+  return hip_check(launch_dq(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd, s), "dQ launch");
+}
+
+int enqueue_dbias(const cpattn_problem* p, const Plan& pl, AttnArgs a, float* dbias, void* ws,
+                  hipStream_t s) {
+  if (!pl.bias || empty(pl.grid_dbias)) return CPATTN_OK;
+  float* partial = pl.parts > 1 ? (float*)((char*)ws + pl.delta_bytes) : dbias;
+  a.dbias = partial;
+  int r = hip_check(launch_dbias(a, pl.D, pl.grid_dbias, s), "dBias launch");
+  if (r || pl.parts == 1) return r;
+  return hip_check(launch_dbias_reduce(partial, dbias, pl.bias_bytes / 4, pl.parts, a.dev_err, s),
+                   "dBias reduce launch");
+}
+
+}  // namespace
+
+int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
+               const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
+               const float* bias, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* dbias, int dkv_accumulate,
+               void* ws, size_t ws_bytes, int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
+                             dev_err)))
+    return r;
+  if ((r = check_ptr(o, pl.q_bytes, 16, "o")) || (r = check_ptr(dq, pl.q_bytes, 16, "dq")) ||
+      (r = check_ptr(dk, pl.kv_bytes, 16, "dk")) || (r = check_ptr(dv, pl.kv_bytes, 16, "dv")))
+    return r;
+  if (dbias && !pl.bias) return fail(CPATTN_EINVAL, "dbias given but bias_len is 0");
+  if (dbias && !aligned(dbias, 16)) return fail(CPATTN_EINVAL, "dbias is not 16-byte aligned");
+  if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
+  const int64_t need = pl.delta_bytes + (dbias ? pl.partial_bytes : 0);
+  if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
+  if ((r = check_ptr(ws, need, 256, "ws"))) return r;
+  const int64_t dbias_bytes = dbias ? pl.bias_bytes : 0;
+  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),        rng("k", k, pl.kv_bytes, false),
+                           rng("v", v, pl.kv_bytes, false),        rng("bias", bias, pl.bias_bytes, false),
+                           rng("o", o, pl.q_bytes, false),         rng("lse", lse, pl.stat_bytes, false),
+                           rng("dout", dout, pl.q_bytes, false),   rng("dq", dq, pl.q_bytes, true),
+                           rng("dk", dk, pl.kv_bytes, true),       rng("dv", dv, pl.kv_bytes, true),
+                           rng("dbias", dbias, dbias_bytes, true), rng("ws", ws, need, true)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, true);
+  if ((r = alias_audit(rs))) return r;
+
+  hipStream_t s = (hipStream_t)stream;
+  float* delta = (float*)ws;
+  if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
+  if ((r = enqueue_prepass(p, pl, q_chunk_map, o, dout, delta, dev_err, s))) return r;
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, delta, dev_err);
+  if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
+  if ((r = enqueue_dq(p, pl, a, dq, s))) return r;
+  if (dbias) return enqueue_dbias(p, pl, a, dbias, ws, s);
+  return CPATTN_OK;
+}
+
+int cpattn_bwd_prepass(const cpattn_problem* p, const int32_t* q_chunk_map, const void* o,
+                       const void* dout, float* delta, const int32_t* dev_err,
+                       cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = check_ptr(o, pl.q_bytes, 16, "o")) || (r = check_ptr(dout, pl.q_bytes, 16, "dout")) ||
+      (r = check_ptr(delta, pl.stat_bytes, 4, "delta")) ||
+      (r = check_ptr(q_chunk_map, (uint64_t)p->num_chunks * 16, 16, "q_chunk_map")) ||
+      (r = check_ptr(dev_err, 4, 4, "dev_err")))
+    return r;
+  std::vector<Range> rs = {rng("o", o, pl.q_bytes, false), rng("dout", dout, pl.q_bytes, false),
+                           rng("q_chunk_map", q_chunk_map, (uint64_t)p->num_chunks * 16, false),
+                           rng("dev_err", dev_err, 4, false), rng("delta", delta, pl.stat_bytes, true)};
+  if ((r = alias_audit(rs))) return r;
+  return enqueue_prepass(p, pl, q_chunk_map, o, dout, delta, dev_err, (hipStream_t)stream);
+}
+
+int cpattn_bwd_dkdv(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                    const int32_t* seq_offsets, const int32_t* seq_lens,
+                    const int32_t* q_chunk_map, const float* bias, const float* lse,
+                    const void* dout, const float* delta, void* dk, void* dv,
+                    int dkv_accumulate, const int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
+                             dev_err)))
+    return r;
+  if ((r = check_ptr(delta, pl.stat_bytes, 4, "delta")) || (r = check_ptr(dk, pl.kv_bytes, 16, "dk")) ||
+      (r = check_ptr(dv, pl.kv_bytes, 16, "dv")))
+    return r;
+  if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
+  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
+                           rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
+                           rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
+                           rng("delta", delta, pl.stat_bytes, false), rng("dk", dk, pl.kv_bytes, true),
+                           rng("dv", dv, pl.kv_bytes, true)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  if ((r = alias_audit(rs))) return r;
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, delta, dev_err);
+  return enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, (hipStream_t)stream);
+}
+
+int cpattn_bwd_dq(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                  const int32_t* seq_offsets, const int32_t* seq_lens,
+                  const int32_t* q_chunk_map, const float* bias, const float* lse,
+                  const void* dout, const float* delta, void* dq, const int32_t* dev_err,
+                  cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
+                             dev_err)))
+    return r;
+  if ((r = check_ptr(delta, pl.stat_bytes, 4, "delta")) || (r = check_ptr(dq, pl.q_bytes, 16, "dq")))
+    return r;
+  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
+                           rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
+                           rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
+                           rng("delta", delta, pl.stat_bytes, false), rng("dq", dq, pl.q_bytes, true)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  if ((r = alias_audit(rs))) return r;
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, delta, dev_err);
+  return enqueue_dq(p, pl, a, dq, (hipStream_t)stream);
+}
+
+int cpattn_bwd_dbias(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                     const int32_t* seq_offsets, const int32_t* seq_lens,
+                     const int32_t* q_chunk_map, const float* bias, const float* lse,
+                     const void* dout, float* dbias, void* ws, size_t ws_bytes,
+                     const int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if (!pl.bias) return fail(CPATTN_EINVAL, "dBias needs a bias (bias_len > 0)");
+  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
+                             dev_err)))
+    return r;
+  if ((r = check_ptr(dbias, pl.bias_bytes, 16, "dbias"))) return r;
+  const int64_t need = pl.delta_bytes + pl.partial_bytes;
+  if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
+  if ((r = check_ptr(ws, need, 256, "ws"))) return r;
+  // The delta array at the head of ws is read; the partial slab after it is written.
+  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
+                           rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
+                           rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
+                           rng("delta", ws, pl.stat_bytes, false), rng("dbias", dbias, pl.bias_bytes, true),
+                           rng("ws partials", (char*)ws + pl.delta_bytes, pl.partial_bytes, true)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  if ((r = alias_audit(rs))) return r;
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout,
+                        (const float*)ws, dev_err);
+  return enqueue_dbias(p, pl, a, dbias, ws, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- layout copies
+
+static int layout_call(const void* src, void* dst, int32_t B, int32_t H, int32_t S_pitch, int32_t D,
+                       int64_t thd_rows, const int32_t* so, const int32_t* sl, int32_t* dev_err,
+                       hipStream_t s, int unpack) {
+  g_last_error.clear();
+  if (B < 0 || H <= 0 || S_pitch < 0 || D <= 0 || thd_rows < 0)
+    return fail(CPATTN_EINVAL, "bad layout sizes");
+  if (D % 8) return fail(CPATTN_EUNSUPPORTED, "D must be a multiple of 8 for the layout copies");
+  if (B > 65535) return fail(CPATTN_EUNSUPPORTED, "more than 65535 sequences");
+  const int64_t bhsd_bytes = (int64_t)B * H * S_pitch * D * 2;
+  const int64_t thd_bytes = thd_rows * H * (int64_t)D * 2;
+  int r;
+  if ((r = check_ptr(src, unpack ? thd_bytes : bhsd_bytes, 16, "src")) ||
+      (r = check_ptr(dst, unpack ? bhsd_bytes : thd_bytes, 16, "dst")) ||
+      (r = check_ptr(so, (uint64_t)B * 4, 4, "seq_offsets")) ||
+      (r = check_ptr(sl, (uint64_t)B * 4, 4, "seq_lens")) || (r = check_ptr(dev_err, 4, 4, "dev_err")))
+    return r;
+  std::vector<Range> rs = {rng("src", src, unpack ? thd_bytes : bhsd_bytes, false),
+                           rng("dst", dst, unpack ? bhsd_bytes : thd_bytes, true),
+                           rng("seq_offsets", so, (uint64_t)B * 4, false),
+                           rng("seq_lens", sl, (uint64_t)B * 4, false), rng("dev_err", dev_err, 4, true)};
+  if ((r = alias_audit(rs))) return r;
+  ValidateArgs v{};
+  v.seq_offsets = so;
+  v.seq_lens = sl;
+  v.chunks = nullptr;
+  v.dev_err = dev_err;
+  v.rows = thd_rows;
+  v.num_seqs = B;
+  v.max_kv_len = S_pitch;
+  v.s_pitch = S_pitch > 0 ? S_pitch : 1;
+  if ((r = hip_check(launch_validate(v, s), "validate launch"))) return r;
+  LayoutArgs a{(const uint16_t*)src, (uint16_t*)dst, so, sl, dev_err, B, H, S_pitch, D, unpack};
+  return hip_check(launch_layout(a, s), "layout launch");
+}
+
+int cpattn_pack(const void* bhsd, void* thd, int32_t B, int32_t H, int32_t S_pitch, int32_t D,
+                int64_t thd_rows, const int32_t* seq_offsets, const int32_t* seq_lens,
+                int32_t* dev_err, cpattn_stream_t stream) {
+  return layout_call(bhsd, thd, B, H, S_pitch, D, thd_rows, seq_offsets, seq_lens, dev_err,
+                     (hipStream_t)stream, 0);
+}
+
+int cpattn_unpack(const void* thd, void* bhsd, int32_t B, int32_t H, int32_t S_pitch, int32_t D,
+                  int64_t thd_rows, const int32_t* seq_offsets, const int32_t* seq_lens,
+                  int32_t* dev_err, cpattn_stream_t stream) {
+  return layout_call(thd, bhsd, B, H, S_pitch, D, thd_rows, seq_offsets, seq_lens, dev_err,
+                     (hipStream_t)stream, 1);
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal launchers (host side) for the cpattn kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+struct AttnArgs;
+
+struct ValidateArgs {
+  const int32_t* seq_offsets;
+  const int32_t* seq_lens;
+  const int32_t* chunks;  // may be null (layout copies)
+  int32_t* dev_err;
+  int64_t rows;           // kv_rows (attention) or thd_rows (layout copies)
+  int64_t q_rows;
+  int num_seqs, num_chunks, max_chunk_len, max_kv_len, bias_len;
+  int s_pitch;            // layout copies: BHSD pitch (0 for attention)
+};
+
+struct LayoutArgs {
+  const uint16_t* src;
+  uint16_t* dst;
+  const int32_t* seq_offsets;
+  const int32_t* seq_lens;
+  const int32_t* dev_err;
+  int B, H, S_pitch, D;
+  int unpack;  // 0: BHSD -> THD, 1: THD -> BHSD
+};
+
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+hipError_t launch_fwd(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
+hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
+hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
+hipError_t launch_dq(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
+hipError_t launch_dbias(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
+hipError_t launch_dbias_reduce(const float* partial, float* out, int64_t n, int parts,
+                               const int32_t* dev_err, hipStream_t s);
+
+// Rows of a chunk handled by one pre-pass workgroup.
+constexpr int kPrepassRows = 16;
+// Keys per dK/dV workgroup (four waves of 32 keys).
+constexpr int kDkdvKeys = 128;
+// dBias tile: 128 query positions x 64 keys per workgroup.
+constexpr int kDbiasPos = 128;
+constexpr int kDbiasKeys = 64;
+
+}  // namespace cpattn

@@ -1,0 +1,201 @@
+/*
+ * cpattn: blockwise causal grouped-query softmax attention, forward and
+ * backward in BF16, on one context-parallel rank's share of a packed THD batch,
+ * for AMD MI355X (gfx950).
+ *
+ * The operations follow the page "Optimize context parallel attention layouts
+ * and gradient accumulation" (TransformerEngine PR 3683): its "Description" and
+ * "Changes" sections (equal-length and padded THD inputs with physical offsets,
+ * separate Q/K/V, GQA, head dims 128/256, the on-device check of the promised
+ * lengths and offsets, output zeroing removed, the BF16 layout copies), its
+ * "CP8 first-gradient accumulator reuse" section (the first dK/dV contribution
+ * is the accumulator, the later one is added) and its "CP8 AllGather:
+ * composition with first-gradient reuse" section (the dO.O row-dot pre-pass);
+ * and the triangle (pair-biased row) attention named on the page "Support and
+ * performance optimization for Hopper (H200) architecture?".
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no memory and keeps no state between calls.
+ *  - BF16 tensors are passed as raw 16-bit patterns, contiguous, head dim
+ *    innermost, 16-byte aligned:
+ *        Q, O, dO, dQ : [q_rows,  hq,  head_dim]
+ *        K, V, dK, dV : [kv_rows, hkv, head_dim]
+ *    LSE and the pre-pass output Delta are fp32 [hq, q_rows].
+ *    The pair bias and dBias are fp32 [hq, bias_len, bias_len].
+ *  - Sequence and chunk descriptors live in device memory:
+ *        seq_offsets int32 [num_seqs]: K/V row holding position 0 of sequence b
+ *        seq_lens    int32 [num_seqs]: valid length L_b of sequence b
+ *        q_chunk_map int32 [num_chunks][4] = {seq, q_row, pos0, len}: Q rows
+ *            [q_row, q_row+len) hold positions [pos0, pos0+len) of `seq`.
+ *    Promises checked on the device on every call (cpattn_validate):
+ *        0 <= L_b <= max_kv_len; sequences lie in [0, kv_rows), in ascending
+ *        order, without overlap; chunks are listed with non-decreasing `seq`
+ *        and ascending, non-overlapping Q rows inside [0, q_rows);
+ *        0 <= len <= max_chunk_len; pos0 >= 0 and pos0+len <= L_seq; with a
+ *        bias, every L_b <= bias_len.
+ *  - Rows of Q/O/dO/dQ that no chunk covers and K/V/dK/dV rows past L_b
+ *    (padding) are never read or written.
+ *  - Causal visibility: the query at position p of a sequence sees key j iff
+ *    j < L and (not causal or j <= p).  GQA maps query head h to KV head
+ *    h / (hq / hkv).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronizes.
+ *  - Host-detectable errors return a non-zero status before anything is
+ *    enqueued: CPATTN_EINVAL for null or misaligned pointers, bad sizes,
+ *    hq % hkv != 0, a workspace that is too small, or any output byte range
+ *    that overlaps an input or another output (pointer-alias audit);
+ *    CPATTN_EUNSUPPORTED for unsupported head dims or variants;
+ *    CPATTN_EHIP when a launch fails.  cpattn_last_error() describes it.
+ *  - Device-detectable errors: the validation step overwrites *dev_err (a
+ *    caller-owned device int32) with the CPATTN_DEV_* bits of every broken
+ *    promise, 0 if none.  Every later kernel of the same call reads *dev_err
+ *    first and writes nothing when it is non-zero (fail closed).  The caller
+ *    reads it back after synchronizing.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* cpattn_stream_t; /* same type as hipStream_t */
+
+typedef enum cpattn_status {
+  CPATTN_OK = 0,
+  CPATTN_EINVAL = 1,
+  CPATTN_EUNSUPPORTED = 2,
+  CPATTN_EHIP = 3
+} cpattn_status;
+
+/* Bits of the device error word. */
+#define CPATTN_DEV_ESEQ_LEN    0x01 /* a seq_lens entry < 0 or > max_kv_len            */
+#define CPATTN_DEV_ESEQ_RANGE  0x02 /* a sequence outside [0,kv_rows), unordered or overlapping */
+#define CPATTN_DEV_ECHUNK_SEQ  0x04 /* chunk seq out of range or decreasing             */
+#define CPATTN_DEV_ECHUNK_ROWS 0x08 /* chunk Q rows outside [0,q_rows), unordered or overlapping */
+#define CPATTN_DEV_ECHUNK_POS  0x10 /* len < 0, len > max_chunk_len, pos0 < 0 or pos0+len > L */
+#define CPATTN_DEV_EBIAS       0x20 /* a sequence longer than bias_len                 */
+#define CPATTN_DEV_ELAYOUT     0x40 /* pack/unpack: L_b > S_pitch or THD rows out of range */
+
+/* Shape and variant of one rank share. */
+typedef struct cpattn_problem {
+  int32_t num_seqs;      /* B */
+  int32_t hq;            /* query heads */
+  int32_t hkv;           /* key/value heads; hq % hkv == 0 */
+  int32_t head_dim;      /* D: 64, 128 or 256 (causal or not); 32, 64 or 128 with a bias */
+  int64_t q_rows;        /* physical Q rows, padding included */
+  int64_t kv_rows;       /* physical K/V rows, padding included */
+  int32_t num_chunks;    /* C */
+  int32_t max_chunk_len; /* host-known bound on every chunk len (sizes the grids) */
+  int32_t max_kv_len;    /* host-known bound on every L_b (sizes the grids) */
+  int32_t causal;        /* 1: causal by position; 0: every key of the sequence */
+  float scale;           /* score scale, usually 1/sqrt(head_dim) */
+  int32_t bias_len;      /* 0: no bias; else bias is fp32 [hq, bias_len, bias_len]
+                            indexed [h, query position, key position]; needs causal = 0 */
+} cpattn_problem;
+
+#define CPATTN_OP_FWD 0
+#define CPATTN_OP_BWD 1
+
+/* Text of a status code. */
+const char* cpattn_status_str(int status);
+
+/* Description of the last host-side failure of the calling thread ("" if none). */
+const char* cpattn_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int cpattn_version(void);
+
+/* Bytes of caller-provided device workspace that cpattn_fwd (op = CPATTN_OP_FWD)
+ * or cpattn_bwd (op = CPATTN_OP_BWD) needs for `p`: Delta (fp32 [hq, q_rows]) and,
+ * with a bias, the per-partition dBias partial sums.  Returns 0 for an invalid
+ * problem (check it with the entry point for the reason). */
+size_t cpattn_workspace_size(const cpattn_problem* p, int op);
+
+/* The device promise check alone ("Changes": promised sequence lengths and
+ * physical offsets checked on the device on every execution).  Overwrites
+ * *dev_err with the CPATTN_DEV_* bits. */
+int cpattn_validate(const cpattn_problem* p, const int32_t* seq_offsets, const int32_t* seq_lens,
+                    const int32_t* q_chunk_map, int32_t* dev_err, cpattn_stream_t stream);
+
+/* Forward.  For every chunk row and query head: O = softmax(scale Q K^T (+bias)) V
+ * over the visible keys (BF16, round to nearest even) and LSE = natural-log
+ * log-sum-exp of the scaled scores (fp32, the "Stats" layout [hq, q_rows]).
+ * Writes O and LSE on chunk rows only.  ws may be NULL when
+ * cpattn_workspace_size(p, CPATTN_OP_FWD) is 0. */
+int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
+               const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
+               const float* bias, void* o, float* lse, void* ws, size_t ws_bytes,
+               int32_t* dev_err, cpattn_stream_t stream);
+
+/* Backward: validate, the Delta pre-pass, dK/dV, then dQ.
+ *  dQ (BF16) is written on chunk rows.
+ *  dK/dV (BF16) are the sums over all chunks of each sequence and over the
+ *  hq/hkv query heads of each KV head, accumulated in fp32 and rounded once.
+ *  dkv_accumulate = 0 (first contribution): every valid K/V row of every
+ *  sequence is STORED (0 where no query attends), so dK/dV need no zero fill.
+ *  dkv_accumulate = 1 (second addition): the existing BF16 dK/dV values are
+ *  read, this call's contribution is added in fp32 and the sum is rounded once.
+ *  dbias (fp32, with a bias only, may be NULL to skip it) is STORED: the sum of
+ *  dS over every chunk row, unscaled.  O and LSE are the forward's outputs.
+ *  ws must hold cpattn_workspace_size(p, CPATTN_OP_BWD) bytes. */
+int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
+               const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
+               const float* bias, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, float* dbias, int dkv_accumulate,
+               void* ws, size_t ws_bytes, int32_t* dev_err, cpattn_stream_t stream);
+
+/* The backward's steps one by one, for callers that schedule them (and for
+ * timing each kernel).  None of them validates: call cpattn_validate first on
+ * the same stream with the same dev_err.
+ *  cpattn_bwd_prepass: delta[h, r] = sum_d dO[r,h,d] O[r,h,d] (fp32) on chunk
+ *      rows ("CP8 AllGather: composition with first-gradient reuse": the row
+ *      dot of dO and O, loaded at their physical pitch).
+ *  cpattn_bwd_dkdv: dK/dV as in cpattn_bwd from delta.
+ *  cpattn_bwd_dq: dQ as in cpattn_bwd from delta.
+ *  cpattn_bwd_dbias: dBias as in cpattn_bwd from delta; ws as for cpattn_bwd
+ *      (the delta array is ws's first hq*q_rows floats). */
+int cpattn_bwd_prepass(const cpattn_problem* p, const int32_t* q_chunk_map, const void* o,
+                       const void* dout, float* delta, const int32_t* dev_err,
+                       cpattn_stream_t stream);
+int cpattn_bwd_dkdv(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                    const int32_t* seq_offsets, const int32_t* seq_lens,
+                    const int32_t* q_chunk_map, const float* bias, const float* lse,
+                    const void* dout, const float* delta, void* dk, void* dv,
+                    int dkv_accumulate, const int32_t* dev_err, cpattn_stream_t stream);
+int cpattn_bwd_dq(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                  const int32_t* seq_offsets, const int32_t* seq_lens,
+                  const int32_t* q_chunk_map, const float* bias, const float* lse,
+                  const void* dout, const float* delta, void* dq, const int32_t* dev_err,
+                  cpattn_stream_t stream);
+int cpattn_bwd_dbias(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                     const int32_t* seq_offsets, const int32_t* seq_lens,
+                     const int32_t* q_chunk_map, const float* bias, const float* lse,
+                     const void* dout, float* dbias, void* ws, size_t ws_bytes,
+                     const int32_t* dev_err, cpattn_stream_t stream);
+
+/* Layout copies ("Changes": vectorised BF16 pack/unpack copies that keep
+ * physical sequence origins).  BHSD is [B, H, S_pitch, D]; THD is
+ * [thd_rows, H, D].  pack: thd[seq_offsets[b]+s, h, :] = bhsd[b, h, s, :] for
+ * s < seq_lens[b]; unpack is the inverse.  Only valid rows are copied; the
+ * other destination rows keep their contents.  D must be a multiple of 8.
+ * The promises (L_b <= S_pitch, ascending non-overlapping THD ranges inside
+ * [0, thd_rows)) are checked on the device; on a violation *dev_err gets
+ * CPATTN_DEV_ELAYOUT (plus the sequence bits) and nothing is copied. */
+int cpattn_pack(const void* bhsd, void* thd, int32_t B, int32_t H, int32_t S_pitch, int32_t D,
+                int64_t thd_rows, const int32_t* seq_offsets, const int32_t* seq_lens,
+                int32_t* dev_err, cpattn_stream_t stream);
+int cpattn_unpack(const void* thd, void* bhsd, int32_t B, int32_t H, int32_t S_pitch, int32_t D,
+                  int64_t thd_rows, const int32_t* seq_offsets, const int32_t* seq_lens,
+                  int32_t* dev_err, cpattn_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol,
+and rejects host-detectable contract violations before touching the device.
+
+Every call below fails a host check, so no kernel is ever launched with the fake
+addresses used here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import context_causal_gqa_cpattn_amd as cp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(cp.LIB_PATH), reason="library not built")
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(cpattn_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_what_the_binding_expects():
+    assert declared_symbols() == sorted(cp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cp.load()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.cpattn_version() == 10000
+    assert lib.cpattn_status_str(0) == b"CPATTN_OK"
+
+
+A = 0x7f0000000000  # fake, 256-aligned base addresses: never dereferenced
+
+
+def _prob(**kw):
+    d = dict(num_seqs=2, hq=8, hkv=2, head_dim=128, q_rows=64, kv_rows=128, num_chunks=2,
+             max_chunk_len=32, max_kv_len=64, causal=1, scale=0.088, bias_len=0)
+    d.update(kw)
+    return cp.Problem(**d)
+
+
+def _fwd(prob, q=A, k=A + (1 << 24), v=A + (2 << 24), so=A + (3 << 24), sl=A + (3 << 24) + 256,
+         cm=A + (3 << 24) + 512, bias=None, o=A + (4 << 24), lse=A + (5 << 24), err=A + (6 << 24)):
+    lib = cp.load()
+    return lib.cpattn_fwd(ctypes.byref(prob), q, k, v, so, sl, cm, bias, o, lse, None, 0, err, None)
+
+
+def _err():
+    return cp.load().cpattn_last_error().decode()
+
+
+def test_rejects_bad_problems():
+    assert _fwd(_prob(hq=6, hkv=4)) == cp.EINVAL and "multiple" in _err()
+    assert _fwd(_prob(head_dim=96)) == cp.EUNSUPPORTED
+    assert _fwd(_prob(head_dim=256, bias_len=64, causal=0)) == cp.EUNSUPPORTED
+    assert _fwd(_prob(bias_len=64, causal=1)) == cp.EUNSUPPORTED
+    assert _fwd(_prob(num_seqs=-1)) == cp.EINVAL
+    assert _fwd(_prob(scale=float("nan"))) == cp.EINVAL
+    assert _fwd(_prob(causal=2)) == cp.EINVAL
+    lib = cp.load()
+    assert lib.cpattn_fwd(None, A, A, A, A, A, A, None, A, A, None, 0, A, None) == cp.EINVAL
+
+
+def test_rejects_null_and_misaligned_pointers():
+    assert _fwd(_prob(), q=None) == cp.EINVAL and "q is NULL" in _err()
+    assert _fwd(_prob(), o=A + (4 << 24) + 2) == cp.EINVAL and "aligned" in _err()
+    assert _fwd(_prob(), cm=A + (3 << 24) + 520) == cp.EINVAL  # chunk map needs 16 bytes
+    assert _fwd(_prob(), err=None) == cp.EINVAL
+    assert _fwd(_prob(), bias=A + (7 << 24)) == cp.EINVAL and "bias_len is 0" in _err()
+
+
+def test_alias_audit_rejects_overlapping_outputs():
+    # O overlapping Q
+    assert _fwd(_prob(), o=A + 4096) == cp.EINVAL and "alias" in _err()
+    # LSE overlapping O
+    assert _fwd(_prob(), lse=A + (4 << 24) + 256) == cp.EINVAL and "alias" in _err()
+    # dev_err inside the chunk map
+    assert _fwd(_prob(), err=A + (3 << 24) + 512 + 16) == cp.EINVAL and "alias" in _err()
+
+
+def test_bwd_rejects_small_workspace_and_aliases():
+    lib = cp.load()
+    p = _prob()
+    need = lib.cpattn_workspace_size(ctypes.byref(p), cp.OP_BWD)
+    assert need >= 8 * 64 * 4 and need % 256 == 0
+    base = [ctypes.byref(p), A, A + (1 << 24), A + (2 << 24), A + (3 << 24), A + (3 << 24) + 256,
+            A + (3 << 24) + 512, None, A + (4 << 24), A + (5 << 24), A + (8 << 24),
+            A + (9 << 24), A + (10 << 24), A + (11 << 24), None, 0]
+    tail = [A + (12 << 24), need - 4, A + (6 << 24), None]
+    assert lib.cpattn_bwd(*base, *tail) == cp.EINVAL and "workspace" in _err()
+    bad = list(base)
+    bad[12] = A + (1 << 24)  # dk == k
+    assert lib.cpattn_bwd(*bad, A + (12 << 24), need, A + (6 << 24), None) == cp.EINVAL
+    assert "alias" in _err()
+    bad = list(base)
+    bad[15] = 2  # dkv_accumulate must be 0/1
+    assert lib.cpattn_bwd(*bad, A + (12 << 24), need, A + (6 << 24), None) == cp.EINVAL
+
+
+def test_workspace_sizes():
+    lib = cp.load()
+    p = _prob()
+    assert lib.cpattn_workspace_size(ctypes.byref(p), cp.OP_FWD) == 0
+    pb = _prob(head_dim=32, bias_len=1024, causal=0, hq=4, hkv=4, num_chunks=1024, q_rows=1 << 20,
+               kv_rows=1 << 20)
+    ws = lib.cpattn_workspace_size(ctypes.byref(pb), cp.OP_BWD)
+    assert ws >= 4 * (1 << 20) * 4 + 4 * 1024 * 1024 * 4  # delta + at least one partial slab
+    assert lib.cpattn_workspace_size(ctypes.byref(_prob(hq=3)), cp.OP_BWD) == 0
+
+
+def test_layout_copy_host_checks():
+    lib = cp.load()
+    assert lib.cpattn_pack(A, A + (1 << 24), 2, 4, 64, 12, 128, A + (2 << 24), A + (2 << 24) + 256,
+                           A + (3 << 24), None) == cp.EUNSUPPORTED  # D % 8
+    assert lib.cpattn_pack(A, A + 64, 2, 4, 64, 128, 128, A + (2 << 24), A + (2 << 24) + 256,
+                           A + (3 << 24), None) == cp.EINVAL  # dst overlaps src
+    assert lib.cpattn_unpack(None, A, 2, 4, 64, 128, 128, A + (2 << 24), A + (2 << 24) + 256,
+                             A + (3 << 24), None) == cp.EINVAL

@@ -258,3 +258,80 @@ def make_bhsd(B: int, H: int, S_pitch: int, D: int, seed: int) -> np.ndarray:
     """BF16 bits of a [B, H, S_pitch, D] tensor for the layout-copy path."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return draw_bf16(rng, (B, H, S_pitch, D))
+
+
+def subset(w: Workload, seqs=None, chunks=None):
+    """A compact copy of part of a workload (pure re-indexing, no arithmetic).
+
+    Keeps the given sequences with all their chunks, or the sequences named by an
+    explicit chunk list.  Returns (sub, q_index, kv_index): sub's Q row i is row
+    q_index[i] of w, and its K/V row j is row kv_index[j] of w.
+    """
+    if chunks is None:
+        keep = set(range(w.num_seqs)) if seqs is None else set(int(s) for s in seqs)
+        chunks = [tuple(int(x) for x in c) for c in w.chunks if int(c[0]) in keep]
+        seq_ids = sorted(keep)
+    else:
+        chunks = [tuple(int(x) for x in c) for c in chunks]
+        seq_ids = sorted(set(c[0] for c in chunks)) if seqs is None else sorted(set(int(s) for s in seqs))
+    seq_map = {s: i for i, s in enumerate(seq_ids)}
+    kv_parts, offs, lens = [], [], []
+    n = 0
+    for s in seq_ids:
+        o, L = int(w.seq_offsets[s]), int(w.seq_lens[s])
+        offs.append(n)
+        lens.append(L)
+        kv_parts.append(np.arange(o, o + L, dtype=np.int64))
+        n += L
+    kv_index = np.concatenate(kv_parts) if kv_parts else np.zeros(0, np.int64)
+    chunks = sorted(chunks, key=lambda c: (seq_map[c[0]], c[1]))
+    q_parts, new_chunks = [], []
+    r = 0
+    for (s, r0, p0, ln) in chunks:
+        new_chunks.append((seq_map[s], r, p0, ln))
+        q_parts.append(np.arange(r0, r0 + ln, dtype=np.int64))
+        r += ln
+    q_index = np.concatenate(q_parts) if q_parts else np.zeros(0, np.int64)
+    sub = Workload(w.name + "[subset]", w.hq, w.hkv, w.head_dim, len(q_index), len(kv_index),
+                   w.causal, w.scale, np.asarray(offs, np.int32), np.asarray(lens, np.int32),
+                   np.asarray(new_chunks, np.int32).reshape(-1, 4), bias_len=w.bias_len, seed=w.seed)
+    if w.q is not None:
+        sub.q, sub.do = w.q[q_index], w.do[q_index]
+        sub.k, sub.v = w.k[kv_index], w.v[kv_index]
+        sub.bias = w.bias
+    return sub, q_index, kv_index
+
+
+def draw_on_device(w: Workload, seed: int, device="cuda", poison_padding: bool = True):
+    """Full-size inputs drawn on the GPU: N(0,1) float32 from a seeded torch
+    generator, rounded to BF16 (round to nearest even), NaN in padding rows.
+
+    Same shapes and distribution as the host draws, for workloads too large to
+    draw on the host quickly.  Returns torch tensors (q, k, v, do, bias)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        flat = out.view(-1)
+        step = 1 << 26
+        for s in range(0, flat.numel(), step):
+            e = min(flat.numel(), s + step)
+            flat[s:e] = torch.randn(e - s, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+        return out
+
+    q = draw((w.q_rows, w.hq, w.head_dim))
+    k = draw((w.kv_rows, w.hkv, w.head_dim))
+    v = draw((w.kv_rows, w.hkv, w.head_dim))
+    do = draw((w.q_rows, w.hq, w.head_dim))
+    bias = None
+    if w.bias_len:
+        bias = torch.randn((w.hq, w.bias_len, w.bias_len), generator=g, device=device)
+    if poison_padding:
+        qpad = torch.from_numpy(~w.q_valid_rows()).to(device)
+        kpad = torch.from_numpy(~w.kv_valid_rows()).to(device)
+        for t, m in ((q, qpad), (do, qpad), (k, kpad), (v, kpad)):
+            if bool(m.any()):
+                t[m] = float("nan")
+    return q, k, v, do, bias
