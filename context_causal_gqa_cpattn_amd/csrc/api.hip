@@ -83,7 +83,7 @@ struct Plan {
   int64_t delta_bytes;  // rounded to 256
   int parts;            // dBias partitions
   int64_t partial_bytes;
-  dim3 grid_fwd, grid_prepass, grid_dkdv, grid_dbias;
+  dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias;
   int bpc_fwd, bpc_prepass, kv_tiles;
 };
 
@@ -132,6 +132,8 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
       p->hkv > 65535)
     return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_fwd = dim3((unsigned)gx_fwd, (unsigned)(p->hq / pl.hpw));
+  if (gx_fwd * (p->hq / pl.hpw) > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
+  pl.grid_fwd1d = dim3((unsigned)(gx_fwd * (p->hq / pl.hpw)));
   pl.grid_prepass = dim3((unsigned)gx_pre);
   pl.grid_dkdv = dim3((unsigned)gx_kv, (unsigned)p->hkv);
 
@@ -270,7 +272,7 @@ int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void
 
   hipStream_t s = (hipStream_t)stream;
   if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
-  if (empty(pl.grid_fwd)) return CPATTN_OK;
+  if (empty(pl.grid_fwd1d)) return CPATTN_OK;
   AttnArgs a = base_args(p, pl);
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -283,7 +285,7 @@ int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void
   a.chunks = q_chunk_map;
   a.dev_err = dev_err;
   a.blocks_per_chunk = pl.bpc_fwd;
-  return hip_check(launch_fwd(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd, s), "forward launch");
+  return hip_check(launch_fwd(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd1d, s), "forward launch");
 }
 
 // ---------------------------------------------------------------- backward steps

@@ -81,6 +81,67 @@ __device__ __forceinline__ float log2f_fast(float x) { return __builtin_amdgcn_l
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define CPATTN_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Physical block id -> logical work item, so that consecutive logical items (which
+// share K/V) run on the same XCD (blocks are dealt to the 8 XCDs round robin) and
+// hit that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  const int per = n >> 3;
+  return pid < per * 8 ? (pid & 7) * per + (pid >> 3) : pid;
+}
+
+// LDS tile layouts for [rows][D] BF16 tiles written by LDS DMA (contiguous 1 KB per
+// wave instruction, so no padding): K-like tiles read with 16-byte row reads swap
+// 16-byte granules by (row & KMASK); V-like tiles read with transposing 8-byte reads
+// swap 64-byte chunks by (row & VMASK).  Both make the reads of one instruction
+// cover distinct LDS banks.
+template <int D>
+struct TileSwz {
+  static constexpr int G = D / 8;   // 16-byte granules per row
+  static constexpr int KMASK = G >= 16 ? 15 : G - 1;
+  static constexpr int C = D / 32;  // 64-byte chunks per row
+  static constexpr int VMASK = C >= 4 ? 3 : C - 1;
+};
+
+// One 16-byte LDS DMA per lane: lane l's data lands at lds + 16*l bytes.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)g, CPATTN_LDS(void, lds), 16, 0, 0);
+}
+
+// DMA rows [key0, key0+64) of K and V (row stride rs elements) into swizzled LDS
+// tiles.  Rows at or past L repeat row L-1 (finite data; they are masked later).
+template <int D>
+__device__ __forceinline__ void dma_kv_tile(uint16_t* kl, uint16_t* vl, const uint16_t* kbase,
+                                            const uint16_t* vbase, int64_t rs, int key0, int L,
+                                            int wave, int lane) {
+  constexpr int G = TileSwz<D>::G, KM = TileSwz<D>::KMASK, VM = TileSwz<D>::VMASK;
+  for (int i = __builtin_amdgcn_readfirstlane(wave); i < G; i += 4) {
+    const int idx = i * 64 + lane;
+    const int r = idx / G, p = idx % G;
+    const int64_t key = min(key0 + r, L - 1);
+    dma16(kbase + key * rs + ((p ^ (r & KM)) * 8), kl + i * 512);
+    dma16(vbase + key * rs + ((((p >> 2) ^ (r & VM)) * 4 + (p & 3)) * 8), vl + i * 512);
+  }
+}
+
+// A operand of V^T P^T for 16 keys starting at row r0 - tr_row and 32 dims of block db,
+// read from a natural-layout [key][D] tile with two transposing LDS reads.  Lane l gets
+// V[k][32*db + l%32] for k = r0 - tr_row + 4*(l/32) + {0..3} and the same + 8, which is
+// the key order (sigma16) of a 32x32 accumulator's rows.
+template <int D>
+__device__ __forceinline__ u32x4 tr_read_vt(const uint16_t* vt, int r0, int db, int tr_d) {
+  constexpr int VM = TileSwz<D>::VMASK;
+  const int pc = ((db ^ (r0 & VM)) * 32) + tr_d;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, vt + r0 * D + pc));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, vt + (r0 + 8) * D + pc));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
 struct Chunk {
   int seq, q_row, pos0, len;
 };
