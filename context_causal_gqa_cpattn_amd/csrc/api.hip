@@ -135,7 +135,8 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   if (gx_fwd * (p->hq / pl.hpw) > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_fwd1d = dim3((unsigned)(gx_fwd * (p->hq / pl.hpw)));
   pl.grid_prepass = dim3((unsigned)gx_pre);
-  pl.grid_dkdv = dim3((unsigned)gx_kv, (unsigned)p->hkv);
+  if (gx_kv * p->hkv > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
+  pl.grid_dkdv = dim3((unsigned)(gx_kv * p->hkv));
 
   pl.parts = 1;
   pl.partial_bytes = 0;
@@ -346,10 +347,10 @@ int enqueue_dkdv(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dk, 
 }
 
 int enqueue_dq(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dq, hipStream_t s) {
-  if (empty(pl.grid_fwd)) return CPATTN_OK;
+  if (empty(pl.grid_fwd1d)) return CPATTN_OK;
   a.dq = (uint16_t*)dq;
   a.blocks_per_chunk = pl.bpc_fwd;
-  return hip_check(launch_dq(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd, s), "dQ launch");
+  return hip_check(launch_dq(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd1d, s), "dQ launch");
 }
 
 int enqueue_dbias(const cpattn_problem* p, const Plan& pl, AttnArgs a, float* dbias, void* ws,

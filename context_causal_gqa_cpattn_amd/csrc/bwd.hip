@@ -59,220 +59,250 @@ hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- dK / dV
+//
+// Workgroup = (sequence, 128-key tile, KV head g) with eight waves; wave w owns keys
+// [16w, 16w+16) of the tile and keeps them in registers as B operands (K^T, V^T) for
+// the whole loop, with dK^T and dV^T (16 keys x D) accumulating in fp32 (16x16x32 MFMA
+// tiles keep that at 2*D/16*4 registers per lane).  The loop runs over every (chunk of
+// the sequence, query head of the group, 32-query tile) that sees the key tile; Q and
+// dO tiles (and their LSE/Delta) are DMA'd into LDS one iteration ahead.  Per tile:
+//   S  = Q K^T     A = Q rows (16-byte LDS reads), B = K^T registers
+//   dP = dO V^T    A = dO rows, B = V^T registers
+//   P = exp(scale S - LSE), dS = P (dP - Delta)    (C layout: lane = key, rows = queries)
+//   dV^T += dO^T P   A = dO^T by transposing LDS reads, B = P (already in B layout)
+//   dK^T += Q^T dS   A = Q^T likewise, B = dS
+// The GQA sum over the group's query heads and the sum over chunks happen in the fp32
+// accumulators; dK = scale dK^T and dV are rounded to BF16 once (STORE), or added to
+// the existing BF16 values and rounded once (ADD).
 
-template <int D>
-struct DkdvSmem {
-  static constexpr int NS = D + 8;   // natural [query][d] stride
-  static constexpr int TS = 32 + 8;  // transposed [d][query slot] stride
-  uint16_t q[32 * NS];
-  uint16_t dO[32 * NS];
-  uint16_t qt[D * TS];
-  uint16_t dOt[D * TS];
-  float lse2[32];
-  float delta[32];
+constexpr int kBM = 32;          // queries per tile
+constexpr int kDkdvWaves = 8;    // waves per dK/dV workgroup (16 keys each)
+constexpr int kDkdvThreads = kDkdvWaves * 64;
+
+struct QTileIter {
+  int c, hh, qt, qt_first, n_qt;
+  Chunk ch;
 };
 
-// Stage 32 chunk rows of Q and dO for head h: natural and transposed (sigma slots).
-template <int D>
-__device__ __forceinline__ void stage_q_do(DkdvSmem<D>& sm, const AttnArgs& a, int64_t qrow0,
-                                           int nq, int h, int tid) {
-  constexpr int D8 = D / 8;
-  constexpr int NBLK = 4 * D8;  // 8x8 blocks per tensor
-  const int64_t rs = (int64_t)a.hq * D;
-  for (int i = tid; i < 2 * NBLK; i += kThreads) {
-    const int tsel = i / NBLK, j = i % NBLK;
-    const int pg = j & 3, dg = j >> 2;
-    const uint16_t* base = (tsel ? a.dout : a.q) + qrow0 * rs + (int64_t)h * D + dg * 8;
-    uint16_t* nat = tsel ? sm.dO : sm.q;
-    uint16_t* tr = tsel ? sm.dOt : sm.qt;
-    u32x4 rows[8], cols[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int qi = (pg >> 1) * 16 + sigma16((pg & 1) * 8 + e);
-      rows[e] = (qi < nq) ? ld16(base + (int64_t)qi * rs) : u32x4{0u, 0u, 0u, 0u};
-      st16(&nat[qi * DkdvSmem<D>::NS + dg * 8], rows[e]);
+// Advance to the next chunk (from c) that has query tiles seeing keys >= key0.
+template <bool CAUSAL>
+__device__ __forceinline__ bool seek_chunk(const AttnArgs& a, QTileIter& it, int c_end, int key0) {
+  for (; it.c < c_end; ++it.c) {
+    it.ch = load_chunk(a.chunks, it.c);
+    const int first_row = CAUSAL ? max(0, key0 - it.ch.pos0) : 0;
+    if (first_row < it.ch.len) {
+      it.qt_first = first_row / kBM;
+      it.n_qt = (it.ch.len + kBM - 1) / kBM;
+      it.qt = it.qt_first;
+      it.hh = 0;
+      return true;
     }
-    transpose8x8(rows, cols);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) st16(&tr[(dg * 8 + d) * DkdvSmem<D>::TS + pg * 8], cols[d]);
   }
-  if (tid < 32) {
-    const bool ok = tid < nq;
-    const int64_t idx = (int64_t)h * a.q_rows + qrow0 + tid;
-    sm.lse2[tid] = ok ? a.lse[idx] * kLog2e : INFINITY;
-    sm.delta[tid] = ok ? a.delta[idx] : 0.f;
-  }
+  return false;
+}
+
+template <bool CAUSAL>
+__device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_end, int key0) {
+  if (++it.qt < it.n_qt) return true;
+  it.qt = it.qt_first;
+  if (++it.hh < a.group) return true;
+  ++it.c;
+  return seek_chunk<CAUSAL>(a, it, c_end, key0);
+}
+
+template <int D>
+__device__ __forceinline__ void dma_q_do(uint16_t* lq, uint16_t* ldo, const AttnArgs& a,
+                                         const QTileIter& it, int g, int wave, int lane) {
+  const int h = g * a.group + it.hh;
+  const int64_t rs = (int64_t)a.hq * D;
+  const int64_t off = ((int64_t)it.ch.q_row + it.qt * kBM) * rs + (int64_t)h * D;
+  const int nq = min(kBM, it.ch.len - it.qt * kBM);
+  dma_rows<D, kBM, kDkdvWaves>(lq, a.q + off, rs, nq, wave, lane);
+  dma_rows<D, kBM, kDkdvWaves>(ldo, a.dout + off, rs, nq, wave, lane);
+}
+
+// LSE (as base-2) and Delta of tile row `r` (clamped to the valid rows).
+__device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& it, int g, int r,
+                                           float& lse2, float& dl) {
+  const int h = g * a.group + it.hh;
+  const int nq = min(kBM, it.ch.len - it.qt * kBM);
+  const int64_t idx = (int64_t)h * a.q_rows + it.ch.q_row + it.qt * kBM + min(r, nq - 1);
+  lse2 = a.lse[idx] * kLog2e;
+  dl = a.delta[idx];
 }
 
 template <int D, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(kThreads) void dkdv_kernel(const AttnArgs a) {
-  constexpr int NST = D / 16;
-  constexpr int NDB = D / 32;
-  __shared__ DkdvSmem<D> sm;
+__global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
+  constexpr int NS = D / 32;   // 32-wide k-steps of S and dP
+  constexpr int NDB = D / 16;  // 16-row d blocks of dK^T and dV^T
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_q[2][kBM * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_do[2][kBM * D];
+  __shared__ __attribute__((aligned(16))) float lds_lse[2][kBM];
+  __shared__ __attribute__((aligned(16))) float lds_dl[2][kBM];
 
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kg = lane >> 5, col = lane & 31;
-  const int b = blockIdx.x / a.kv_tiles;
-  const int kt = blockIdx.x % a.kv_tiles;
-  const int g = blockIdx.y;
+  const int lg = lane >> 4, n = lane & 15;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = logical % a.kv_tiles;
+  const int rest = logical / a.kv_tiles;
+  const int g = rest % a.hkv;
+  const int b = rest / a.hkv;
   const int L = a.seq_lens[b];
   const int wg_key0 = kt * kDkdvKeys;
   if (wg_key0 >= L) return;
   const int64_t koff = a.seq_offsets[b];
-  const int wkey0 = wg_key0 + wave * 32;
-  const int nk = max(0, min(32, L - wkey0));
-  const int key = wkey0 + col;  // this lane's key (column of S, dP; of dK^T, dV^T)
+  const int wkey0 = wg_key0 + wave * 16;
+  const int nk = max(0, min(16, L - wkey0));
+  const int key = wkey0 + n;  // this lane's key (column of S, dP; of dK^T, dV^T)
 
   // K and V as B operands (columns = keys), held for the whole loop.
   const int64_t kv_stride = (int64_t)a.hkv * D;
-  u32x4 kf[NST], vf[NST];
+  u32x4 kf[NS], vf[NS];
   {
-    const int64_t off = (koff + key) * kv_stride + (int64_t)g * D + kg * 8;
+    const int64_t off = (koff + min(key, L - 1)) * kv_stride + (int64_t)g * D + lg * 8;
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      kf[st] = (col < nk) ? ld16(a.k + off + st * 16) : u32x4{0u, 0u, 0u, 0u};
-      vf[st] = (col < nk) ? ld16(a.v + off + st * 16) : u32x4{0u, 0u, 0u, 0u};
+    for (int st = 0; st < NS; ++st) {
+      kf[st] = (n < nk) ? ld16(a.k + off + st * 32) : u32x4{0u, 0u, 0u, 0u};
+      vf[st] = (n < nk) ? ld16(a.v + off + st * 32) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  f32x16 dkt[NDB], dvt[NDB];
+  f32x4 dkt[NDB], dvt[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
+  for (int db = 0; db < NDB; ++db) { dkt[db] = f32x4{}; dvt[db] = f32x4{}; }
 
-  const int c_begin = chunk_lower_bound(a.chunks, a.num_chunks, b);
   const int c_end = chunk_lower_bound(a.chunks, a.num_chunks, b + 1);
-  for (int c = c_begin; c < c_end; ++c) {
-    const Chunk ch = load_chunk(a.chunks, c);
-    const int first_row = CAUSAL ? max(0, wg_key0 - ch.pos0) : 0;
-    if (first_row >= ch.len) continue;
-    const int n_qt = (ch.len + 31) / 32;
-    for (int hh = 0; hh < a.group; ++hh) {
-      const int h = g * a.group + hh;
-      const float* bias_h = BIAS ? a.bias + (int64_t)h * a.bias_len * a.bias_len : nullptr;
-      for (int qt = first_row / 32; qt < n_qt; ++qt) {
-        const int nq = min(32, ch.len - qt * 32);
-        const int64_t qrow0 = (int64_t)ch.q_row + qt * 32;
-        const int tile_pos0 = ch.pos0 + qt * 32;
-        __syncthreads();
-        stage_q_do<D>(sm, a, qrow0, nq, h, tid);
-        __syncthreads();
-        if (nk == 0) continue;
-        if (CAUSAL && tile_pos0 + nq - 1 < wkey0) continue;
-
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const uint16_t* qa = &sm.q[col * DkdvSmem<D>::NS + kg * 8];
-        const uint16_t* da = &sm.dO[col * DkdvSmem<D>::NS + kg * 8];
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          s = mfma32(ld16(qa + st * 16), kf[st], s);
-          dp = mfma32(ld16(da + st * 16), vf[st], dp);
-        }
-        // P and dS; element r of s is query 8*(r/4) + 4*kg + r%4 of the tile.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = (r >> 2) * 8 + kg * 4 + (r & 3);
-          const int qpos = tile_pos0 + qi;
-          float x = s[r] * a.scale_log2;
-          if (BIAS) x += bias_h[(int64_t)min(qpos, a.bias_len - 1) * a.bias_len + min(key, a.bias_len - 1)] * kLog2e;
-          const bool vis = (col < nk) && (!CAUSAL || key <= qpos);
-          const float p = vis ? exp2f_fast(x - sm.lse2[qi]) : 0.f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - sm.delta[qi]);
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 pf = to_bf16x8(s, st * 8);
-          const u32x4 dsf = to_bf16x8(dp, st * 8);
-          const uint16_t* dta = &sm.dOt[col * DkdvSmem<D>::TS + st * 16 + kg * 8];
-          const uint16_t* qta = &sm.qt[col * DkdvSmem<D>::TS + st * 16 + kg * 8];
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dvt[db] = mfma32(ld16(dta + db * 32 * DkdvSmem<D>::TS), pf, dvt[db]);
-            dkt[db] = mfma32(ld16(qta + db * 32 * DkdvSmem<D>::TS), dsf, dkt[db]);
-          }
-        }
-      }
+  QTileIter cur;
+  cur.c = chunk_lower_bound(a.chunks, a.num_chunks, b);
+  bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0);
+  float st_lse = 0.f, st_dl = 0.f;  // stats staged for the next tile (threads < kBM)
+  if (have) {
+    dma_q_do<D>(lds_q[0], lds_do[0], a, cur, g, wave, lane);
+    if (tid < kBM) {
+      load_stats(a, cur, g, tid, st_lse, st_dl);
+      lds_lse[0][tid] = st_lse;
+      lds_dl[0][tid] = st_dl;
     }
   }
+  wait_vm_all();
+  __syncthreads();
 
-  if (col >= nk) return;
-  const int64_t off = (koff + key) * kv_stride + (int64_t)g * D + kg * 4;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t o = off + db * 32 + i * 8;
-      float k0 = dkt[db][i * 4 + 0] * a.scale, k1 = dkt[db][i * 4 + 1] * a.scale;
-      float k2 = dkt[db][i * 4 + 2] * a.scale, k3 = dkt[db][i * 4 + 3] * a.scale;
-      float v0 = dvt[db][i * 4 + 0], v1 = dvt[db][i * 4 + 1];
-      float v2 = dvt[db][i * 4 + 2], v3 = dvt[db][i * 4 + 3];
-      if (a.accumulate) {
-        const u32x2 ok = ld8(a.dk + o), ov = ld8(a.dv + o);
-        k0 += bf16_lo(ok[0]); k1 += bf16_hi(ok[0]); k2 += bf16_lo(ok[1]); k3 += bf16_hi(ok[1]);
-        v0 += bf16_lo(ov[0]); v1 += bf16_hi(ov[0]); v2 += bf16_lo(ov[1]); v3 += bf16_hi(ov[1]);
-      }
-      st8(a.dk + o, u32x2{pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)});
-      st8(a.dv + o, u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)});
+  int buf = 0;
+  while (have) {
+    QTileIter nxt = cur;
+    const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
+    if (have_next) {
+      dma_q_do<D>(lds_q[buf ^ 1], lds_do[buf ^ 1], a, nxt, g, wave, lane);
+      if (tid < kBM) load_stats(a, nxt, g, tid, st_lse, st_dl);
     }
+
+    const int nq = min(kBM, cur.ch.len - cur.qt * kBM);
+    const int tile_pos0 = cur.ch.pos0 + cur.qt * kBM;
+    if (nk > 0 && !(CAUSAL && tile_pos0 + nq - 1 < wkey0)) {
+      const uint16_t* qt_l = lds_q[buf];
+      const uint16_t* dt_l = lds_do[buf];
+      f32x4 s[2], dp[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = f32x4{};
+        dp[mb] = f32x4{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          s[mb] = mfma16(lds_row16<D>(qt_l, mb * 16 + n, st * 4 + lg), kf[st], s[mb]);
+          dp[mb] = mfma16(lds_row16<D>(dt_l, mb * 16 + n, st * 4 + lg), vf[st], dp[mb]);
+        }
+      }
+      const bool need_mask = (nk < 16) || (nq < kBM) || (CAUSAL && tile_pos0 < wkey0 + 15);
+      const float* bias_h = BIAS ? a.bias + (int64_t)(g * a.group + cur.hh) * a.bias_len * a.bias_len : nullptr;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int q4 = mb * 16 + lg * 4;  // element j is tile query q4 + j
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[buf][q4]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dl[buf][q4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qi = q4 + j;
+          float x = s[mb][j] * a.scale_log2;
+          if (BIAS)
+            x = fmaf(bias_h[(int64_t)min(tile_pos0 + qi, a.bias_len - 1) * a.bias_len + min(key, a.bias_len - 1)],
+                     kLog2e, x);
+          bool vis = true;
+          if (need_mask) vis = (n < nk) && (qi < nq) && (!CAUSAL || key <= tile_pos0 + qi);
+          const float p = vis ? exp2f_fast(x - l4[j]) : 0.f;
+          s[mb][j] = p;
+          dp[mb][j] = p * (dp[mb][j] - d4[j]);
+        }
+      }
+      const u32x4 pf = {pack_bf16x2(s[0][0], s[0][1]), pack_bf16x2(s[0][2], s[0][3]),
+                        pack_bf16x2(s[1][0], s[1][1]), pack_bf16x2(s[1][2], s[1][3])};
+      const u32x4 dsf = {pack_bf16x2(dp[0][0], dp[0][1]), pack_bf16x2(dp[0][2], dp[0][3]),
+                         pack_bf16x2(dp[1][0], dp[1][1]), pack_bf16x2(dp[1][2], dp[1][3])};
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dvt[db] = mfma16(tr_frag16<D>(dt_l, db, lane), pf, dvt[db]);
+        dkt[db] = mfma16(tr_frag16<D>(qt_l, db, lane), dsf, dkt[db]);
+      }
+    }
+    if (have_next && tid < kBM) {
+      lds_lse[buf ^ 1][tid] = st_lse;
+      lds_dl[buf ^ 1][tid] = st_dl;
+    }
+    wait_vm_all();
+    __syncthreads();
+    cur = nxt;
+    have = have_next;
+    buf ^= 1;
+  }
+
+  if (n >= nk) return;
+  const int64_t off = (koff + key) * kv_stride + (int64_t)g * D + lg * 4;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int64_t o = off + db * 16;
+    float k0 = dkt[db][0] * a.scale, k1 = dkt[db][1] * a.scale;
+    float k2 = dkt[db][2] * a.scale, k3 = dkt[db][3] * a.scale;
+    float v0 = dvt[db][0], v1 = dvt[db][1], v2 = dvt[db][2], v3 = dvt[db][3];
+    if (a.accumulate) {
+      const u32x2 ok = ld8(a.dk + o), ov = ld8(a.dv + o);
+      k0 += bf16_lo(ok[0]); k1 += bf16_hi(ok[0]); k2 += bf16_lo(ok[1]); k3 += bf16_hi(ok[1]);
+      v0 += bf16_lo(ov[0]); v1 += bf16_hi(ov[0]); v2 += bf16_lo(ov[1]); v3 += bf16_hi(ov[1]);
+    }
+    st8(a.dk + o, u32x2{pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)});
+    st8(a.dv + o, u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)});
+  }
 }
 
 // ---------------------------------------------------------------- dQ
+//
+// Same decomposition as the forward: a wave owns 32 query rows of one head and keeps Q
+// and dO in registers; K and V tiles of 64 keys are DMA'd into LDS (double buffer).
+//   S^T = K Q^T,  dP^T = V dO^T   (A = K / V rows, 16-byte LDS reads)
+//   dS^T = P^T (dP^T - Delta)     (lane = query)
+//   dQ^T += K^T dS^T              (A = K^T by transposing reads of the same K tile)
 
 constexpr int kBNq = 64;  // keys per KV tile in the dQ kernel
-
-template <int D>
-struct DqSmem {
-  static constexpr int NS = D + 8;
-  static constexpr int TS = kBNq + 8;
-  uint16_t k[kBNq * NS];
-  uint16_t v[kBNq * NS];
-  uint16_t kt[D * TS];
-};
-
-template <int D>
-__device__ __forceinline__ void stage_kv_dq(DqSmem<D>& sm, const uint16_t* __restrict__ kbase,
-                                            const uint16_t* __restrict__ vbase, int64_t rs,
-                                            int key0, int L, int tid) {
-  constexpr int D8 = D / 8;
-  // K: natural rows and the transpose (sigma slots), from one load.
-  for (int i = tid; i < (kBNq / 8) * D8; i += kThreads) {
-    const int pg = i % (kBNq / 8), dg = i / (kBNq / 8);
-    u32x4 rows[8], cols[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int kl = (pg >> 1) * 16 + sigma16((pg & 1) * 8 + e);
-      const int key = key0 + kl;
-      rows[e] = (key < L) ? ld16(kbase + (int64_t)key * rs + dg * 8) : u32x4{0u, 0u, 0u, 0u};
-      st16(&sm.k[kl * DqSmem<D>::NS + dg * 8], rows[e]);
-    }
-    transpose8x8(rows, cols);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) st16(&sm.kt[(dg * 8 + d) * DqSmem<D>::TS + pg * 8], cols[d]);
-  }
-  for (int i = tid; i < kBNq * D8; i += kThreads) {
-    const int r = i / D8, c = i % D8;
-    const int key = key0 + r;
-    st16(&sm.v[r * DqSmem<D>::NS + c * 8],
-         (key < L) ? ld16(vbase + (int64_t)key * rs + c * 8) : u32x4{0u, 0u, 0u, 0u});
-  }
-}
 
 template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
   constexpr int NST = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ DqSmem<D> sm;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kBNq * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][kBNq * D];
 
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 5, col = lane & 31;
-  const int c = blockIdx.x / a.blocks_per_chunk;
-  const int pb = blockIdx.x % a.blocks_per_chunk;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_hg = a.hq / a.hpw;
+  const int pb = logical % a.blocks_per_chunk;
+  const int rest = logical / a.blocks_per_chunk;
+  const int hg = rest % n_hg;
+  const int c = rest / n_hg;
   const Chunk ch = load_chunk(a.chunks, c);
   const int segs = 4 / a.hpw;
   const int wg_row0 = pb * 32 * segs;
   if (wg_row0 >= ch.len) return;
-  const int h = blockIdx.y * a.hpw + (wave % a.hpw);
+  const int h = hg * a.hpw + (wave % a.hpw);
   const int g = h / a.group;
   const int row0 = wg_row0 + (wave / a.hpw) * 32;
   const int nrows = max(0, min(32, ch.len - row0));
@@ -281,8 +311,9 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + 32 * segs) - 1;
   const int kv_end = CAUSAL ? min(L, wg_last_pos + 1) : L;
   const int n_tiles = (kv_end + kBNq - 1) / kBNq;
-  const int wave_last_pos = ch.pos0 + row0 + nrows - 1;
-  const int qpos = ch.pos0 + row0 + col;
+  const int wave_first_pos = ch.pos0 + row0;
+  const int wave_last_pos = wave_first_pos + nrows - 1;
+  const int qpos = wave_first_pos + col;
   const bool qok = col < nrows;
   const int64_t qrow = (int64_t)ch.q_row + row0 + col;
 
@@ -308,50 +339,62 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)g * D;
 
+  if (n_tiles > 0) {
+    dma_rows<D, kBNq>(lds_k[0], kbase, kv_stride, L, wave, lane);
+    dma_rows<D, kBNq>(lds_v[0], vbase, kv_stride, L, wave, lane);
+  }
+  wait_vm_all();
+  __syncthreads();
+
   for (int t = 0; t < n_tiles; ++t) {
     const int key0 = t * kBNq;
-    __syncthreads();
-    stage_kv_dq<D>(sm, kbase, vbase, kv_stride, key0, L, tid);
-    __syncthreads();
-    if (nrows == 0) continue;
-    if (CAUSAL && key0 > wave_last_pos) continue;
-
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-      const uint16_t* kp = &sm.k[(kb * 32 + col) * DqSmem<D>::NS + kg * 8];
-      const uint16_t* vp = &sm.v[(kb * 32 + col) * DqSmem<D>::NS + kg * 8];
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        s[kb] = mfma32(ld16(kp + st * 16), qf[st], s[kb]);
-        dp[kb] = mfma32(ld16(vp + st * 16), dof[st], dp[kb]);
-      }
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) {
+      const int64_t nxt = (int64_t)(key0 + kBNq) * kv_stride;
+      dma_rows<D, kBNq>(lds_k[buf ^ 1], kbase + nxt, kv_stride, L - key0 - kBNq, wave, lane);
+      dma_rows<D, kBNq>(lds_v[buf ^ 1], vbase + nxt, kv_stride, L - key0 - kBNq, wave, lane);
     }
+    if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
+      const uint16_t* kt = lds_k[buf];
+      const uint16_t* vt = lds_v[buf];
+      f32x16 s[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kbase_i = key0 + kb * 32 + i * 8 + kg * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kk = kbase_i + j;
-          float x = s[kb][i * 4 + j] * a.scale_log2;
-          if (BIAS) x += bias_row[min(kk, a.bias_len - 1)] * kLog2e;
-          const bool vis = (kk < L) && (!CAUSAL || kk <= qpos);
-          const float p = vis ? exp2f_fast(x - lse2) : 0.f;
-          dp[kb][i * 4 + j] = p * (dp[kb][i * 4 + j] - dlt);
+        for (int st = 0; st < NST; ++st) {
+          s[kb] = mfma32(lds_row16<D>(kt, kb * 32 + col, st * 2 + kg), qf[st], s[kb]);
+          dp[kb] = mfma32(lds_row16<D>(vt, kb * 32 + col, st * 2 + kg), dof[st], dp[kb]);
         }
       }
+      const bool need_mask = (key0 + kBNq > L) || (CAUSAL && key0 + kBNq - 1 > wave_first_pos);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const u32x4 dsf = to_bf16x8(dp[st >> 1], (st & 1) * 8);
-      const uint16_t* kta = &sm.kt[col * DqSmem<D>::TS + st * 16 + kg * 8];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dqt[db] = mfma32(ld16(kta + db * 32 * DqSmem<D>::TS), dsf, dqt[db]);
+        for (int i = 0; i < 4; ++i) {
+          const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kk = kbi + j;
+            float x = s[kb][i * 4 + j] * a.scale_log2;
+            if (BIAS) x = fmaf(bias_row[min(kk, a.bias_len - 1)], kLog2e, x);
+            bool vis = true;
+            if (need_mask) vis = (kk < L) && (!CAUSAL || kk <= qpos);
+            const float p = vis ? exp2f_fast(x - lse2) : 0.f;
+            dp[kb][i * 4 + j] = p * (dp[kb][i * 4 + j] - dlt);
+          }
+        }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 dsf = to_bf16x8(dp[st >> 1], (st & 1) * 8);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dqt[db] = mfma32(tr_frag<D>(kt, st * 16, db, lane), dsf, dqt[db]);
+      }
     }
+    wait_vm_all();
+    __syncthreads();
   }
 
   if (!qok) return;
@@ -398,6 +441,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
   return hipGetLastError();
 
 hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s) {
+  constexpr int kThreads = kDkdvThreads;
   CPATTN_BWD_DISPATCH(dkdv_kernel)
 }
 

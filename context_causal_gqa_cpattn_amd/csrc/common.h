@@ -94,50 +94,83 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return pid < per * 8 ? (pid & 7) * per + (pid >> 3) : pid;
 }
 
-// LDS tile layouts for [rows][D] BF16 tiles written by LDS DMA (contiguous 1 KB per
-// wave instruction, so no padding): K-like tiles read with 16-byte row reads swap
-// 16-byte granules by (row & KMASK); V-like tiles read with transposing 8-byte reads
-// swap 64-byte chunks by (row & VMASK).  Both make the reads of one instruction
-// cover distinct LDS banks.
+// LDS tiles [rows][D] of BF16 are written by LDS DMA (1 KB contiguous per wave
+// instruction, so rows are unpadded) and read two ways: 16-byte row reads (A operands
+// whose contracted index runs along D) and transposing 8-byte reads (A operands whose
+// contracted index runs along the rows).  Granule g (16 bytes) of row r is stored at
+// granule g ^ swz(r), swz(r) = (r & 3) * 4 + ((r >> 2) & 3): sixteen consecutive rows
+// read at one granule hit sixteen distinct bank groups, and the 4 rows x 64 bytes of
+// one transposing read also do.
 template <int D>
-struct TileSwz {
-  static constexpr int G = D / 8;   // 16-byte granules per row
-  static constexpr int KMASK = G >= 16 ? 15 : G - 1;
-  static constexpr int C = D / 32;  // 64-byte chunks per row
-  static constexpr int VMASK = C >= 4 ? 3 : C - 1;
-};
+__device__ __forceinline__ int swz(int r) {
+  constexpr int G = D / 8;
+  return (((r & 3) << 2) | ((r >> 2) & 3)) & (G - 1);
+}
 
 // One 16-byte LDS DMA per lane: lane l's data lands at lds + 16*l bytes.
 __device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
   __builtin_amdgcn_global_load_lds((const void*)g, CPATTN_LDS(void, lds), 16, 0, 0);
 }
 
-// DMA rows [key0, key0+64) of K and V (row stride rs elements) into swizzled LDS
-// tiles.  Rows at or past L repeat row L-1 (finite data; they are masked later).
-template <int D>
-__device__ __forceinline__ void dma_kv_tile(uint16_t* kl, uint16_t* vl, const uint16_t* kbase,
-                                            const uint16_t* vbase, int64_t rs, int key0, int L,
-                                            int wave, int lane) {
-  constexpr int G = TileSwz<D>::G, KM = TileSwz<D>::KMASK, VM = TileSwz<D>::VMASK;
-  for (int i = __builtin_amdgcn_readfirstlane(wave); i < G; i += 4) {
+// DMA an R-row tile: tile row r comes from base + min(r, nvalid-1) * rs (rows past
+// the valid ones repeat the last valid row: finite data, masked by the caller).
+template <int D, int R, int NW = 4>
+__device__ __forceinline__ void dma_rows(uint16_t* lds, const uint16_t* base, int64_t rs,
+                                         int nvalid, int wave, int lane) {
+  constexpr int G = D / 8;
+  constexpr int NI = R * G / 64;  // wave instructions per tile
+  for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += NW) {
     const int idx = i * 64 + lane;
     const int r = idx / G, p = idx % G;
-    const int64_t key = min(key0 + r, L - 1);
-    dma16(kbase + key * rs + ((p ^ (r & KM)) * 8), kl + i * 512);
-    dma16(vbase + key * rs + ((((p >> 2) ^ (r & VM)) * 4 + (p & 3)) * 8), vl + i * 512);
+    const int64_t row = min(r, nvalid - 1);
+    dma16(base + row * rs + ((p ^ swz<D>(r)) * 8), lds + i * 512);
   }
 }
 
-// A operand of V^T P^T for 16 keys starting at row r0 - tr_row and 32 dims of block db,
-// read from a natural-layout [key][D] tile with two transposing LDS reads.  Lane l gets
-// V[k][32*db + l%32] for k = r0 - tr_row + 4*(l/32) + {0..3} and the same + 8, which is
-// the key order (sigma16) of a 32x32 accumulator's rows.
+// 16-byte read of logical granule g of row r.
 template <int D>
-__device__ __forceinline__ u32x4 tr_read_vt(const uint16_t* vt, int r0, int db, int tr_d) {
-  constexpr int VM = TileSwz<D>::VMASK;
-  const int pc = ((db ^ (r0 & VM)) * 32) + tr_d;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, vt + r0 * D + pc));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, vt + (r0 + 8) * D + pc));
+__device__ __forceinline__ u32x4 lds_row16(const uint16_t* t, int r, int g) {
+  return ld16(t + r * D + ((g ^ swz<D>(r)) * 8));
+}
+
+// A operand (32 x 16) whose rows are 32 columns [32*db, +32) of the tile and whose 16
+// contracted values are tile rows kr0 + sigma16(8*(lane/32) + e): two transposing reads.
+// Lane l gets tile[kr0 + 4*(l/32) + j][32*db + l%32] for j = 0..3, then the same + 8.
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const uint16_t* t, int kr0, int db, int lane) {
+  const int r = kr0 + (lane >> 5) * 4 + ((lane & 15) >> 2);
+  const int d = db * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const int gl = d >> 3, off = d & 7;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      CPATTN_LDS(v4i16, t + r * D + ((gl ^ swz<D>(r)) << 3) + off));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      CPATTN_LDS(v4i16, t + (r + 8) * D + ((gl ^ swz<D>(r + 8)) << 3) + off));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// One 16x16x32 BF16 MFMA with fp32 accumulation.
+//  A (16 x 32): lane l holds row l%16, the 8 k-values of lane group l/16.
+//  B (32 x 16): lane l holds column l%16, the same 8 k-values.
+//  C (16 x 16): lane l holds column l%16; element j is row 4*(l/16) + j.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// A operand (16 x 32) of a 16x16x32 product whose rows are columns [16*dblk, +16) of a
+// 32-row tile and whose contracted values are the tile's rows in the order of two stacked
+// 16x16 accumulators: lane group g, element e -> row 16*(e/4) + 4*g + e%4.  Two
+// transposing reads; lane l gets tile[4*(l/16) + j][16*dblk + l%16], then rows + 16.
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag16(const uint16_t* t, int dblk, int lane) {
+  const int r = (lane >> 4) * 4 + ((lane & 15) >> 2);
+  const int d = dblk * 16 + 4 * (lane & 3);
+  const int gl = d >> 3, off = d & 7;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      CPATTN_LDS(v4i16, t + r * D + ((gl ^ swz<D>(r)) << 3) + off));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      CPATTN_LDS(v4i16, t + (r + 16) * D + ((gl ^ swz<D>(r + 16)) << 3) + off));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }

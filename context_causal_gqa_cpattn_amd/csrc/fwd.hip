@@ -31,7 +31,6 @@ template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NST = D / 16;  // 16-wide k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  constexpr int KM = TileSwz<D>::KMASK, VM = TileSwz<D>::VMASK;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][kBN * D];
 
@@ -84,19 +83,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)g * D;
 
-  // per-lane offsets of the transposing V reads (see tr_read_vt)
-  const int tr_row = (lane >> 5) * 4 + ((lane & 15) >> 2);
-  const int tr_d = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-
-  if (n_tiles > 0) dma_kv_tile<D>(lds_k[0], lds_v[0], kbase, vbase, kv_stride, 0, L, wave, lane);
+  if (n_tiles > 0) {
+    dma_rows<D, kBN>(lds_k[0], kbase, kv_stride, L, wave, lane);
+    dma_rows<D, kBN>(lds_v[0], vbase, kv_stride, L, wave, lane);
+  }
   wait_vm_all();
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int key0 = t * kBN;
     const int buf = t & 1;
-    if (t + 1 < n_tiles)
-      dma_kv_tile<D>(lds_k[buf ^ 1], lds_v[buf ^ 1], kbase, vbase, kv_stride, key0 + kBN, L, wave, lane);
+    if (t + 1 < n_tiles) {
+      const int64_t nxt = (int64_t)(key0 + kBN) * kv_stride;
+      dma_rows<D, kBN>(lds_k[buf ^ 1], kbase + nxt, kv_stride, L - key0 - kBN, wave, lane);
+      dma_rows<D, kBN>(lds_v[buf ^ 1], vbase + nxt, kv_stride, L - key0 - kBN, wave, lane);
+    }
 
     if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
       const uint16_t* kt = lds_k[buf];
@@ -106,10 +107,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
-        const uint16_t* krow = kt + (kb * 32 + col) * D;
 #pragma unroll
         for (int st = 0; st < NST; ++st)
-          s[kb] = mfma32(ld16(krow + (((st * 2 + kg) ^ (col & KM)) * 8)), qf[st], s[kb]);
+          s[kb] = mfma32(lds_row16<D>(kt, kb * 32 + col, st * 2 + kg), qf[st], s[kb]);
       }
 
       // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.
@@ -167,10 +167,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const u32x4 pf = to_bf16x8(s[st >> 1], (st & 1) * 8);
-        const int r0 = st * 16 + tr_row;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          oacc[db] = mfma32(tr_read_vt<D>(vt, r0, db, tr_d), pf, oacc[db]);
+          oacc[db] = mfma32(tr_frag<D>(vt, st * 16, db, lane), pf, oacc[db]);
       }
     }
     wait_vm_all();
