@@ -58,6 +58,33 @@ def parse():
     return ap.parse_args()
 
 
+def layout_copy_rates(cp, torch, reps=10):
+    """BHSD <-> THD copies at B8/H32/S2048/D128 (256 MiB moved per call), GB/s."""
+    B, H, S, D = 8, 32, 2048, 128
+    x = torch.empty((B, H, S, D), dtype=torch.bfloat16, device="cuda").normal_()
+    so = torch.arange(B, dtype=torch.int32, device="cuda") * S
+    sl = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    thd = torch.empty((B * S, H, D), dtype=torch.bfloat16, device="cuda")
+    back = torch.empty_like(x)
+    err = cp.new_dev_err()
+    out = {}
+    for name, fn in (("pack", lambda: cp.pack(x, so, sl, B * S, thd=thd, dev_err=err)),
+                     ("unpack", lambda: cp.unpack(thd, so, sl, B, S, bhsd=back, dev_err=err))):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name + "_gbs"] = round(2 * x.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+        out[name + "_ms"] = round(ms, 4)
+    cp.check(err)
+    out["bytes_per_call"] = 2 * x.numel() * 2
+    return out
+
+
 def cpu_baseline(w, q, k, v, do, bias, budget_s):
     """The FP64 oracle, as it stands, on whole (sequence, KV-head group) samples."""
     import oracle
@@ -161,6 +188,8 @@ def main():
                                      for i in range(args.steps)])) for j, n in enumerate(names)}
     ms = wall * 1e3 / args.steps
 
+    copy = layout_copy_rates(cp, torch)
+
     pairs = visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq
     D = w.head_dim
     flop = pairs * 14 * D
@@ -197,6 +226,7 @@ def main():
         "bwd_tflops": round(bwd_tflops, 2),
         "kernel_ms": {n: round(x, 4) for n, x in per_kernel.items()},
         "prepass_gbs": round(pre_bytes / (per_kernel["prepass"] * 1e-3) / 1e9, 1),
+        "layout_copy": copy,
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

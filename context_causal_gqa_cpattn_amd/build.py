@@ -33,13 +33,21 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source extra flags: MFMA accumulators in arch VGPRs, so the softmax rescale of the
+# output accumulators is plain VALU work instead of AGPR round trips.
+FILE_FLAGS = {
+    "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, resource_usage: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if resource_usage:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

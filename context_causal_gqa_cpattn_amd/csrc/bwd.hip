@@ -117,8 +117,8 @@ __device__ __forceinline__ void dma_q_do(uint16_t* lq, uint16_t* ldo, const Attn
   const int64_t rs = (int64_t)a.hq * D;
   const int64_t off = ((int64_t)it.ch.q_row + it.qt * kBM) * rs + (int64_t)h * D;
   const int nq = min(kBM, it.ch.len - it.qt * kBM);
-  dma_rows<D, kBM, kDkdvWaves>(lq, a.q + off, rs, nq, wave, lane);
-  dma_rows<D, kBM, kDkdvWaves>(ldo, a.dout + off, rs, nq, wave, lane);
+  dma_rows<D, kBM, kDkdvWaves, 1>(lq, a.q + off, rs, nq, wave, lane);
+  dma_rows<D, kBM, kDkdvWaves, 1>(ldo, a.dout + off, rs, nq, wave, lane);
 }
 
 // LSE (as base-2) and Delta of tile row `r` (clamped to the valid rows).
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
         dp[mb] = f32x4{};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          s[mb] = mfma16(lds_row16<D>(qt_l, mb * 16 + n, st * 4 + lg), kf[st], s[mb]);
-          dp[mb] = mfma16(lds_row16<D>(dt_l, mb * 16 + n, st * 4 + lg), vf[st], dp[mb]);
+          s[mb] = mfma16(lds_row16<D, 1>(qt_l, mb * 16 + n, st * 4 + lg), kf[st], s[mb]);
+          dp[mb] = mfma16(lds_row16<D, 1>(dt_l, mb * 16 + n, st * 4 + lg), vf[st], dp[mb]);
         }
       }
       const bool need_mask = (nk < 16) || (nq < kBM) || (CAUSAL && tile_pos0 < wkey0 + 15);
@@ -281,6 +281,29 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
 //   dQ^T += K^T dS^T              (A = K^T by transposing reads of the same K tile)
 
 constexpr int kBNq = 64;  // keys per KV tile in the dQ kernel
+
+// dS^T = P^T (dP^T - Delta) for one 64-key tile, in place in dp (lane = query).
+template <bool BIAS, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void ds_tile(f32x16 (&s)[2], f32x16 (&dp)[2], float c, const float* bias_row,
+                                        int key0, int L, int qpos, int kg, int bias_len, float lse2,
+                                        float dlt) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = kbi + j;
+        float x = s[kb][i * 4 + j] * c;
+        if (BIAS) x = fmaf(bias_row[min(kk, bias_len - 1)], kLog2e, x);
+        bool vis = true;
+        if (MASK) vis = (kk < L) && (!CAUSAL || kk <= qpos);
+        const float p = vis ? exp2f_fast(x - lse2) : 0.f;
+        dp[kb][i * 4 + j] = p * (dp[kb][i * 4 + j] - dlt);
+      }
+    }
+}
 
 template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
@@ -369,22 +392,12 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
         }
       }
       const bool need_mask = (key0 + kBNq > L) || (CAUSAL && key0 + kBNq - 1 > wave_first_pos);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int kk = kbi + j;
-            float x = s[kb][i * 4 + j] * a.scale_log2;
-            if (BIAS) x = fmaf(bias_row[min(kk, a.bias_len - 1)], kLog2e, x);
-            bool vis = true;
-            if (need_mask) vis = (kk < L) && (!CAUSAL || kk <= qpos);
-            const float p = vis ? exp2f_fast(x - lse2) : 0.f;
-            dp[kb][i * 4 + j] = p * (dp[kb][i * 4 + j] - dlt);
-          }
-        }
+      if (need_mask) {
+        asm volatile("" ::: "memory");
+        ds_tile<BIAS, true, CAUSAL>(s, dp, a.scale_log2, bias_row, key0, L, qpos, kg, a.bias_len, lse2, dlt);
+      } else {
+        ds_tile<BIAS, false, CAUSAL>(s, dp, a.scale_log2, bias_row, key0, L, qpos, kg, a.bias_len, lse2, dlt);
+      }
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const u32x4 dsf = to_bf16x8(dp[st >> 1], (st & 1) * 8);

@@ -101,10 +101,13 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
 // granule g ^ swz(r), swz(r) = (r & 3) * 4 + ((r >> 2) & 3): sixteen consecutive rows
 // read at one granule hit sixteen distinct bank groups, and the 4 rows x 64 bytes of
 // one transposing read also do.
-template <int D>
+template <int D, int KIND = 0>
 __device__ __forceinline__ int swz(int r) {
   constexpr int G = D / 8;
-  return (((r & 3) << 2) | ((r >> 2) & 3)) & (G - 1);
+  if (KIND == 0) return (((r & 3) << 2) | ((r >> 2) & 3)) & (G - 1);
+  // KIND 1 (tiles read by 16x16x32 operands): sixteen rows at one granule still hit
+  // sixteen bank groups, and the 8 rows x 32 bytes of half a 16x16 transposing read do.
+  return (((r & 7) << 1) | ((r >> 3) & 1)) & (G - 1);
 }
 
 // One 16-byte LDS DMA per lane: lane l's data lands at lds + 16*l bytes.
@@ -114,7 +117,7 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
 
 // DMA an R-row tile: tile row r comes from base + min(r, nvalid-1) * rs (rows past
 // the valid ones repeat the last valid row: finite data, masked by the caller).
-template <int D, int R, int NW = 4>
+template <int D, int R, int NW = 4, int KIND = 0>
 __device__ __forceinline__ void dma_rows(uint16_t* lds, const uint16_t* base, int64_t rs,
                                          int nvalid, int wave, int lane) {
   constexpr int G = D / 8;
@@ -123,14 +126,14 @@ __device__ __forceinline__ void dma_rows(uint16_t* lds, const uint16_t* base, in
     const int idx = i * 64 + lane;
     const int r = idx / G, p = idx % G;
     const int64_t row = min(r, nvalid - 1);
-    dma16(base + row * rs + ((p ^ swz<D>(r)) * 8), lds + i * 512);
+    dma16(base + row * rs + ((p ^ swz<D, KIND>(r)) * 8), lds + i * 512);
   }
 }
 
 // 16-byte read of logical granule g of row r.
-template <int D>
+template <int D, int KIND = 0>
 __device__ __forceinline__ u32x4 lds_row16(const uint16_t* t, int r, int g) {
-  return ld16(t + r * D + ((g ^ swz<D>(r)) * 8));
+  return ld16(t + r * D + ((g ^ swz<D, KIND>(r)) * 8));
 }
 
 // A operand (32 x 16) whose rows are 32 columns [32*db, +32) of the tile and whose 16
@@ -168,9 +171,9 @@ __device__ __forceinline__ u32x4 tr_frag16(const uint16_t* t, int dblk, int lane
   const int d = dblk * 16 + 4 * (lane & 3);
   const int gl = d >> 3, off = d & 7;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      CPATTN_LDS(v4i16, t + r * D + ((gl ^ swz<D>(r)) << 3) + off));
+      CPATTN_LDS(v4i16, t + r * D + ((gl ^ swz<D, 1>(r)) << 3) + off));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      CPATTN_LDS(v4i16, t + (r + 16) * D + ((gl ^ swz<D>(r + 16)) << 3) + off));
+      CPATTN_LDS(v4i16, t + (r + 16) * D + ((gl ^ swz<D, 1>(r + 16)) << 3) + off));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }

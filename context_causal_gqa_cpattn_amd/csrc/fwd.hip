@@ -27,6 +27,39 @@ namespace cpattn {
 
 constexpr int kBN = 64;  // keys per KV tile
 
+// Scores of one 64-key tile in base 2 (+ bias), masked when MASK; returns the lane max.
+// Element r of block kb is key key0 + 32 kb + 8 (r/4) + 4 kg + r%4.
+template <bool BIAS, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float* bias_row, int key0,
+                                           int L, int qpos, int kg, int bias_len, float& mx) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
+      f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+      if (BIAS) {
+        if (kbi + 3 < L && (bias_len & 3) == 0)
+          bv = *reinterpret_cast<const f32x4*>(bias_row + kbi);
+        else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[j] = (kbi + j < L) ? bias_row[kbi + j] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = s[kb][i * 4 + j] * c;
+        if (BIAS) x = fmaf(bv[j], kLog2e, x);
+        if (MASK) {
+          const int key = kbi + j;
+          x = ((key < L) && (!CAUSAL || key <= qpos)) ? x : -INFINITY;
+        }
+        s[kb][i * 4 + j] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+}
+
 template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NST = D / 16;  // 16-wide k-steps over the head dim
@@ -102,48 +135,40 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
       const uint16_t* kt = lds_k[buf];
       const uint16_t* vt = lds_v[buf];
-      // S^T for two 32-key blocks.
-      f32x16 s[2];
+      // S^T for two 32-key blocks, as two interleaved accumulator chains; the LDS
+      // fragments for step st+1 are requested before the MFMAs of step st.
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      {
+        u32x4 ka = lds_row16<D>(kt, col, kg), kb_ = lds_row16<D>(kt, 32 + col, kg);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-          s[kb] = mfma32(lds_row16<D>(kt, kb * 32 + col, st * 2 + kg), qf[st], s[kb]);
+        for (int st = 0; st < NST; ++st) {
+          u32x4 na = ka, nb = kb_;
+          if (st + 1 < NST) {
+            na = lds_row16<D>(kt, col, (st + 1) * 2 + kg);
+            nb = lds_row16<D>(kt, 32 + col, (st + 1) * 2 + kg);
+          }
+          s[0] = mfma32(ka, qf[st], s[0]);
+          s[1] = mfma32(kb_, qf[st], s[1]);
+          ka = na;
+          kb_ = nb;
+        }
       }
 
-      // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.
+      // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.  The
+      // masked and unmasked tiles take separate, wave-uniform paths.
       const bool need_mask = (key0 + kBN > L) || (CAUSAL && key0 + kBN - 1 > wave_first_pos);
       float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
-          f32x4 bv = {0.f, 0.f, 0.f, 0.f};
-          if (BIAS) {
-            if (kbi + 3 < L && (a.bias_len & 3) == 0)
-              bv = *reinterpret_cast<const f32x4*>(bias_row + kbi);
-            else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) bv[j] = (kbi + j < L) ? bias_row[kbi + j] : 0.f;
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float x = s[kb][i * 4 + j] * a.scale_log2;
-            if (BIAS) x = fmaf(bv[j], kLog2e, x);
-            if (need_mask) {
-              const int key = kbi + j;
-              x = ((key < L) && (!CAUSAL || key <= qpos)) ? x : -INFINITY;
-            }
-            s[kb][i * 4 + j] = x;
-            mx = fmaxf(mx, x);
-          }
-        }
+      if (need_mask) {
+        asm volatile("" ::: "memory");
+        scale_tile<BIAS, true, CAUSAL>(s, a.scale_log2, bias_row, key0, L, qpos, kg, a.bias_len, mx);
+      } else {
+        scale_tile<BIAS, false, CAUSAL>(s, a.scale_log2, bias_row, key0, L, qpos, kg, a.bias_len, mx);
+      }
       mx = fmaxf(mx, xor32(mx));
       // Lazy rescale: move the reference max only when it grows by more than 8 (x256).
-      if (__any(mx > m_run + 8.f)) {
+      if (__builtin_expect(__any(mx > m_run + 8.f), 0)) {
+        // A real branch: the rescale must not be if-converted into every tile.
+        asm volatile("" ::: "memory");
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2f_fast(m_run - m_new);
 #pragma unroll
@@ -163,13 +188,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
         }
       l_run += rs;
 
-      // O^T += V^T P^T over four 16-key steps.
+      // O^T += V^T P^T over four 16-key steps; the V^T fragment of the next MFMA is
+      // requested before the current one issues.
+      {
+        u32x4 pf[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const u32x4 pf = to_bf16x8(s[st >> 1], (st & 1) * 8);
+        for (int st = 0; st < 4; ++st) pf[st] = to_bf16x8(s[st >> 1], (st & 1) * 8);
+        u32x4 va = tr_frag<D>(vt, 0, 0, lane);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          oacc[db] = mfma32(tr_frag<D>(vt, st * 16, db, lane), pf, oacc[db]);
+        for (int it = 0; it < 4 * NDB; ++it) {
+          const int st = it / NDB, db = it % NDB;
+          u32x4 nv = va;
+          if (it + 1 < 4 * NDB) nv = tr_frag<D>(vt, ((it + 1) / NDB) * 16, (it + 1) % NDB, lane);
+          oacc[db] = mfma32(va, pf[st], oacc[db]);
+          va = nv;
+        }
       }
     }
     wait_vm_all();
