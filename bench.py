@@ -58,6 +58,34 @@ def parse():
     return ap.parse_args()
 
 
+def kernel_source_hash() -> str:
+    """Short hash of the HIP sources (what the counter summaries were taken on)."""
+    import hashlib
+    d = os.path.join(ROOT, "context_causal_gqa_cpattn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    src_hash, val = None, None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("kernel_source_hash:"):
+            src_hash = line.split(":", 1)[1].strip().strip("`")
+        if line.startswith(f"hbm_bytes_per_launch[{kernel}]:"):
+            val = float(line.split(":", 1)[1].strip().strip("`"))
+    return val if (val is not None and src_hash == kernel_source_hash()) else None
+
+
 def layout_copy_rates(cp, torch, reps=10):
     """BHSD <-> THD copies at B8/H32/S2048/D128 (256 MiB moved per call), GB/s."""
     B, H, S, D = 8, 32, 2048, 128
@@ -230,7 +258,8 @@ def main():
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(w.name, dom),
                      "algorithmic_flop_per_launch": dom_flop},
     }
     if not args.no_cpu:
