@@ -174,7 +174,6 @@ def main():
     dv = torch.empty_like(v)
     dbias = torch.empty_like(bias) if bias is not None else None
     ws = torch.empty(max(cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
-    delta = ws[: w.hq * w.q_rows * 4].view(torch.float32)
     err = cp.new_dev_err()
 
     names = ["fwd", "validate", "prepass", "dkdv", "dq"] + (["dbias"] if bias is not None else [])
@@ -188,14 +187,14 @@ def main():
         mark(1)
         cp.validate(prob, lay, err)
         mark(2)
-        cp.bwd_prepass(prob, lay, o, do, delta, err)
+        cp.bwd_prepass(prob, lay, q, o, do, ws, err)
         mark(3)
-        cp.bwd_dkdv(prob, lay, q, k, v, bias, lse, do, delta, dk, dv, False, err)
+        cp.bwd_dkdv(prob, lay, q, k, v, bias, lse, do, ws, dk, dv, False, err)
         mark(4)
-        cp.bwd_dq(prob, lay, q, k, v, bias, lse, do, delta, dq, err)
+        cp.bwd_dq(prob, lay, q, k, v, bias, lse, do, ws, dq, err)
         mark(5)
         if bias is not None:
-            cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, dbias, ws, err)
+            cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, ws, dbias, err)
             mark(6)
 
     for _ in range(args.warmup):
@@ -230,7 +229,10 @@ def main():
     dom = max((n for n in per_kernel if n in algo), key=lambda n: per_kernel[n])
     dom_flop = pairs * algo[dom]
     achieved = dom_flop / (per_kernel[dom] * 1e-3) / 1e12
-    pre_bytes = 2 * w.q_valid_rows().sum() * w.hq * D * 2 + 4 * w.q_valid_rows().sum() * w.hq
+    # pre-pass: reads Q, O, dO; writes Delta and the Q^T / dO^T tiles (32-query, zero-padded)
+    tile_rows = int(sum(-(-int(n) // 32) * 32 for n in w.chunks[:, 3]))
+    pre_bytes = (3 * w.q_valid_rows().sum() * w.hq * D * 2 + 4 * w.q_valid_rows().sum() * w.hq
+                 + 2 * tile_rows * w.hq * D * 2)
 
     line = {
         "metric": METRIC,

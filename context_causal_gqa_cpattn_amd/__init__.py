@@ -83,11 +83,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "cpattn_fwd": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
         "cpattn_bwd": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                        ctypes.c_int, _vp, sz, _vp, _vp],
-        "cpattn_bwd_prepass": [P, _vp, _vp, _vp, _vp, _vp, _vp],
-        "cpattn_bwd_dkdv": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        "cpattn_bwd_prepass": [P, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
+        "cpattn_bwd_dkdv": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp,
                             ctypes.c_int, _vp, _vp],
-        "cpattn_bwd_dq": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
-        "cpattn_bwd_dbias": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
+        "cpattn_bwd_dq": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
+        "cpattn_bwd_dbias": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
         "cpattn_pack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
         "cpattn_unpack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
     }
@@ -263,33 +263,34 @@ def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optiona
     return dq, dk, dv, dbias, dev_err
 
 
-def bwd_prepass(prob: Problem, layout: Layout, o, do, delta, dev_err, stream=None):
+def bwd_prepass(prob: Problem, layout: Layout, q, o, do, ws, dev_err, stream=None):
+    """Delta and the transposed Q/dO tiles into the backward workspace `ws` (uint8)."""
     lib = load()
-    _check(lib.cpattn_bwd_prepass(ctypes.byref(prob), _ptr(layout.chunks), _ptr(o), _ptr(do),
-                                  _ptr(delta), _ptr(dev_err), _stream(stream)))
+    _check(lib.cpattn_bwd_prepass(ctypes.byref(prob), _ptr(q), _ptr(layout.chunks), _ptr(o), _ptr(do),
+                                  _ptr(ws), ws.numel(), _ptr(dev_err), _stream(stream)))
 
 
-def bwd_dkdv(prob: Problem, layout: Layout, q, k, v, bias, lse, do, delta, dk, dv,
+def bwd_dkdv(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dk, dv,
              dkv_accumulate: bool, dev_err, stream=None):
     lib = load()
     _check(lib.cpattn_bwd_dkdv(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
                                _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
-                               _ptr(do), _ptr(delta), _ptr(dk), _ptr(dv), 1 if dkv_accumulate else 0,
-                               _ptr(dev_err), _stream(stream)))
+                               _ptr(do), _ptr(ws), ws.numel(), _ptr(dk), _ptr(dv),
+                               1 if dkv_accumulate else 0, _ptr(dev_err), _stream(stream)))
 
 
-def bwd_dq(prob: Problem, layout: Layout, q, k, v, bias, lse, do, delta, dq, dev_err, stream=None):
+def bwd_dq(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dq, dev_err, stream=None):
     lib = load()
     _check(lib.cpattn_bwd_dq(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
                              _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
-                             _ptr(do), _ptr(delta), _ptr(dq), _ptr(dev_err), _stream(stream)))
+                             _ptr(do), _ptr(ws), ws.numel(), _ptr(dq), _ptr(dev_err), _stream(stream)))
 
 
-def bwd_dbias(prob: Problem, layout: Layout, q, k, v, bias, lse, do, dbias, ws, dev_err, stream=None):
+def bwd_dbias(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dbias, dev_err, stream=None):
     lib = load()
     _check(lib.cpattn_bwd_dbias(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
                                 _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
-                                _ptr(do), _ptr(dbias), _ptr(ws), ws.numel(), _ptr(dev_err),
+                                _ptr(do), _ptr(ws), ws.numel(), _ptr(dbias), _ptr(dev_err),
                                 _stream(stream)))
 
 

@@ -83,6 +83,8 @@ struct Plan {
   int64_t delta_bytes;  // rounded to 256
   int parts;            // dBias partitions
   int64_t partial_bytes;
+  // backward workspace: delta | tile_base | Q^T tiles | dO^T tiles | dBias partials
+  int64_t off_tiles, off_qt, off_dot, off_partials, ws_core;
   dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias;
   int bpc_fwd, bpc_prepass, kv_tiles;
 };
@@ -134,7 +136,6 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.grid_fwd = dim3((unsigned)gx_fwd, (unsigned)(p->hq / pl.hpw));
   if (gx_fwd * (p->hq / pl.hpw) > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_fwd1d = dim3((unsigned)(gx_fwd * (p->hq / pl.hpw)));
-  pl.grid_prepass = dim3((unsigned)gx_pre);
   if (gx_kv * p->hkv > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_dkdv = dim3((unsigned)(gx_kv * p->hkv));
 
@@ -150,6 +151,15 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
     pl.grid_dbias = dim3((unsigned)cdiv(p->bias_len, kDbiasKeys), (unsigned)cdiv(p->bias_len, kDbiasPos),
                          (unsigned)(p->hq * pl.parts));
   }
+  // Transposed 32-query tiles: at most ceil(q_rows/32) + C of them.
+  const int64_t max_tiles = cdiv(p->q_rows, kPrepassRows) + p->num_chunks;
+  const int64_t tile_bytes = max_tiles * p->hq * (int64_t)D * kPrepassRows * 2;
+  pl.off_tiles = pl.delta_bytes;
+  pl.off_qt = pl.off_tiles + round256(((int64_t)p->num_chunks + 1) * 4);
+  pl.off_dot = pl.off_qt + round256(tile_bytes);
+  pl.off_partials = pl.off_dot + round256(tile_bytes);
+  pl.ws_core = pl.off_partials;
+  pl.grid_prepass = dim3((unsigned)gx_pre, (unsigned)p->hq);
   return CPATTN_OK;
 }
 
@@ -231,7 +241,7 @@ size_t cpattn_workspace_size(const cpattn_problem* p, int op) {
   Plan pl;
   if (make_plan(p, pl)) return 0;
   if (op == CPATTN_OP_FWD) return 0;
-  if (op == CPATTN_OP_BWD) return (size_t)(pl.delta_bytes + pl.partial_bytes);
+  if (op == CPATTN_OP_BWD) return (size_t)(pl.ws_core + pl.partial_bytes);
   return 0;
 }
 
@@ -308,8 +318,13 @@ int bwd_common_checks(const cpattn_problem* p, const Plan& pl, const void* q, co
 
 AttnArgs bwd_args(const cpattn_problem* p, const Plan& pl, const void* q, const void* k, const void* v,
                   const int32_t* so, const int32_t* sl, const int32_t* cm, const float* bias,
-                  const float* lse, const void* dout, const float* delta, const int32_t* dev_err) {
+                  const float* lse, const void* dout, const void* ws, const int32_t* dev_err) {
   AttnArgs a = base_args(p, pl);
+  const char* w = (const char*)ws;
+  const float* delta = (const float*)w;
+  a.tile_base = (const int32_t*)(w + pl.off_tiles);
+  a.qt = (const uint16_t*)(w + pl.off_qt);
+  a.dot = (const uint16_t*)(w + pl.off_dot);
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
@@ -324,16 +339,23 @@ AttnArgs bwd_args(const cpattn_problem* p, const Plan& pl, const void* q, const 
   return a;
 }
 
-int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, const void* o,
-                    const void* dout, float* delta, const int32_t* dev_err, hipStream_t s) {
-  if (empty(pl.grid_prepass)) return CPATTN_OK;
+int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, const void* q,
+                    const void* o, const void* dout, void* ws, const int32_t* dev_err, hipStream_t s) {
   AttnArgs a = base_args(p, pl);
+  char* w = (char*)ws;
+  a.q = (const uint16_t*)q;
   a.o = (const uint16_t*)o;
   a.dout = (const uint16_t*)dout;
-  a.delta_out = delta;
+  a.delta_out = (float*)w;
+  a.tile_base_out = (int32_t*)(w + pl.off_tiles);
+  a.tile_base = a.tile_base_out;
+  a.qt_out = (uint16_t*)(w + pl.off_qt);
+  a.dot_out = (uint16_t*)(w + pl.off_dot);
   a.chunks = cm;
   a.dev_err = dev_err;
   a.blocks_per_chunk = pl.bpc_prepass;
+  int r = hip_check(launch_tile_scan(a, s), "tile scan launch");
+  if (r || empty(pl.grid_prepass)) return r;
   return hip_check(launch_prepass(a, pl.D, pl.grid_prepass, s), "pre-pass launch");
 }
 
@@ -356,7 +378,7 @@ int enqueue_dq(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dq, hi
 int enqueue_dbias(const cpattn_problem* p, const Plan& pl, AttnArgs a, float* dbias, void* ws,
                   hipStream_t s) {
   if (!pl.bias || empty(pl.grid_dbias)) return CPATTN_OK;
-  float* partial = pl.parts > 1 ? (float*)((char*)ws + pl.delta_bytes) : dbias;
+  float* partial = pl.parts > 1 ? (float*)((char*)ws + pl.off_partials) : dbias;
   a.dbias = partial;
   int r = hip_check(launch_dbias(a, pl.D, pl.grid_dbias, s), "dBias launch");
   if (r || pl.parts == 1) return r;
@@ -384,7 +406,7 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
   if (dbias && !pl.bias) return fail(CPATTN_EINVAL, "dbias given but bias_len is 0");
   if (dbias && !aligned(dbias, 16)) return fail(CPATTN_EINVAL, "dbias is not 16-byte aligned");
   if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
-  const int64_t need = pl.delta_bytes + (dbias ? pl.partial_bytes : 0);
+  const int64_t need = pl.ws_core + (dbias ? pl.partial_bytes : 0);
   if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
   if ((r = check_ptr(ws, need, 256, "ws"))) return r;
   const int64_t dbias_bytes = dbias ? pl.bias_bytes : 0;
@@ -398,113 +420,118 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
   if ((r = alias_audit(rs))) return r;
 
   hipStream_t s = (hipStream_t)stream;
-  float* delta = (float*)ws;
   if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
-  if ((r = enqueue_prepass(p, pl, q_chunk_map, o, dout, delta, dev_err, s))) return r;
-  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, delta, dev_err);
+  if ((r = enqueue_prepass(p, pl, q_chunk_map, q, o, dout, ws, dev_err, s))) return r;
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
   if ((r = enqueue_dq(p, pl, a, dq, s))) return r;
   if (dbias) return enqueue_dbias(p, pl, a, dbias, ws, s);
   return CPATTN_OK;
 }
 
-int cpattn_bwd_prepass(const cpattn_problem* p, const int32_t* q_chunk_map, const void* o,
-                       const void* dout, float* delta, const int32_t* dev_err,
-                       cpattn_stream_t stream) {
+int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
+                       const void* o, const void* dout, void* ws, size_t ws_bytes,
+                       const int32_t* dev_err, cpattn_stream_t stream) {
   g_last_error.clear();
   Plan pl;
   int r;
   if ((r = make_plan(p, pl))) return r;
-  if ((r = check_ptr(o, pl.q_bytes, 16, "o")) || (r = check_ptr(dout, pl.q_bytes, 16, "dout")) ||
-      (r = check_ptr(delta, pl.stat_bytes, 4, "delta")) ||
+  if ((r = check_ptr(q, pl.q_bytes, 16, "q")) || (r = check_ptr(o, pl.q_bytes, 16, "o")) ||
+      (r = check_ptr(dout, pl.q_bytes, 16, "dout")) ||
       (r = check_ptr(q_chunk_map, (uint64_t)p->num_chunks * 16, 16, "q_chunk_map")) ||
       (r = check_ptr(dev_err, 4, 4, "dev_err")))
     return r;
-  std::vector<Range> rs = {rng("o", o, pl.q_bytes, false), rng("dout", dout, pl.q_bytes, false),
+  if ((int64_t)ws_bytes < pl.ws_core)
+    return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)pl.ws_core);
+  if ((r = check_ptr(ws, pl.ws_core, 256, "ws"))) return r;
+  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false), rng("o", o, pl.q_bytes, false),
+                           rng("dout", dout, pl.q_bytes, false),
                            rng("q_chunk_map", q_chunk_map, (uint64_t)p->num_chunks * 16, false),
-                           rng("dev_err", dev_err, 4, false), rng("delta", delta, pl.stat_bytes, true)};
+                           rng("dev_err", dev_err, 4, false), rng("ws", ws, pl.ws_core, true)};
   if ((r = alias_audit(rs))) return r;
-  return enqueue_prepass(p, pl, q_chunk_map, o, dout, delta, dev_err, (hipStream_t)stream);
+  return enqueue_prepass(p, pl, q_chunk_map, q, o, dout, ws, dev_err, (hipStream_t)stream);
 }
+
+namespace {
+// Shared checks of the dK/dV, dQ and dBias steps, which read the pre-pass workspace.
+int step_checks(const cpattn_problem* p, const Plan& pl, const void* q, const void* k, const void* v,
+                const int32_t* so, const int32_t* sl, const int32_t* cm, const float* bias,
+                const float* lse, const void* dout, const void* ws, size_t ws_bytes, int64_t need,
+                const int32_t* dev_err, std::vector<Range>& rs) {
+  int r;
+  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, so, sl, cm, dev_err))) return r;
+  if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
+  if ((r = check_ptr(ws, need, 256, "ws"))) return r;
+  rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
+        rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
+        rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
+        rng("ws (pre-pass results)", ws, pl.ws_core, false)};
+  add_descriptor_ranges(rs, p, so, sl, cm, dev_err, false);
+  return CPATTN_OK;
+}
+}  // namespace
 
 int cpattn_bwd_dkdv(const cpattn_problem* p, const void* q, const void* k, const void* v,
                     const int32_t* seq_offsets, const int32_t* seq_lens,
                     const int32_t* q_chunk_map, const float* bias, const float* lse,
-                    const void* dout, const float* delta, void* dk, void* dv,
+                    const void* dout, const void* ws, size_t ws_bytes, void* dk, void* dv,
                     int dkv_accumulate, const int32_t* dev_err, cpattn_stream_t stream) {
   g_last_error.clear();
   Plan pl;
   int r;
+  std::vector<Range> rs;
   if ((r = make_plan(p, pl))) return r;
-  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
-                             dev_err)))
+  if ((r = step_checks(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws,
+                       ws_bytes, pl.ws_core, dev_err, rs)))
     return r;
-  if ((r = check_ptr(delta, pl.stat_bytes, 4, "delta")) || (r = check_ptr(dk, pl.kv_bytes, 16, "dk")) ||
-      (r = check_ptr(dv, pl.kv_bytes, 16, "dv")))
-    return r;
+  if ((r = check_ptr(dk, pl.kv_bytes, 16, "dk")) || (r = check_ptr(dv, pl.kv_bytes, 16, "dv"))) return r;
   if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
-  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
-                           rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
-                           rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
-                           rng("delta", delta, pl.stat_bytes, false), rng("dk", dk, pl.kv_bytes, true),
-                           rng("dv", dv, pl.kv_bytes, true)};
-  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  rs.push_back(rng("dk", dk, pl.kv_bytes, true));
+  rs.push_back(rng("dv", dv, pl.kv_bytes, true));
   if ((r = alias_audit(rs))) return r;
-  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, delta, dev_err);
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   return enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, (hipStream_t)stream);
 }
 
 int cpattn_bwd_dq(const cpattn_problem* p, const void* q, const void* k, const void* v,
                   const int32_t* seq_offsets, const int32_t* seq_lens,
                   const int32_t* q_chunk_map, const float* bias, const float* lse,
-                  const void* dout, const float* delta, void* dq, const int32_t* dev_err,
-                  cpattn_stream_t stream) {
+                  const void* dout, const void* ws, size_t ws_bytes, void* dq,
+                  const int32_t* dev_err, cpattn_stream_t stream) {
   g_last_error.clear();
   Plan pl;
   int r;
+  std::vector<Range> rs;
   if ((r = make_plan(p, pl))) return r;
-  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
-                             dev_err)))
+  if ((r = step_checks(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws,
+                       ws_bytes, pl.ws_core, dev_err, rs)))
     return r;
-  if ((r = check_ptr(delta, pl.stat_bytes, 4, "delta")) || (r = check_ptr(dq, pl.q_bytes, 16, "dq")))
-    return r;
-  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
-                           rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
-                           rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
-                           rng("delta", delta, pl.stat_bytes, false), rng("dq", dq, pl.q_bytes, true)};
-  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  if ((r = check_ptr(dq, pl.q_bytes, 16, "dq"))) return r;
+  rs.push_back(rng("dq", dq, pl.q_bytes, true));
   if ((r = alias_audit(rs))) return r;
-  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, delta, dev_err);
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   return enqueue_dq(p, pl, a, dq, (hipStream_t)stream);
 }
 
 int cpattn_bwd_dbias(const cpattn_problem* p, const void* q, const void* k, const void* v,
                      const int32_t* seq_offsets, const int32_t* seq_lens,
                      const int32_t* q_chunk_map, const float* bias, const float* lse,
-                     const void* dout, float* dbias, void* ws, size_t ws_bytes,
+                     const void* dout, void* ws, size_t ws_bytes, float* dbias,
                      const int32_t* dev_err, cpattn_stream_t stream) {
   g_last_error.clear();
   Plan pl;
   int r;
+  std::vector<Range> rs;
   if ((r = make_plan(p, pl))) return r;
   if (!pl.bias) return fail(CPATTN_EINVAL, "dBias needs a bias (bias_len > 0)");
-  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
-                             dev_err)))
+  if ((r = step_checks(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws,
+                       ws_bytes, pl.ws_core + pl.partial_bytes, dev_err, rs)))
     return r;
   if ((r = check_ptr(dbias, pl.bias_bytes, 16, "dbias"))) return r;
-  const int64_t need = pl.delta_bytes + pl.partial_bytes;
-  if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
-  if ((r = check_ptr(ws, need, 256, "ws"))) return r;
-  // The delta array at the head of ws is read; the partial slab after it is written.
-  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
-                           rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
-                           rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
-                           rng("delta", ws, pl.stat_bytes, false), rng("dbias", dbias, pl.bias_bytes, true),
-                           rng("ws partials", (char*)ws + pl.delta_bytes, pl.partial_bytes, true)};
-  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  rs.push_back(rng("dbias", dbias, pl.bias_bytes, true));
+  rs.push_back(rng("ws partials", (char*)ws + pl.off_partials, pl.partial_bytes, true));
   if ((r = alias_audit(rs))) return r;
-  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout,
-                        (const float*)ws, dev_err);
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   return enqueue_dbias(p, pl, a, dbias, ws, (hipStream_t)stream);
 }
 

@@ -16,34 +16,103 @@
 namespace cpattn {
 
 // ---------------------------------------------------------------- pre-pass
+//
+// One workgroup per (chunk, 32-query tile, query head):
+//  - Delta[h, r] = sum_d dO[r,h,d] O[r,h,d] in fp32 for the tile's rows, from 16-byte
+//    loads of O and dO at their physical pitch with 64-bit addressing;
+//  - the tile's Q and dO transposed to [D][32] (rows past the chunk are zero), the
+//    layout in which dK/dV contracts over queries with 16-byte LDS reads.
+// Tiles are numbered per chunk through tile_base (prefix sums of ceil(len/32)).
+
+constexpr int kTileQ = 32;
+
+__global__ __launch_bounds__(1024) void tile_scan_kernel(const int32_t* chunks, int num_chunks,
+                                                          int32_t* tile_base, const int32_t* dev_err) {
+  if (*dev_err) return;
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (num_chunks + 1023) / 1024;
+  const int c0 = min(num_chunks, t * per), c1 = min(num_chunks, c0 + per);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += (max(chunks[4 * c + 3], 0) + kTileQ - 1) / kTileQ;
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+  for (int c = c0; c < c1; ++c) {
+    tile_base[c] = run;
+    run += (max(chunks[4 * c + 3], 0) + kTileQ - 1) / kTileQ;
+  }
+  if (t == 1023) tile_base[num_chunks] = part[1023];
+}
+
+hipError_t launch_tile_scan(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(1024), 0, s, a.chunks, a.num_chunks,
+                     a.tile_base_out, a.dev_err);
+  return hipGetLastError();
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void prepass_kernel(const AttnArgs a) {
   if (*a.dev_err) return;
-  constexpr int TPP = D / 8;  // threads per (row, head) pair, 8 elements each
+  constexpr int DG = D / 8;       // 16-byte granules per row
+  constexpr int TASKS = DG * 4;   // (8-row group, granule) tasks per tensor
   const int tid = threadIdx.x;
   const int c = blockIdx.x / a.blocks_per_chunk;
-  const int rb = blockIdx.x % a.blocks_per_chunk;
+  const int qt = blockIdx.x % a.blocks_per_chunk;
+  const int h = blockIdx.y;
   const Chunk ch = load_chunk(a.chunks, c);
-  const int r0 = rb * kPrepassRows;
-  if (r0 >= ch.len) return;
-  const int nr = min(kPrepassRows, ch.len - r0);
-  const int pairs = nr * a.hq;
-  const int sub = tid % TPP;
-  for (int p = tid / TPP; p < pairs; p += kThreads / TPP) {
-    const int row = p / a.hq, h = p % a.hq;
-    const int64_t qr = (int64_t)ch.q_row + r0 + row;
-    const int64_t off = (qr * a.hq + h) * D + sub * 8;
-    const u32x4 ov = ld16(a.o + off), dv = ld16(a.dout + off);
-    float acc = 0.f;
+  const int r0 = qt * kTileQ;
+  if (r0 >= ch.len || tid >= 2 * TASKS) return;  // no barriers below
+  const int nq = min(kTileQ, ch.len - r0);
+  const int tile = a.tile_base[c] + qt;
+  const int tensor = tid / TASKS;  // 0: Q, 1: dO
+  const int task = tid % TASKS;
+  const int qg = task / DG, dg = task % DG;  // dg varies fastest within a wave
+  const int64_t rs = (int64_t)a.hq * D;
+  const int64_t off = ((int64_t)ch.q_row + r0) * rs + (int64_t)h * D + dg * 8;
+  const uint16_t* src = (tensor ? a.dout : a.q) + off;
+  u32x4 rows[8], cols[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = fmaf(bf16_lo(ov[w]), bf16_lo(dv[w]), acc);
-      acc = fmaf(bf16_hi(ov[w]), bf16_hi(dv[w]), acc);
+  for (int e = 0; e < 8; ++e) {
+    const int qi = qg * 8 + e;
+    rows[e] = qi < nq ? ld16(src + qi * rs) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tensor == 1) {
+    float ds[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int qi = qg * 8 + e;
+      const u32x4 ov = qi < nq ? ld16(a.o + off + qi * rs) : u32x4{0u, 0u, 0u, 0u};
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(bf16_lo(ov[w]), bf16_lo(rows[e][w]), acc);
+        acc = fmaf(bf16_hi(ov[w]), bf16_hi(rows[e][w]), acc);
+      }
+      ds[e] = acc;
     }
 #pragma unroll
-    for (int m = TPP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-    if (sub == 0) a.delta_out[(int64_t)h * a.q_rows + qr] = acc;
+    for (int m = DG / 2; m >= 1; m >>= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ds[e] += __shfl_xor(ds[e], m, 64);
+    if (dg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (qg * 8 + e < nq) a.delta_out[(int64_t)h * a.q_rows + ch.q_row + r0 + qg * 8 + e] = ds[e];
+    }
+  }
+  transpose8x8(rows, cols);  // cols[d]: the 8 queries of dimension dg*8 + d
+  uint16_t* dst = (tensor ? a.dot_out : a.qt_out) + ((int64_t)tile * a.hq + h) * D * kTileQ;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const int dd = dg * 8 + d;
+    st16(dst + dd * kTileQ + ((qg ^ tswz(dd)) * 8), cols[d]);
   }
 }
 
@@ -69,8 +138,11 @@ hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s) {
 //   S  = Q K^T     A = Q rows (16-byte LDS reads), B = K^T registers
 //   dP = dO V^T    A = dO rows, B = V^T registers
 //   P = exp(scale S - LSE), dS = P (dP - Delta)    (C layout: lane = key, rows = queries)
-//   dV^T += dO^T P   A = dO^T by transposing LDS reads, B = P (already in B layout)
-//   dK^T += Q^T dS   A = Q^T likewise, B = dS
+//   dV^T += dO^T P   A = rows of the pre-pass's transposed dO tile (16-byte reads),
+//                    B = P (already in B layout)
+//   dK^T += Q^T dS   A = rows of the transposed Q tile, B = dS
+// The S/dP row order is chosen so that lane group g of P and dS holds the eight
+// contiguous queries 8g..8g+7, the order of one 16-byte granule of a transposed row.
 // The GQA sum over the group's query heads and the sum over chunks happen in the fp32
 // accumulators; dK = scale dK^T and dV are rounded to BF16 once (STORE), or added to
 // the existing BF16 values and rounded once (ADD).
@@ -111,14 +183,22 @@ __device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_
 }
 
 template <int D>
-__device__ __forceinline__ void dma_q_do(uint16_t* lq, uint16_t* ldo, const AttnArgs& a,
-                                         const QTileIter& it, int g, int wave, int lane) {
+__device__ __forceinline__ void dma_q_do(uint16_t* lq, uint16_t* ldo, uint16_t* lqt, uint16_t* ldot,
+                                         const AttnArgs& a, const QTileIter& it, int g, int wave,
+                                         int lane) {
   const int h = g * a.group + it.hh;
   const int64_t rs = (int64_t)a.hq * D;
   const int64_t off = ((int64_t)it.ch.q_row + it.qt * kBM) * rs + (int64_t)h * D;
   const int nq = min(kBM, it.ch.len - it.qt * kBM);
-  dma_rows<D, kBM, kDkdvWaves, 1>(lq, a.q + off, rs, nq, wave, lane);
-  dma_rows<D, kBM, kDkdvWaves, 1>(ldo, a.dout + off, rs, nq, wave, lane);
+  dma_rows<D, kBM, kDkdvWaves, 2>(lq, a.q + off, rs, nq, wave, lane);
+  dma_rows<D, kBM, kDkdvWaves, 2>(ldo, a.dout + off, rs, nq, wave, lane);
+  // transposed tiles: already swizzled by the pre-pass, copied as they are
+  const int64_t toff = ((int64_t)(a.tile_base[it.c] + it.qt) * a.hq + h) * D * kTileQ;
+  constexpr int NI = D * kTileQ * 2 / 1024;
+  for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += kDkdvWaves) {
+    dma16(a.qt + toff + i * 512 + lane * 8, lqt + i * 512);
+    dma16(a.dot + toff + i * 512 + lane * 8, ldot + i * 512);
+  }
 }
 
 // LSE (as base-2) and Delta of tile row `r` (clamped to the valid rows).
@@ -137,12 +217,16 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
   constexpr int NDB = D / 16;  // 16-row d blocks of dK^T and dV^T
   __shared__ __attribute__((aligned(1024))) uint16_t lds_q[2][kBM * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_do[2][kBM * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_qt[2][D * kBM];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_dot[2][D * kBM];
   __shared__ __attribute__((aligned(16))) float lds_lse[2][kBM];
   __shared__ __attribute__((aligned(16))) float lds_dl[2][kBM];
 
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, n = lane & 15;
+  // S/dP A-operand row n of block mb is tile query 8*(n/4) + 4*mb + n%4
+  const int qrow_a = 8 * (n >> 2) + (n & 3);
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % a.kv_tiles;
   const int rest = logical / a.kv_tiles;
@@ -177,7 +261,7 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
   bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0);
   float st_lse = 0.f, st_dl = 0.f;  // stats staged for the next tile (threads < kBM)
   if (have) {
-    dma_q_do<D>(lds_q[0], lds_do[0], a, cur, g, wave, lane);
+    dma_q_do<D>(lds_q[0], lds_do[0], lds_qt[0], lds_dot[0], a, cur, g, wave, lane);
     if (tid < kBM) {
       load_stats(a, cur, g, tid, st_lse, st_dl);
       lds_lse[0][tid] = st_lse;
@@ -192,7 +276,8 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
     QTileIter nxt = cur;
     const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
     if (have_next) {
-      dma_q_do<D>(lds_q[buf ^ 1], lds_do[buf ^ 1], a, nxt, g, wave, lane);
+      dma_q_do<D>(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_qt[buf ^ 1], lds_dot[buf ^ 1], a, nxt, g,
+                  wave, lane);
       if (tid < kBM) load_stats(a, nxt, g, tid, st_lse, st_dl);
     }
 
@@ -208,15 +293,15 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
         dp[mb] = f32x4{};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          s[mb] = mfma16(lds_row16<D, 1>(qt_l, mb * 16 + n, st * 4 + lg), kf[st], s[mb]);
-          dp[mb] = mfma16(lds_row16<D, 1>(dt_l, mb * 16 + n, st * 4 + lg), vf[st], dp[mb]);
+          s[mb] = mfma16(lds_row16<D, 2>(qt_l, qrow_a + 4 * mb, st * 4 + lg), kf[st], s[mb]);
+          dp[mb] = mfma16(lds_row16<D, 2>(dt_l, qrow_a + 4 * mb, st * 4 + lg), vf[st], dp[mb]);
         }
       }
       const bool need_mask = (nk < 16) || (nq < kBM) || (CAUSAL && tile_pos0 < wkey0 + 15);
       const float* bias_h = BIAS ? a.bias + (int64_t)(g * a.group + cur.hh) * a.bias_len * a.bias_len : nullptr;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int q4 = mb * 16 + lg * 4;  // element j is tile query q4 + j
+        const int q4 = lg * 8 + mb * 4;  // element j is tile query q4 + j
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_lse[buf][q4]);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dl[buf][q4]);
 #pragma unroll
@@ -237,10 +322,14 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(const AttnArgs a) {
                         pack_bf16x2(s[1][0], s[1][1]), pack_bf16x2(s[1][2], s[1][3])};
       const u32x4 dsf = {pack_bf16x2(dp[0][0], dp[0][1]), pack_bf16x2(dp[0][2], dp[0][3]),
                          pack_bf16x2(dp[1][0], dp[1][1]), pack_bf16x2(dp[1][2], dp[1][3])};
+      const uint16_t* qtt = lds_qt[buf];
+      const uint16_t* dtt = lds_dot[buf];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dvt[db] = mfma16(tr_frag16<D>(dt_l, db, lane), pf, dvt[db]);
-        dkt[db] = mfma16(tr_frag16<D>(qt_l, db, lane), dsf, dkt[db]);
+        const int d = db * 16 + n;
+        const int o = d * kBM + ((lg ^ tswz(d)) * 8);
+        dvt[db] = mfma16(ld16(dtt + o), pf, dvt[db]);
+        dkt[db] = mfma16(ld16(qtt + o), dsf, dkt[db]);
       }
     }
     if (have_next && tid < kBM) {

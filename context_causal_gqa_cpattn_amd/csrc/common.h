@@ -105,9 +105,10 @@ template <int D, int KIND = 0>
 __device__ __forceinline__ int swz(int r) {
   constexpr int G = D / 8;
   if (KIND == 0) return (((r & 3) << 2) | ((r >> 2) & 3)) & (G - 1);
-  // KIND 1 (tiles read by 16x16x32 operands): sixteen rows at one granule still hit
-  // sixteen bank groups, and the 8 rows x 32 bytes of half a 16x16 transposing read do.
-  return (((r & 7) << 1) | ((r >> 3) & 1)) & (G - 1);
+  if (KIND == 1) return (((r & 7) << 1) | ((r >> 3) & 1)) & (G - 1);
+  // KIND 2: rows read sixteen at a time as {8a + 4b' + c : a, c in 0..3} for a fixed b'
+  // (the dK/dV query order) land in sixteen distinct bank groups.
+  return ((r & 3) | (((r >> 3) & 3) << 2)) & (G - 1);
 }
 
 // One 16-byte LDS DMA per lane: lane l's data lands at lds + 16*l bytes.
@@ -196,6 +197,11 @@ __device__ __forceinline__ int chunk_lower_bound(const int32_t* map, int num_chu
   return lo;
 }
 
+// Transposed 32-query tiles [D][32] (query-contiguous rows of 64 bytes) written by the
+// pre-pass and read by dK/dV with 16-byte reads: granule g of row d is stored at
+// g ^ ((d >> 2) & 3), so 16 consecutive rows read at one granule hit 16 bank groups.
+__device__ __forceinline__ int tswz(int d) { return (d >> 2) & 3; }
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -212,6 +218,12 @@ struct AttnArgs {
   uint16_t* dv;
   float* dbias;          // dBias (or the partial-sum slab when parts > 1)
   float* delta_out;      // pre-pass output
+  uint16_t* qt_out;      // pre-pass output: transposed Q tiles
+  uint16_t* dot_out;     // pre-pass output: transposed dO tiles
+  const uint16_t* qt;    // transposed Q tiles [tile][hq][D][32]
+  const uint16_t* dot;   // transposed dO tiles
+  int32_t* tile_base_out;
+  const int32_t* tile_base;  // [C+1] prefix sums of ceil(len/32)
   const int32_t* seq_offsets;
   const int32_t* seq_lens;
   const int32_t* chunks;

@@ -31,6 +31,7 @@ struct LayoutArgs {
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
+hipError_t launch_tile_scan(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
@@ -38,8 +39,8 @@ hipError_t launch_dbias(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
 hipError_t launch_dbias_reduce(const float* partial, float* out, int64_t n, int parts,
                                const int32_t* dev_err, hipStream_t s);
 
-// Rows of a chunk handled by one pre-pass workgroup.
-constexpr int kPrepassRows = 16;
+// Rows of a chunk handled by one pre-pass workgroup (one transposed tile).
+constexpr int kPrepassRows = 32;
 // Keys per dK/dV workgroup (four waves of 32 keys).
 constexpr int kDkdvKeys = 128;
 // dBias tile: 128 query positions x 64 keys per workgroup.

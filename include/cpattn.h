@@ -112,9 +112,13 @@ const char* cpattn_last_error(void);
 int cpattn_version(void);
 
 /* Bytes of caller-provided device workspace that cpattn_fwd (op = CPATTN_OP_FWD)
- * or cpattn_bwd (op = CPATTN_OP_BWD) needs for `p`: Delta (fp32 [hq, q_rows]) and,
- * with a bias, the per-partition dBias partial sums.  Returns 0 for an invalid
- * problem (check it with the entry point for the reason). */
+ * or cpattn_bwd (op = CPATTN_OP_BWD) needs for `p`.  The backward workspace holds,
+ * each part starting on a 256-byte boundary: Delta (fp32 [hq, q_rows], at offset
+ * 0), the per-chunk prefix sums of 32-query tile counts (int32 [num_chunks + 1]),
+ * Q^T and dO^T as BF16 tiles [tile][hq][head_dim][32] (at most
+ * ceil(q_rows/32) + num_chunks tiles each; query columns past the chunk end are
+ * zero) and, with a bias, the per-partition dBias partial sums.  Returns 0 for
+ * an invalid problem (check it with the entry point for the reason). */
 size_t cpattn_workspace_size(const cpattn_problem* p, int op);
 
 /* The device promise check alone ("Changes": promised sequence lengths and
@@ -152,31 +156,34 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
 
 /* The backward's steps one by one, for callers that schedule them (and for
  * timing each kernel).  None of them validates: call cpattn_validate first on
- * the same stream with the same dev_err.
- *  cpattn_bwd_prepass: delta[h, r] = sum_d dO[r,h,d] O[r,h,d] (fp32) on chunk
- *      rows ("CP8 AllGather: composition with first-gradient reuse": the row
- *      dot of dO and O, loaded at their physical pitch).
- *  cpattn_bwd_dkdv: dK/dV as in cpattn_bwd from delta.
- *  cpattn_bwd_dq: dQ as in cpattn_bwd from delta.
- *  cpattn_bwd_dbias: dBias as in cpattn_bwd from delta; ws as for cpattn_bwd
- *      (the delta array is ws's first hq*q_rows floats). */
-int cpattn_bwd_prepass(const cpattn_problem* p, const int32_t* q_chunk_map, const void* o,
-                       const void* dout, float* delta, const int32_t* dev_err,
-                       cpattn_stream_t stream);
+ * the same stream with the same dev_err.  All take the backward workspace
+ * (cpattn_workspace_size(p, CPATTN_OP_BWD) bytes; without dBias the partial
+ * sums may be left off, so ws_bytes may be that size minus them).
+ *  cpattn_bwd_prepass: writes Delta[h, r] = sum_d dO[r,h,d] O[r,h,d] (fp32) on
+ *      chunk rows ("CP8 AllGather: composition with first-gradient reuse": the
+ *      row dot of dO and O, loaded at their physical pitch), and the transposed
+ *      32-query tiles of Q and dO that dK/dV multiplies with.
+ *  cpattn_bwd_dkdv: dK/dV as in cpattn_bwd from the pre-pass results.
+ *  cpattn_bwd_dq: dQ as in cpattn_bwd from the pre-pass results.
+ *  cpattn_bwd_dbias: dBias as in cpattn_bwd from the pre-pass results; ws must
+ *      also hold the partial sums. */
+int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
+                       const void* o, const void* dout, void* ws, size_t ws_bytes,
+                       const int32_t* dev_err, cpattn_stream_t stream);
 int cpattn_bwd_dkdv(const cpattn_problem* p, const void* q, const void* k, const void* v,
                     const int32_t* seq_offsets, const int32_t* seq_lens,
                     const int32_t* q_chunk_map, const float* bias, const float* lse,
-                    const void* dout, const float* delta, void* dk, void* dv,
+                    const void* dout, const void* ws, size_t ws_bytes, void* dk, void* dv,
                     int dkv_accumulate, const int32_t* dev_err, cpattn_stream_t stream);
 int cpattn_bwd_dq(const cpattn_problem* p, const void* q, const void* k, const void* v,
                   const int32_t* seq_offsets, const int32_t* seq_lens,
                   const int32_t* q_chunk_map, const float* bias, const float* lse,
-                  const void* dout, const float* delta, void* dq, const int32_t* dev_err,
-                  cpattn_stream_t stream);
+                  const void* dout, const void* ws, size_t ws_bytes, void* dq,
+                  const int32_t* dev_err, cpattn_stream_t stream);
 int cpattn_bwd_dbias(const cpattn_problem* p, const void* q, const void* k, const void* v,
                      const int32_t* seq_offsets, const int32_t* seq_lens,
                      const int32_t* q_chunk_map, const float* bias, const float* lse,
-                     const void* dout, float* dbias, void* ws, size_t ws_bytes,
+                     const void* dout, void* ws, size_t ws_bytes, float* dbias,
                      const int32_t* dev_err, cpattn_stream_t stream);
 
 /* Layout copies ("Changes": vectorised BF16 pack/unpack copies that keep

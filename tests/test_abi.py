@@ -102,15 +102,50 @@ def test_bwd_rejects_small_workspace_and_aliases():
     assert lib.cpattn_bwd(*bad, A + (12 << 24), need, A + (6 << 24), None) == cp.EINVAL
 
 
+def _ws_layout(hq, q_rows, num_chunks, head_dim):
+    """Backward workspace bytes without dBias partials, from the layout the header states."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    tiles = -(-q_rows // 32) + num_chunks
+    return r256(hq * q_rows * 4) + r256((num_chunks + 1) * 4) + 2 * r256(tiles * hq * head_dim * 32 * 2)
+
+
 def test_workspace_sizes():
     lib = cp.load()
     p = _prob()
     assert lib.cpattn_workspace_size(ctypes.byref(p), cp.OP_FWD) == 0
+    assert lib.cpattn_workspace_size(ctypes.byref(p), cp.OP_BWD) == _ws_layout(8, 64, 2, 128)
+    p3 = _prob(num_seqs=64, hq=32, hkv=8, head_dim=256, q_rows=64 * 1024, kv_rows=64 * 8192,
+               num_chunks=128, max_chunk_len=512, max_kv_len=8192)
+    assert lib.cpattn_workspace_size(ctypes.byref(p3), cp.OP_BWD) == _ws_layout(32, 64 * 1024, 128, 256)
     pb = _prob(head_dim=32, bias_len=1024, causal=0, hq=4, hkv=4, num_chunks=1024, q_rows=1 << 20,
                kv_rows=1 << 20)
     ws = lib.cpattn_workspace_size(ctypes.byref(pb), cp.OP_BWD)
-    assert ws >= 4 * (1 << 20) * 4 + 4 * 1024 * 1024 * 4  # delta + at least one partial slab
+    assert ws >= _ws_layout(4, 1 << 20, 1024, 32) + 4 * 1024 * 1024 * 4  # + one partial slab
     assert lib.cpattn_workspace_size(ctypes.byref(_prob(hq=3)), cp.OP_BWD) == 0
+
+
+def test_backward_steps_check_workspace():
+    lib = cp.load()
+    p = _prob()
+    core = _ws_layout(8, 64, 2, 128)
+    q, k, v = A, A + (1 << 24), A + (2 << 24)
+    so, sl, cm = A + (3 << 24), A + (3 << 24) + 256, A + (3 << 24) + 512
+    o, lse, do, err, ws = A + (4 << 24), A + (5 << 24), A + (8 << 24), A + (6 << 24), A + (12 << 24)
+    dk, dv, dq = A + (9 << 24), A + (10 << 24), A + (11 << 24)
+    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, ws, core - 256, err, None) == cp.EINVAL
+    assert "workspace" in _err()
+    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, ws + 16, core, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, o, core, err, None) == cp.EINVAL
+    assert "alias" in _err()
+    args = [ctypes.byref(p), q, k, v, so, sl, cm, None, lse, do]
+    assert lib.cpattn_bwd_dkdv(*args, ws, core - 1, dk, dv, 0, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_dkdv(*args, ws, core, ws + 4096, dv, 0, err, None) == cp.EINVAL
+    assert "alias" in _err()
+    assert lib.cpattn_bwd_dkdv(*args, ws, core, dk, dv, 3, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_dq(*args, ws, core - 1, dq, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_dq(*args, ws, core, do, err, None) == cp.EINVAL and "alias" in _err()
+    assert lib.cpattn_bwd_dbias(*args, ws, core, A + (13 << 24), err, None) == cp.EINVAL
+    assert "bias" in _err()
 
 
 def test_layout_copy_host_checks():
