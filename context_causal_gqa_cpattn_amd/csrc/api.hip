@@ -83,8 +83,8 @@ struct Plan {
   int64_t delta_bytes;  // rounded to 256
   int parts;            // dBias partitions
   int64_t partial_bytes;
-  // backward workspace: delta | tile_base | Q^T tiles | dO^T tiles | dBias partials
-  int64_t off_tiles, off_qt, off_dot, off_partials, ws_core;
+  // backward workspace: delta | Q^T tiles | dO^T tiles | dBias partials
+  int64_t off_qt, off_dot, off_partials, ws_core;
   dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias;
   int bpc_fwd, bpc_prepass, kv_tiles;
 };
@@ -154,8 +154,7 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   // Transposed 32-query tiles: at most ceil(q_rows/32) + C of them.
   const int64_t max_tiles = cdiv(p->q_rows, kPrepassRows) + p->num_chunks;
   const int64_t tile_bytes = max_tiles * p->hq * (int64_t)D * kPrepassRows * 2;
-  pl.off_tiles = pl.delta_bytes;
-  pl.off_qt = pl.off_tiles + round256(((int64_t)p->num_chunks + 1) * 4);
+  pl.off_qt = pl.delta_bytes;
   pl.off_dot = pl.off_qt + round256(tile_bytes);
   pl.off_partials = pl.off_dot + round256(tile_bytes);
   pl.ws_core = pl.off_partials;
@@ -322,7 +321,6 @@ AttnArgs bwd_args(const cpattn_problem* p, const Plan& pl, const void* q, const 
   AttnArgs a = base_args(p, pl);
   const char* w = (const char*)ws;
   const float* delta = (const float*)w;
-  a.tile_base = (const int32_t*)(w + pl.off_tiles);
   a.qt = (const uint16_t*)(w + pl.off_qt);
   a.dot = (const uint16_t*)(w + pl.off_dot);
   a.q = (const uint16_t*)q;
@@ -347,15 +345,12 @@ int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, 
   a.o = (const uint16_t*)o;
   a.dout = (const uint16_t*)dout;
   a.delta_out = (float*)w;
-  a.tile_base_out = (int32_t*)(w + pl.off_tiles);
-  a.tile_base = a.tile_base_out;
   a.qt_out = (uint16_t*)(w + pl.off_qt);
   a.dot_out = (uint16_t*)(w + pl.off_dot);
   a.chunks = cm;
   a.dev_err = dev_err;
   a.blocks_per_chunk = pl.bpc_prepass;
-  int r = hip_check(launch_tile_scan(a, s), "tile scan launch");
-  if (r || empty(pl.grid_prepass)) return r;
+  if (empty(pl.grid_prepass)) return CPATTN_OK;
   return hip_check(launch_prepass(a, pl.D, pl.grid_prepass, s), "pre-pass launch");
 }
 

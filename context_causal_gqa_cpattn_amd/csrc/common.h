@@ -202,6 +202,13 @@ __device__ __forceinline__ int chunk_lower_bound(const int32_t* map, int num_chu
 // g ^ ((d >> 2) & 3), so 16 consecutive rows read at one granule hit 16 bank groups.
 __device__ __forceinline__ int tswz(int d) { return (d >> 2) & 3; }
 
+// Slot of query tile qt (32 rows) of chunk c whose first Q row is q_row.  Chunks are
+// ordered by Q row and do not overlap, so slots are distinct, and they stay below
+// ceil(q_rows / 32) + num_chunks.
+__device__ __forceinline__ int64_t tile_slot(int c, int q_row, int qt) {
+  return (int64_t)(q_row >> 5) + c + qt;
+}
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -222,8 +229,6 @@ struct AttnArgs {
   uint16_t* dot_out;     // pre-pass output: transposed dO tiles
   const uint16_t* qt;    // transposed Q tiles [tile][hq][D][32]
   const uint16_t* dot;   // transposed dO tiles
-  int32_t* tile_base_out;
-  const int32_t* tile_base;  // [C+1] prefix sums of ceil(len/32)
   const int32_t* seq_offsets;
   const int32_t* seq_lens;
   const int32_t* chunks;
@@ -239,5 +244,35 @@ struct AttnArgs {
   float scale;
   float scale_log2;         // scale * log2(e)
 };
+
+// Launch KERNEL<D, CAUSAL, BIAS> with kThreads threads for the supported combinations
+// (a bias only without causal masking and with D <= 128); returns the launch status.
+#define CPATTN_BWD_DISPATCH(KERNEL)                                                          \
+  if (bias) {                                                                                \
+    if (causal) return hipErrorInvalidValue;                                                 \
+    switch (D) {                                                                             \
+      case 32: hipLaunchKernelGGL((KERNEL<32, false, true>), grid, dim3(kThreads), 0, s, a); break;   \
+      case 64: hipLaunchKernelGGL((KERNEL<64, false, true>), grid, dim3(kThreads), 0, s, a); break;   \
+      case 128: hipLaunchKernelGGL((KERNEL<128, false, true>), grid, dim3(kThreads), 0, s, a); break; \
+      default: return hipErrorInvalidValue;                                                  \
+    }                                                                                        \
+  } else if (causal) {                                                                       \
+    switch (D) {                                                                             \
+      case 32: hipLaunchKernelGGL((KERNEL<32, true, false>), grid, dim3(kThreads), 0, s, a); break;   \
+      case 64: hipLaunchKernelGGL((KERNEL<64, true, false>), grid, dim3(kThreads), 0, s, a); break;   \
+      case 128: hipLaunchKernelGGL((KERNEL<128, true, false>), grid, dim3(kThreads), 0, s, a); break; \
+      case 256: hipLaunchKernelGGL((KERNEL<256, true, false>), grid, dim3(kThreads), 0, s, a); break; \
+      default: return hipErrorInvalidValue;                                                  \
+    }                                                                                        \
+  } else {                                                                                   \
+    switch (D) {                                                                             \
+      case 32: hipLaunchKernelGGL((KERNEL<32, false, false>), grid, dim3(kThreads), 0, s, a); break;   \
+      case 64: hipLaunchKernelGGL((KERNEL<64, false, false>), grid, dim3(kThreads), 0, s, a); break;   \
+      case 128: hipLaunchKernelGGL((KERNEL<128, false, false>), grid, dim3(kThreads), 0, s, a); break; \
+      case 256: hipLaunchKernelGGL((KERNEL<256, false, false>), grid, dim3(kThreads), 0, s, a); break; \
+      default: return hipErrorInvalidValue;                                                  \
+    }                                                                                        \
+  }                                                                                          \
+  return hipGetLastError();
 
 }  // namespace cpattn

@@ -1,0 +1,373 @@
+// dK/dV kernel of the attention backward (KV-parallel).
+//
+// Page "Optimize context parallel attention layouts and gradient accumulation":
+//  - "CP8 first-gradient accumulator reuse": the first dK/dV contribution is the
+//    accumulator (STORE, no zero fill) and the later one is added (ADD);
+//  - "Changes": GQA, causal THD with physical offsets.
+//
+// With P = exp(scale S - LSE), dP = dO V^T, Delta = rowsum(dO * O) and
+// dS = P * (dP - Delta):  dV = P^T dO and dK = scale dS^T Q, summed over every query
+// that sees the key, over the chunks of the sequence and over the group's query heads.
+//
+// Workgroup = (sequence, 128-key tile, KV head g), four waves with one wave per SIMD;
+// wave w owns keys [32w, 32w+32) of the tile.  It keeps K^T and V^T of its keys in
+// registers as B operands and dK^T, dV^T (D x 32 keys, fp32) as MFMA accumulators for
+// the whole loop.  The loop runs over every (chunk of the sequence, query head of the
+// group, 32-query tile) that sees the key tile; four tiles per step are DMA'd into LDS
+// one step ahead (double buffer):
+//   Q, dO     row-major, one 16-byte pad granule per row (conflict-free 16-byte reads
+//             at immediate offsets), read from the inputs at their physical pitch;
+//   Q^T, dO^T the pre-pass's transposed tiles, copied as they are.
+// Per tile, with 32x32x16 MFMAs (C layout: lane = key, 16 query rows per lane):
+//   S  = Q K^T,  dP = dO V^T           (A = Q / dO rows, B = K^T / V^T registers)
+//   P = exp2(S scale log2e - LSE log2e), dS = P (dP - Delta)
+//   dV^T += dO^T P,  dK^T += Q^T dS    (A = transposed tiles, B = P / dS as packed)
+// The pre-pass stores the transposed tiles in the query order of the accumulator rows,
+// so P and dS become B operands without any data movement.  dK = scale dK^T and dV are
+// rounded to BF16 once (STORE), or added to the existing BF16 values and rounded once
+// (ADD).
+#include "common.h"
+#include "launch.h"
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kTq = 32;     // queries per tile
+constexpr int kWaves = 4;   // waves per workgroup, 32 keys each
+constexpr int kKvThreads = kWaves * 64;
+static_assert(kWaves * 32 == kDkdvKeys, "keys per workgroup");
+
+// A row-major 32 x D tile with one pad granule per row: row r, granule j at element
+// r * (D + 8) + 8 j.  The slot count is rounded up to whole 64-lane DMA instructions.
+template <int D>
+struct NatTile {
+  static constexpr int G = D / 8 + 1;  // granules per padded row
+  static constexpr int SLOTS = (kTq * G + 63) / 64 * 64;
+  static constexpr int ELEMS = SLOTS * 8;
+  static constexpr int NI = SLOTS / 64;  // DMA instructions per tile
+};
+
+struct QTileIter {
+  int c, hh, qt, qt_first, n_qt;
+  Chunk ch;
+};
+
+// Advance to the next chunk (from it.c) that has query tiles seeing keys >= key0.
+template <bool CAUSAL>
+__device__ __forceinline__ bool seek_chunk(const AttnArgs& a, QTileIter& it, int c_end, int key0) {
+  for (; it.c < c_end; ++it.c) {
+    it.ch = load_chunk(a.chunks, it.c);
+    const int first_row = CAUSAL ? max(0, key0 - it.ch.pos0) : 0;
+    if (first_row < it.ch.len) {
+      it.qt_first = first_row / kTq;
+      it.n_qt = (it.ch.len + kTq - 1) / kTq;
+      it.qt = it.qt_first;
+      it.hh = 0;
+      return true;
+    }
+  }
+  return false;
+}
+
+template <bool CAUSAL>
+__device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_end, int key0) {
+  if (++it.qt < it.n_qt) return true;
+  it.qt = it.qt_first;
+  if (++it.hh < a.group) return true;
+  ++it.c;
+  return seek_chunk<CAUSAL>(a, it, c_end, key0);
+}
+
+// The DMA helpers address as a uniform base (forced into scalar registers) plus a
+// 32-bit per-lane byte offset (a 32-row tile spans less than 2 GiB), so no 64-bit
+// per-lane pointer is kept live across the loop.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// DMA rows [0, 32) of a tile into the padded layout.  Rows past nvalid repeat the last
+// valid row (finite data, masked by the caller); pad granules and the slack after the
+// last row receive copies of real granules and are never read.
+template <int D>
+__device__ __forceinline__ void dma_nat(uint16_t* lds, const uint16_t* base, uint32_t rs_bytes,
+                                        int nvalid, int wave, int lane) {
+  using T = NatTile<D>;
+  const char* b = uniform_ptr(base);
+  for (int i = __builtin_amdgcn_readfirstlane(wave); i < T::NI; i += kWaves) {
+    const int slot = i * 64 + lane;
+    const int r = slot / T::G, j = slot - r * T::G;
+    const uint32_t row = (uint32_t)min(min(r, kTq - 1), nvalid - 1);
+    const uint32_t off = row * rs_bytes + (uint32_t)min(j, D / 8 - 1) * 16u;
+    __builtin_amdgcn_global_load_lds((const void*)(b + off), CPATTN_LDS(void, lds + i * 512), 16, 0, 0);
+  }
+}
+
+// DMA a contiguous D x 32 transposed tile.
+template <int D>
+__device__ __forceinline__ void dma_flat(uint16_t* lds, const uint16_t* src, int wave, int lane) {
+  constexpr int NI = D * kTq * 2 / 1024;
+  const char* b = uniform_ptr(src);
+  for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += kWaves)
+    __builtin_amdgcn_global_load_lds((const void*)(b + (uint32_t)(i * 1024 + lane * 16)),
+                                     CPATTN_LDS(void, lds + i * 512), 16, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tiles(uint16_t* lq, uint16_t* ldo, uint16_t* lqt, uint16_t* ldot,
+                                          const AttnArgs& a, const QTileIter& it, int g, int wave,
+                                          int lane) {
+  const int h = g * a.group + it.hh;
+  const int64_t rs = (int64_t)a.hq * D;
+  const int64_t off = ((int64_t)it.ch.q_row + it.qt * kTq) * rs + (int64_t)h * D;
+  const int nq = min(kTq, it.ch.len - it.qt * kTq);
+  const uint32_t rs_bytes = (uint32_t)(rs * 2);
+  dma_nat<D>(lq, a.q + off, rs_bytes, nq, wave, lane);
+  dma_nat<D>(ldo, a.dout + off, rs_bytes, nq, wave, lane);
+  const int64_t toff = (tile_slot(it.c, it.ch.q_row, it.qt) * a.hq + h) * D * kTq;
+  dma_flat<D>(lqt, a.qt + toff, wave, lane);
+  dma_flat<D>(ldot, a.dot + toff, wave, lane);
+}
+
+// LSE (as base 2) and Delta of tile row r (clamped to the valid rows).
+__device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& it, int g, int r,
+                                           float& lse2, float& dl) {
+  const int h = g * a.group + it.hh;
+  const int nq = min(kTq, it.ch.len - it.qt * kTq);
+  const int64_t idx = (int64_t)h * a.q_rows + it.ch.q_row + it.qt * kTq + min(r, nq - 1);
+  lse2 = a.lse[idx] * kLog2e;
+  dl = a.delta[idx];
+}
+
+// P and dS of one tile in place (s -> P, dp -> dS).  Element r of a lane is query
+// 8 (r / 4) + 4 hl + r % 4 of the tile; the lane's key is `key`.
+template <bool MASK, bool CAUSAL, bool BIAS>
+__device__ __forceinline__ void softmax_grad(f32x16& s, f32x16& dp, const float* lse, const float* dl,
+                                             int hl, float c, int key, bool key_ok, int nq,
+                                             int tile_pos0, const float* bias_h, int bias_len) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q0 = 8 * i + 4 * hl;
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse + q0);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + q0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * i + j, qi = q0 + j;
+      float x = s[r] * c;
+      if (BIAS)
+        x = fmaf(bias_h[(int64_t)min(tile_pos0 + qi, bias_len - 1) * bias_len + min(key, bias_len - 1)],
+                 kLog2e, x);
+      x -= l4[j];
+      if (MASK) {
+        const bool vis = key_ok && qi < nq && (!CAUSAL || key <= tile_pos0 + qi);
+        x = vis ? x : -INFINITY;
+      }
+      const float p = exp2f_fast(x);
+      s[r] = p;
+      dp[r] = p * (dp[r] - d4[j]);
+    }
+  }
+}
+
+}  // namespace
+
+template <int D, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
+  constexpr int NS = D / 16;  // 16-deep k-steps of S and dP
+  constexpr int NB = D / 32;  // 32-row blocks of dK^T and dV^T
+  using T = NatTile<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_q[2][T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_do[2][T::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_qt[2][D * kTq];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_dot[2][D * kTq];
+  __shared__ __attribute__((aligned(16))) float lds_lse[2][kTq];
+  __shared__ __attribute__((aligned(16))) float lds_dl[2][kTq];
+
+  if (*a.dev_err) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, n = lane & 31;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = logical % a.kv_tiles;
+  const int rest = logical / a.kv_tiles;
+  const int g = rest % a.hkv;
+  const int b = rest / a.hkv;
+  const int L = a.seq_lens[b];
+  const int wg_key0 = kt * kDkdvKeys;
+  if (wg_key0 >= L) return;  // uniform over the workgroup, before any barrier
+  const int64_t koff = a.seq_offsets[b];
+  const int wkey0 = wg_key0 + wave * 32;
+  const int nk = max(0, min(32, L - wkey0));
+  const int key = wkey0 + n;  // this lane's key (column of S, dP, dK^T, dV^T)
+  const bool key_ok = n < nk;
+
+  // K and V as B operands: lane (hl, n) holds key n, dimensions 16 st + 8 hl + [0, 8).
+  // Lanes past the sequence end load its last key (finite values; their P and dS are 0).
+  const int64_t kv_stride = (int64_t)a.hkv * D;
+  u32x4 kf[NS], vf[NS];
+  {
+    const int64_t off = (koff + min(key, L - 1)) * kv_stride + (int64_t)g * D + hl * 8;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      kf[st] = ld16(a.k + off + st * 16);
+      vf[st] = ld16(a.v + off + st * 16);
+    }
+  }
+  f32x16 dkt[NB], dvt[NB];
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    dkt[blk] = f32x16{};
+    dvt[blk] = f32x16{};
+  }
+  // Lane offsets: S/dP A operand = row n, granule 2 st + hl of the padded tiles;
+  // dV/dK A operand, k-step t = row 32 blk + n, granule (2 t + hl) ^ tswz(n) of the
+  // transposed tiles (tswz depends on the row's bits 2-3 only).
+  const int nat_off = n * (D + 8) + hl * 8;
+  const int tr_off0 = n * kTq + ((hl ^ tswz(n)) * 8);
+  const int tr_off1 = n * kTq + (((2 + hl) ^ tswz(n)) * 8);
+
+  const int c_end = chunk_lower_bound(a.chunks, a.num_chunks, b + 1);
+  QTileIter cur;
+  cur.c = chunk_lower_bound(a.chunks, a.num_chunks, b);
+  bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0);
+  float st_lse = 0.f, st_dl = 0.f;  // stats staged for the next tile (threads < kTq)
+  if (have) {
+    dma_tiles<D>(lds_q[0], lds_do[0], lds_qt[0], lds_dot[0], a, cur, g, wave, lane);
+    if (tid < kTq) {
+      load_stats(a, cur, g, tid, st_lse, st_dl);
+      lds_lse[0][tid] = st_lse;
+      lds_dl[0][tid] = st_dl;
+    }
+  }
+  wait_vm_all();
+  __syncthreads();
+
+  int buf = 0;
+  while (have) {
+    QTileIter nxt = cur;
+    const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
+    if (have_next) {
+      // stats first: loads complete in order, so waiting for them does not wait for
+      // the tiles issued after them
+      if (tid < kTq) load_stats(a, nxt, g, tid, st_lse, st_dl);
+      dma_tiles<D>(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_qt[buf ^ 1], lds_dot[buf ^ 1], a, nxt, g,
+                   wave, lane);
+    }
+
+    // Every wave runs every tile of the loop: tiles that a wave's keys do not see (at the
+    // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
+    const int nq = min(kTq, cur.ch.len - cur.qt * kTq);
+    const int tile_pos0 = cur.ch.pos0 + cur.qt * kTq;
+    {
+      const uint16_t* lq = lds_q[buf] + nat_off;
+      const uint16_t* ld = lds_do[buf] + nat_off;
+      // S, then dP: each A operand is read two k-steps ahead of its product (the
+      // scheduling barriers keep the compiler from hoisting every read at once).
+      f32x16 s = {}, dp = {};
+      {
+        u32x4 f[3];
+        f[0] = ld16(lq);
+        f[1] = ld16(lq + 16);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          if (st + 2 < NS) f[(st + 2) % 3] = ld16(lq + (st + 2) * 16);
+          else f[(st + 2) % 3] = ld16(ld + (st + 2 - NS) * 16);
+          s = mfma32(f[st % 3], kf[st], s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          if (st + 2 < NS) f[(NS + st + 2) % 3] = ld16(ld + (st + 2) * 16);
+          dp = mfma32(f[(NS + st) % 3], vf[st], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const bool need_mask = (nk < 32) || (nq < kTq) || (CAUSAL && tile_pos0 < wkey0 + 31);
+      const float* bias_h =
+          BIAS ? a.bias + (int64_t)(g * a.group + cur.hh) * a.bias_len * a.bias_len : nullptr;
+      if (need_mask)
+        softmax_grad<true, CAUSAL, BIAS>(s, dp, lds_lse[buf], lds_dl[buf], hl, a.scale_log2, key,
+                                         key_ok, nq, tile_pos0, bias_h, a.bias_len);
+      else
+        softmax_grad<false, CAUSAL, BIAS>(s, dp, lds_lse[buf], lds_dl[buf], hl, a.scale_log2, key,
+                                          key_ok, nq, tile_pos0, bias_h, a.bias_len);
+      // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
+      const u32x4 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 8);
+      const u32x4 ds0 = to_bf16x8(dp, 0), ds1 = to_bf16x8(dp, 8);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* qtt = lds_qt[buf];
+      const uint16_t* dtt = lds_dot[buf];
+      // dV^T and dK^T: the A operands form one stream (per block: dO^T step 0 and 1, then
+      // Q^T step 0 and 1), each read three products ahead.
+      {
+        constexpr int NOP = 4 * NB;
+        auto operand = [&](int i) {
+          const int blk = i >> 2, which = i & 3;
+          const uint16_t* t = (which < 2) ? dtt : qtt;
+          return ld16(t + blk * 32 * kTq + ((which & 1) ? tr_off1 : tr_off0));
+        };
+        u32x4 f[4];
+        f[0] = operand(0);
+        f[1] = operand(1);
+        f[2] = operand(2);
+#pragma unroll
+        for (int i = 0; i < NOP; ++i) {
+          if (i + 3 < NOP) f[(i + 3) & 3] = operand(i + 3);
+          const int blk = i >> 2, which = i & 3;
+          if (which < 2) dvt[blk] = mfma32(f[i & 3], which ? p1 : p0, dvt[blk]);
+          else dkt[blk] = mfma32(f[i & 3], (which & 1) ? ds1 : ds0, dkt[blk]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (have_next && tid < kTq) {
+      lds_lse[buf ^ 1][tid] = st_lse;
+      lds_dl[buf ^ 1][tid] = st_dl;
+    }
+    wait_vm_all();
+    __syncthreads();
+    cur = nxt;
+    have = have_next;
+    buf ^= 1;
+  }
+
+  if (!key_ok) return;
+  // element r of block blk is dimension 32 blk + 8 (r / 4) + 4 hl + r % 4
+  const int64_t off = (koff + key) * kv_stride + (int64_t)g * D + hl * 4;
+  if (a.accumulate) {
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t o = off + blk * 32 + i * 8;
+        const u32x2 ok = ld8(a.dk + o), ov = ld8(a.dv + o);
+        const float k0 = fmaf(dkt[blk][4 * i], a.scale, bf16_lo(ok[0]));
+        const float k1 = fmaf(dkt[blk][4 * i + 1], a.scale, bf16_hi(ok[0]));
+        const float k2 = fmaf(dkt[blk][4 * i + 2], a.scale, bf16_lo(ok[1]));
+        const float k3 = fmaf(dkt[blk][4 * i + 3], a.scale, bf16_hi(ok[1]));
+        st8(a.dk + o, u32x2{pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)});
+        st8(a.dv + o, u32x2{pack_bf16x2(dvt[blk][4 * i] + bf16_lo(ov[0]), dvt[blk][4 * i + 1] + bf16_hi(ov[0])),
+                            pack_bf16x2(dvt[blk][4 * i + 2] + bf16_lo(ov[1]), dvt[blk][4 * i + 3] + bf16_hi(ov[1]))});
+      }
+  } else {
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t o = off + blk * 32 + i * 8;
+        st8(a.dk + o, u32x2{pack_bf16x2(dkt[blk][4 * i] * a.scale, dkt[blk][4 * i + 1] * a.scale),
+                            pack_bf16x2(dkt[blk][4 * i + 2] * a.scale, dkt[blk][4 * i + 3] * a.scale)});
+        st8(a.dv + o, u32x2{pack_bf16x2(dvt[blk][4 * i], dvt[blk][4 * i + 1]),
+                            pack_bf16x2(dvt[blk][4 * i + 2], dvt[blk][4 * i + 3])});
+      }
+  }
+}
+
+hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s) {
+  constexpr int kThreads = kKvThreads;
+  CPATTN_BWD_DISPATCH(dkdv_kernel)
+}
+
+}  // namespace cpattn

@@ -31,7 +31,6 @@ struct LayoutArgs {
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
-hipError_t launch_tile_scan(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);

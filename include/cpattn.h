@@ -114,11 +114,11 @@ int cpattn_version(void);
 /* Bytes of caller-provided device workspace that cpattn_fwd (op = CPATTN_OP_FWD)
  * or cpattn_bwd (op = CPATTN_OP_BWD) needs for `p`.  The backward workspace holds,
  * each part starting on a 256-byte boundary: Delta (fp32 [hq, q_rows], at offset
- * 0), the per-chunk prefix sums of 32-query tile counts (int32 [num_chunks + 1]),
- * Q^T and dO^T as BF16 tiles [tile][hq][head_dim][32] (at most
- * ceil(q_rows/32) + num_chunks tiles each; query columns past the chunk end are
- * zero) and, with a bias, the per-partition dBias partial sums.  Returns 0 for
- * an invalid problem (check it with the entry point for the reason). */
+ * 0), Q^T and dO^T as BF16 tiles [slot][hq][head_dim][32 queries, in an internal
+ * order] (ceil(q_rows/32) + num_chunks slots each; tile t of chunk c is slot
+ * floor(q_row_c / 32) + c + t; query columns past the chunk end are zero) and,
+ * with a bias, the per-partition dBias partial sums.  Returns 0 for an invalid
+ * problem (check it with the entry point for the reason). */
 size_t cpattn_workspace_size(const cpattn_problem* p, int op);
 
 /* The device promise check alone ("Changes": promised sequence lengths and
