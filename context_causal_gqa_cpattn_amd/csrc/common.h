@@ -84,7 +84,12 @@ __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define CPATTN_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their no-wait maxima), through the
+// builtin so that the compiler knows every earlier vector-memory load has completed.
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 
 // Physical block id -> logical work item, so that consecutive logical items (which
 // share K/V) run on the same XCD (blocks are dealt to the 8 XCDs round robin) and
@@ -111,23 +116,48 @@ __device__ __forceinline__ int swz(int r) {
   return ((r & 3) | (((r >> 3) & 3) << 2)) & (G - 1);
 }
 
-// One 16-byte LDS DMA per lane: lane l's data lands at lds + 16*l bytes.
-__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
-  __builtin_amdgcn_global_load_lds((const void*)g, CPATTN_LDS(void, lds), 16, 0, 0);
+// A pointer that is the same in every lane, forced into scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// One 16-byte LDS DMA per lane (global_load_lds_dwordx4): lane l's 16 bytes from
+// base + off (base the same in every lane, off the lane's byte offset) land at
+// lds + 16 l bytes.  It is issued from inline assembly so that the compiler does not
+// track it as an LDS write: the compiler waits for every pending LDS DMA before an LDS
+// read it cannot prove disjoint (a transposing read always), which would serialise the
+// DMA of the next tile with the compute on the current one.  The kernels order DMA and
+// reads themselves: a DMA'd buffer is read only after wait_vm_all() and a workgroup
+// barrier, and is refilled only after the barrier that follows its last read.  M0
+// holds the LDS address (no compiler-generated code in these kernels uses M0); the
+// s_nop separates the M0 write from its use.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, const void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)CPATTN_LDS(const void, lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(l), "v"(off), "s"(base)
+               : "memory", "m0");
 }
 
 // DMA an R-row tile: tile row r comes from base + min(r, nvalid-1) * rs (rows past
 // the valid ones repeat the last valid row: finite data, masked by the caller).
+// R rows of rs elements span less than 2 GiB (R * rs * 2 bytes), so the lane offset is
+// 32-bit.
 template <int D, int R, int NW = 4, int KIND = 0>
 __device__ __forceinline__ void dma_rows(uint16_t* lds, const uint16_t* base, int64_t rs,
                                          int nvalid, int wave, int lane) {
   constexpr int G = D / 8;
   constexpr int NI = R * G / 64;  // wave instructions per tile
+  const char* b = uniform_ptr(base);
+  const uint32_t rs_bytes = (uint32_t)(rs * 2);
   for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += NW) {
     const int idx = i * 64 + lane;
     const int r = idx / G, p = idx % G;
-    const int64_t row = min(r, nvalid - 1);
-    dma16(base + row * rs + ((p ^ swz<D, KIND>(r)) * 8), lds + i * 512);
+    const uint32_t row = (uint32_t)min(r, nvalid - 1);
+    dma16(b, row * rs_bytes + (uint32_t)((p ^ swz<D, KIND>(r)) * 16), lds + i * 512);
   }
 }
 

@@ -80,14 +80,7 @@ __device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_
 }
 
 // The DMA helpers address as a uniform base (forced into scalar registers) plus a
-// 32-bit per-lane byte offset (a 32-row tile spans less than 2 GiB), so no 64-bit
-// per-lane pointer is kept live across the loop.
-__device__ __forceinline__ const char* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
-}
+// 32-bit per-lane byte offset (a 32-row tile spans less than 2 GiB).
 
 // DMA rows [0, 32) of a tile into the padded layout.  Rows past nvalid repeat the last
 // valid row (finite data, masked by the caller); pad granules and the slack after the
@@ -101,8 +94,7 @@ __device__ __forceinline__ void dma_nat(uint16_t* lds, const uint16_t* base, uin
     const int slot = i * 64 + lane;
     const int r = slot / T::G, j = slot - r * T::G;
     const uint32_t row = (uint32_t)min(min(r, kTq - 1), nvalid - 1);
-    const uint32_t off = row * rs_bytes + (uint32_t)min(j, D / 8 - 1) * 16u;
-    __builtin_amdgcn_global_load_lds((const void*)(b + off), CPATTN_LDS(void, lds + i * 512), 16, 0, 0);
+    dma16(b, row * rs_bytes + (uint32_t)min(j, D / 8 - 1) * 16u, lds + i * 512);
   }
 }
 
@@ -112,8 +104,7 @@ __device__ __forceinline__ void dma_flat(uint16_t* lds, const uint16_t* src, int
   constexpr int NI = D * kTq * 2 / 1024;
   const char* b = uniform_ptr(src);
   for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += kWaves)
-    __builtin_amdgcn_global_load_lds((const void*)(b + (uint32_t)(i * 1024 + lane * 16)),
-                                     CPATTN_LDS(void, lds + i * 512), 16, 0, 0);
+    dma16(b, (uint32_t)(i * 1024 + lane * 16), lds + i * 512);
 }
 
 template <int D>
@@ -132,13 +123,15 @@ __device__ __forceinline__ void dma_tiles(uint16_t* lq, uint16_t* ldo, uint16_t*
   dma_flat<D>(ldot, a.dot + toff, wave, lane);
 }
 
-// LSE (as base 2) and Delta of tile row r (clamped to the valid rows).
+// LSE and Delta of tile row r (clamped to the valid rows), as loaded: the values are
+// first used after the step's wait for all loads, so the loads never make a wave wait
+// for the tile DMA issued after them.
 __device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& it, int g, int r,
-                                           float& lse2, float& dl) {
+                                           float& lse, float& dl) {
   const int h = g * a.group + it.hh;
   const int nq = min(kTq, it.ch.len - it.qt * kTq);
   const int64_t idx = (int64_t)h * a.q_rows + it.ch.q_row + it.qt * kTq + min(r, nq - 1);
-  lse2 = a.lse[idx] * kLog2e;
+  lse = a.lse[idx];
   dl = a.delta[idx];
 }
 
@@ -237,7 +230,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     dma_tiles<D>(lds_q[0], lds_do[0], lds_qt[0], lds_dot[0], a, cur, g, wave, lane);
     if (tid < kTq) {
       load_stats(a, cur, g, tid, st_lse, st_dl);
-      lds_lse[0][tid] = st_lse;
+      lds_lse[0][tid] = st_lse * kLog2e;
       lds_dl[0][tid] = st_dl;
     }
   }
@@ -249,8 +242,6 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     QTileIter nxt = cur;
     const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
     if (have_next) {
-      // stats first: loads complete in order, so waiting for them does not wait for
-      // the tiles issued after them
       if (tid < kTq) load_stats(a, nxt, g, tid, st_lse, st_dl);
       dma_tiles<D>(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_qt[buf ^ 1], lds_dot[buf ^ 1], a, nxt, g,
                    wave, lane);
@@ -322,11 +313,11 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
         }
       }
     }
+    wait_vm_all();
     if (have_next && tid < kTq) {
-      lds_lse[buf ^ 1][tid] = st_lse;
+      lds_lse[buf ^ 1][tid] = st_lse * kLog2e;
       lds_dl[buf ^ 1][tid] = st_dl;
     }
-    wait_vm_all();
     __syncthreads();
     cur = nxt;
     have = have_next;
