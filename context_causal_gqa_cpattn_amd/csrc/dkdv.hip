@@ -16,8 +16,9 @@
 // group, 32-query tile) that sees the key tile; four tiles per step are DMA'd into LDS
 // one step ahead (double buffer):
 //   Q, dO     row-major, one 16-byte pad granule per row (conflict-free 16-byte reads
-//             at immediate offsets), read from the inputs at their physical pitch;
-//   Q^T, dO^T the pre-pass's transposed tiles, copied as they are.
+//             at immediate offsets);
+//   Q^T, dO^T transposed.
+// The pre-pass writes all four as contiguous blocks, so every copy is a flat DMA.
 // Per tile, with 32x32x16 MFMAs (C layout: lane = key, 16 query rows per lane):
 //   S  = Q K^T,  dP = dO V^T           (A = Q / dO rows, B = K^T / V^T registers)
 //   P = exp2(S scale log2e - LSE log2e), dS = P (dP - Delta)
@@ -39,13 +40,11 @@ constexpr int kKvThreads = kWaves * 64;
 static_assert(kWaves * 32 == kDkdvKeys, "keys per workgroup");
 
 // A row-major 32 x D tile with one pad granule per row: row r, granule j at element
-// r * (D + 8) + 8 j.  The slot count is rounded up to whole 64-lane DMA instructions.
+// r * (D + 8) + 8 j, as the pre-pass writes it (rounded up to whole 1 KB DMA blocks).
 template <int D>
 struct NatTile {
-  static constexpr int G = D / 8 + 1;  // granules per padded row
-  static constexpr int SLOTS = (kTq * G + 63) / 64 * 64;
-  static constexpr int ELEMS = SLOTS * 8;
-  static constexpr int NI = SLOTS / 64;  // DMA instructions per tile
+  static constexpr int ELEMS = nat_tile_elems(D);
+  static constexpr int NI = ELEMS * 2 / 1024;  // DMA instructions per tile
 };
 
 struct QTileIter {
@@ -79,29 +78,10 @@ __device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_
   return seek_chunk<CAUSAL>(a, it, c_end, key0);
 }
 
-// The DMA helpers address as a uniform base (forced into scalar registers) plus a
-// 32-bit per-lane byte offset (a 32-row tile spans less than 2 GiB).
 
-// DMA rows [0, 32) of a tile into the padded layout.  Rows past nvalid repeat the last
-// valid row (finite data, masked by the caller); pad granules and the slack after the
-// last row receive copies of real granules and are never read.
-template <int D>
-__device__ __forceinline__ void dma_nat(uint16_t* lds, const uint16_t* base, uint32_t rs_bytes,
-                                        int nvalid, int wave, int lane) {
-  using T = NatTile<D>;
-  const char* b = uniform_ptr(base);
-  for (int i = __builtin_amdgcn_readfirstlane(wave); i < T::NI; i += kWaves) {
-    const int slot = i * 64 + lane;
-    const int r = slot / T::G, j = slot - r * T::G;
-    const uint32_t row = (uint32_t)min(min(r, kTq - 1), nvalid - 1);
-    dma16(b, row * rs_bytes + (uint32_t)min(j, D / 8 - 1) * 16u, lds + i * 512);
-  }
-}
-
-// DMA a contiguous D x 32 transposed tile.
-template <int D>
+// DMA a contiguous tile of NI KB.
+template <int NI>
 __device__ __forceinline__ void dma_flat(uint16_t* lds, const uint16_t* src, int wave, int lane) {
-  constexpr int NI = D * kTq * 2 / 1024;
   const char* b = uniform_ptr(src);
   for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += kWaves)
     dma16(b, (uint32_t)(i * 1024 + lane * 16), lds + i * 512);
@@ -111,16 +91,11 @@ template <int D>
 __device__ __forceinline__ void dma_tiles(uint16_t* lq, uint16_t* ldo, uint16_t* lqt, uint16_t* ldot,
                                           const AttnArgs& a, const QTileIter& it, int g, int wave,
                                           int lane) {
-  const int h = g * a.group + it.hh;
-  const int64_t rs = (int64_t)a.hq * D;
-  const int64_t off = ((int64_t)it.ch.q_row + it.qt * kTq) * rs + (int64_t)h * D;
-  const int nq = min(kTq, it.ch.len - it.qt * kTq);
-  const uint32_t rs_bytes = (uint32_t)(rs * 2);
-  dma_nat<D>(lq, a.q + off, rs_bytes, nq, wave, lane);
-  dma_nat<D>(ldo, a.dout + off, rs_bytes, nq, wave, lane);
-  const int64_t toff = (tile_slot(it.c, it.ch.q_row, it.qt) * a.hq + h) * D * kTq;
-  dma_flat<D>(lqt, a.qt + toff, wave, lane);
-  dma_flat<D>(ldot, a.dot + toff, wave, lane);
+  const int64_t unit = tile_slot(it.c, it.ch.q_row, it.qt) * a.hq + g * a.group + it.hh;
+  dma_flat<NatTile<D>::NI>(lq, a.qn + unit * NatTile<D>::ELEMS, wave, lane);
+  dma_flat<NatTile<D>::NI>(ldo, a.don + unit * NatTile<D>::ELEMS, wave, lane);
+  dma_flat<D * kTq * 2 / 1024>(lqt, a.qt + unit * D * kTq, wave, lane);
+  dma_flat<D * kTq * 2 / 1024>(ldot, a.dot + unit * D * kTq, wave, lane);
 }
 
 // LSE and Delta of tile row r (clamped to the valid rows), as loaded: the values are
