@@ -229,12 +229,11 @@ def main():
     dom = max((n for n in per_kernel if n in algo), key=lambda n: per_kernel[n])
     dom_flop = pairs * algo[dom]
     achieved = dom_flop / (per_kernel[dom] * 1e-3) / 1e12
-    # pre-pass: reads Q, O, dO; writes Delta, the Q^T / dO^T tiles (32 queries, zero
-    # padded) and the row-major Q / dO tiles (rows of D + 8, 1 KB-rounded)
+    # pre-pass: reads Q, O, dO; writes Delta and the Q^T / dO^T tiles (32 queries, zero
+    # padded)
     n_tiles = int(sum(-(-int(n) // 32) for n in w.chunks[:, 3]))
-    nat_elems = -(-(32 * (D + 8)) // 512) * 512
     pre_bytes = (3 * w.q_valid_rows().sum() * w.hq * D * 2 + 4 * w.q_valid_rows().sum() * w.hq
-                 + 2 * n_tiles * w.hq * (32 * D + nat_elems) * 2)
+                 + 2 * n_tiles * w.hq * 32 * D * 2)
 
     line = {
         "metric": METRIC,

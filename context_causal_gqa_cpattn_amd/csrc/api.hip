@@ -83,8 +83,8 @@ struct Plan {
   int64_t delta_bytes;  // rounded to 256
   int parts;            // dBias partitions
   int64_t partial_bytes;
-  // backward workspace: delta | Q^T | dO^T | Q rows | dO rows | dBias partials
-  int64_t off_qt, off_dot, off_qn, off_don, off_partials, ws_core;
+  // backward workspace: delta | Q^T tiles | dO^T tiles | dBias partials
+  int64_t off_qt, off_dot, off_partials, ws_core;
   dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias;
   int bpc_fwd, bpc_prepass, kv_tiles;
 };
@@ -155,11 +155,8 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   const int64_t max_tiles = cdiv(p->q_rows, kPrepassRows) + p->num_chunks;
   const int64_t tile_bytes = max_tiles * p->hq * (int64_t)D * kPrepassRows * 2;
   pl.off_qt = pl.delta_bytes;
-  const int64_t nat_bytes = max_tiles * p->hq * (int64_t)nat_tile_elems(D) * 2;
   pl.off_dot = pl.off_qt + round256(tile_bytes);
-  pl.off_qn = pl.off_dot + round256(tile_bytes);
-  pl.off_don = pl.off_qn + round256(nat_bytes);
-  pl.off_partials = pl.off_don + round256(nat_bytes);
+  pl.off_partials = pl.off_dot + round256(tile_bytes);
   pl.ws_core = pl.off_partials;
   pl.grid_prepass = dim3((unsigned)gx_pre, (unsigned)p->hq);
   return CPATTN_OK;
@@ -326,8 +323,6 @@ AttnArgs bwd_args(const cpattn_problem* p, const Plan& pl, const void* q, const 
   const float* delta = (const float*)w;
   a.qt = (const uint16_t*)(w + pl.off_qt);
   a.dot = (const uint16_t*)(w + pl.off_dot);
-  a.qn = (const uint16_t*)(w + pl.off_qn);
-  a.don = (const uint16_t*)(w + pl.off_don);
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
@@ -352,8 +347,6 @@ int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, 
   a.delta_out = (float*)w;
   a.qt_out = (uint16_t*)(w + pl.off_qt);
   a.dot_out = (uint16_t*)(w + pl.off_dot);
-  a.qn_out = (uint16_t*)(w + pl.off_qn);
-  a.don_out = (uint16_t*)(w + pl.off_don);
   a.chunks = cm;
   a.dev_err = dev_err;
   a.blocks_per_chunk = pl.bpc_prepass;

@@ -24,10 +24,7 @@ namespace cpattn {
 //    layout in which dK/dV contracts over queries with 16-byte LDS reads.  Within each
 //    half of 16 queries, position p holds query sigma16(p): the order in which a
 //    32x32 accumulator lists one lane's rows, so that dK/dV's P and dS registers are
-//    B operands as they are.  Granule g of row d is stored at g ^ tswz(d);
-//  - the tile's Q and dO row-major with one pad granule per row (row q at q (D + 8),
-//    rows past the chunk zero), so that dK/dV copies every tile it needs as one
-//    contiguous block.
+//    B operands as they are.  Granule g of row d is stored at g ^ tswz(d).
 // Tile qt of chunk c is stored at slot tile_slot(c, q_row, qt).
 
 constexpr int kTileQ = 32;
@@ -86,10 +83,6 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(const AttnArgs a) {
       }
     }
   }
-  // padded row-major copy: row qi, granule dg (the pad granule is left unwritten)
-  uint16_t* nat = (tensor ? a.don_out : a.qn_out) + (tile * a.hq + h) * nat_tile_elems(D);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) st16(nat + (qbase + sigma16(qsub + e)) * (D + 8) + dg * 8, rows[e]);
   transpose8x8(rows, cols);  // cols[d]: the granule's 8 queries at dimension dg*8 + d
   uint16_t* dst = (tensor ? a.dot_out : a.qt_out) + (tile * a.hq + h) * D * kTileQ;
 #pragma unroll

@@ -257,12 +257,8 @@ struct AttnArgs {
   float* delta_out;      // pre-pass output
   uint16_t* qt_out;      // pre-pass output: transposed Q tiles
   uint16_t* dot_out;     // pre-pass output: transposed dO tiles
-  uint16_t* qn_out;      // pre-pass output: padded row-major Q tiles
-  uint16_t* don_out;     // pre-pass output: padded row-major dO tiles
   const uint16_t* qt;    // transposed Q tiles [slot][hq][D][32]
   const uint16_t* dot;   // transposed dO tiles
-  const uint16_t* qn;    // padded row-major Q tiles [slot][hq][nat_tile_elems(D)]
-  const uint16_t* don;   // padded row-major dO tiles
   const int32_t* seq_offsets;
   const int32_t* seq_lens;
   const int32_t* chunks;

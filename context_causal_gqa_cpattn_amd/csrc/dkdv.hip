@@ -13,20 +13,20 @@
 // wave w owns keys [32w, 32w+32) of the tile.  It keeps K^T and V^T of its keys in
 // registers as B operands and dK^T, dV^T (D x 32 keys, fp32) as MFMA accumulators for
 // the whole loop.  The loop runs over every (chunk of the sequence, query head of the
-// group, 32-query tile) that sees the key tile; four tiles per step are DMA'd into LDS
-// one step ahead (double buffer):
-//   Q, dO     row-major, one 16-byte pad granule per row (conflict-free 16-byte reads
-//             at immediate offsets);
-//   Q^T, dO^T transposed.
-// The pre-pass writes all four as contiguous blocks, so every copy is a flat DMA.
+// group, 32-query tile) that sees the key tile.  The pre-pass's transposed tiles Q^T and
+// dO^T ([D][32], contiguous) are DMA'd into LDS one step ahead, three buffers deep.
 // Per tile, with 32x32x16 MFMAs (C layout: lane = key, 16 query rows per lane):
-//   S  = Q K^T,  dP = dO V^T           (A = Q / dO rows, B = K^T / V^T registers)
+//   S  = Q K^T,  dP = dO V^T           (A = Q / dO rows: two transposing reads of the
+//                                       transposed tiles; B = K^T / V^T registers)
 //   P = exp2(S scale log2e - LSE log2e), dS = P (dP - Delta)
-//   dV^T += dO^T P,  dK^T += Q^T dS    (A = transposed tiles, B = P / dS as packed)
+//   dV^T += dO^T P,  dK^T += Q^T dS    (A = 16-byte reads of the transposed tiles,
+//                                       B = P / dS as packed)
 // The pre-pass stores the transposed tiles in the query order of the accumulator rows,
-// so P and dS become B operands without any data movement.  dK = scale dK^T and dV are
-// rounded to BF16 once (STORE), or added to the existing BF16 values and rounded once
-// (ADD).
+// so P and dS become B operands without any data movement.  The steps are software
+// pipelined: while the S/dP products of tile i are done, the softmax of tile i runs
+// between the dV/dK products of tile i-1, so that VALU work issues while the matrix
+// cores are busy.  dK = scale dK^T and dV are rounded to BF16 once (STORE), or added to
+// the existing BF16 values and rounded once (ADD).
 #include "common.h"
 #include "launch.h"
 
@@ -35,17 +35,10 @@ namespace cpattn {
 namespace {
 
 constexpr int kTq = 32;     // queries per tile
+constexpr int kBufs = 3;    // LDS tile buffers (DMA one step ahead + the step before)
 constexpr int kWaves = 4;   // waves per workgroup, 32 keys each
 constexpr int kKvThreads = kWaves * 64;
 static_assert(kWaves * 32 == kDkdvKeys, "keys per workgroup");
-
-// A row-major 32 x D tile with one pad granule per row: row r, granule j at element
-// r * (D + 8) + 8 j, as the pre-pass writes it (rounded up to whole 1 KB DMA blocks).
-template <int D>
-struct NatTile {
-  static constexpr int ELEMS = nat_tile_elems(D);
-  static constexpr int NI = ELEMS * 2 / 1024;  // DMA instructions per tile
-};
 
 struct QTileIter {
   int c, hh, qt, qt_first, n_qt;
@@ -88,12 +81,9 @@ __device__ __forceinline__ void dma_flat(uint16_t* lds, const uint16_t* src, int
 }
 
 template <int D>
-__device__ __forceinline__ void dma_tiles(uint16_t* lq, uint16_t* ldo, uint16_t* lqt, uint16_t* ldot,
-                                          const AttnArgs& a, const QTileIter& it, int g, int wave,
-                                          int lane) {
+__device__ __forceinline__ void dma_tiles(uint16_t* lqt, uint16_t* ldot, const AttnArgs& a,
+                                          const QTileIter& it, int g, int wave, int lane) {
   const int64_t unit = tile_slot(it.c, it.ch.q_row, it.qt) * a.hq + g * a.group + it.hh;
-  dma_flat<NatTile<D>::NI>(lq, a.qn + unit * NatTile<D>::ELEMS, wave, lane);
-  dma_flat<NatTile<D>::NI>(ldo, a.don + unit * NatTile<D>::ELEMS, wave, lane);
   dma_flat<D * kTq * 2 / 1024>(lqt, a.qt + unit * D * kTq, wave, lane);
   dma_flat<D * kTq * 2 / 1024>(ldot, a.dot + unit * D * kTq, wave, lane);
 }
@@ -110,33 +100,26 @@ __device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& i
   dl = a.delta[idx];
 }
 
-// P and dS of one tile in place (s -> P, dp -> dS).  Element r of a lane is query
-// 8 (r / 4) + 4 hl + r % 4 of the tile; the lane's key is `key`.
-template <bool MASK, bool CAUSAL, bool BIAS>
-__device__ __forceinline__ void softmax_grad(f32x16& s, f32x16& dp, const float* lse, const float* dl,
-                                             int hl, float c, int key, bool key_ok, int nq,
-                                             int tile_pos0, const float* bias_h, int bias_len) {
+// P and dS of accumulator elements [r0, r0 + n) of a lane, in place (s -> P, dp -> dS).
+// Element r is query 8 (r / 4) + 4 hl + r % 4 of the tile; the lane's key is `key`.
+// The mask is applied on every tile (a few VALU operations that issue under the MFMAs).
+template <int N, bool CAUSAL, bool BIAS>
+__device__ __forceinline__ void softmax_part(f32x16& s, f32x16& dp, int r0, const float* lse,
+                                             const float* dl, int hl, float c, int key,
+                                             bool key_ok, int nq, int tile_pos0,
+                                             const float* bias_h, int bias_len) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q0 = 8 * i + 4 * hl;
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse + q0);
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + q0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * i + j, qi = q0 + j;
-      float x = s[r] * c;
-      if (BIAS)
-        x = fmaf(bias_h[(int64_t)min(tile_pos0 + qi, bias_len - 1) * bias_len + min(key, bias_len - 1)],
-                 kLog2e, x);
-      x -= l4[j];
-      if (MASK) {
-        const bool vis = key_ok && qi < nq && (!CAUSAL || key <= tile_pos0 + qi);
-        x = vis ? x : -INFINITY;
-      }
-      const float p = exp2f_fast(x);
-      s[r] = p;
-      dp[r] = p * (dp[r] - d4[j]);
-    }
+  for (int k = 0; k < N; ++k) {
+    const int r = r0 + k, qi = 8 * (r >> 2) + 4 * hl + (r & 3);
+    float x = s[r] * c;
+    if (BIAS)
+      x = fmaf(bias_h[(int64_t)min(tile_pos0 + qi, bias_len - 1) * bias_len + min(key, bias_len - 1)],
+               kLog2e, x);
+    x -= lse[qi];
+    const bool vis = key_ok && qi < nq && (!CAUSAL || key <= tile_pos0 + qi);
+    const float p = exp2f_fast(vis ? x : -INFINITY);
+    s[r] = p;
+    dp[r] = p * (dp[r] - dl[qi]);
   }
 }
 
@@ -144,15 +127,16 @@ __device__ __forceinline__ void softmax_grad(f32x16& s, f32x16& dp, const float*
 
 template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
-  constexpr int NS = D / 16;  // 16-deep k-steps of S and dP
-  constexpr int NB = D / 32;  // 32-row blocks of dK^T and dV^T
-  using T = NatTile<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_q[2][T::ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_do[2][T::ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_qt[2][D * kTq];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_dot[2][D * kTq];
-  __shared__ __attribute__((aligned(16))) float lds_lse[2][kTq];
-  __shared__ __attribute__((aligned(16))) float lds_dl[2][kTq];
+  constexpr int NS = D / 16;       // 16-deep k-steps of S and dP
+  constexpr int NB = D / 32;       // 32-row blocks of dK^T and dV^T
+  constexpr int TE = D * kTq;      // elements of one transposed tile
+  constexpr int EPB = 16 / NB;     // softmax elements per dV/dK block
+  // Software pipelining needs registers for two tiles' P/dS; with D = 256 the
+  // accumulators fill the accumulation registers and the steps run in order instead.
+  constexpr bool PIPE = D <= 128;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_t[kBufs][2][TE];  // [buf][Q^T, dO^T]
+  __shared__ __attribute__((aligned(16))) float lds_lse[kBufs][kTq];
+  __shared__ __attribute__((aligned(16))) float lds_dl[kBufs][kTq];
 
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -189,10 +173,22 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     dkt[blk] = f32x16{};
     dvt[blk] = f32x16{};
   }
-  // Lane offsets: S/dP A operand = row n, granule 2 st + hl of the padded tiles;
-  // dV/dK A operand, k-step t = row 32 blk + n, granule (2 t + hl) ^ tswz(n) of the
-  // transposed tiles (tswz depends on the row's bits 2-3 only).
-  const int nat_off = n * (D + 8) + hl * 8;
+  // S/dP A operand, k-step st: row n of S is tile query n; its 8 values are dimensions
+  // 16 st + 8 hl + 4 r + j (r = 0, 1 reads), gathered by transposing reads in which
+  // source lane 4 j + m of each 16-lane group reads dimension row 16 st + 8 hl + 4 r + j
+  // at stored query positions c0 .. c0 + 3, c0 = 16 (group & 1) + 4 swap2(m) (the stored
+  // order sigma16 within 16 queries, undone).  The row's granule swizzle is
+  // tswz = 2 hl + r, the same for every st.
+  int tra[2];
+  {
+    const int grp = lane >> 4, j = (lane >> 2) & 3, m = lane & 3;
+    const int sm = ((m & 1) << 1) | (m >> 1);
+    const int gq = 2 * (grp & 1) + (sm >> 1);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      tra[r] = (8 * hl + 4 * r + j) * kTq + ((gq ^ (2 * hl + r)) * 8) + 4 * (sm & 1);
+  }
+  // dV/dK A operand, k-step t: row 32 blk + n, granule (2 t + hl) ^ tswz(n).
   const int tr_off0 = n * kTq + ((hl ^ tswz(n)) * 8);
   const int tr_off1 = n * kTq + (((2 + hl) ^ tswz(n)) * 8);
 
@@ -202,7 +198,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0);
   float st_lse = 0.f, st_dl = 0.f;  // stats staged for the next tile (threads < kTq)
   if (have) {
-    dma_tiles<D>(lds_q[0], lds_do[0], lds_qt[0], lds_dot[0], a, cur, g, wave, lane);
+    dma_tiles<D>(lds_t[0][0], lds_t[0][1], a, cur, g, wave, lane);
     if (tid < kTq) {
       load_stats(a, cur, g, tid, st_lse, st_dl);
       lds_lse[0][tid] = st_lse * kLog2e;
@@ -212,92 +208,112 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   wait_vm_all();
   __syncthreads();
 
-  int buf = 0;
+  // dV/dK products of one tile: A operands from buffer pb, B = packed P / dS.  The
+  // operand stream (per block: dO^T steps 0 and 1, then Q^T steps 0 and 1) is read
+  // three products ahead.  Between the blocks, body(blk) issues independent work.
+  auto dvdk = [&](int pb, const u32x4 (&pp)[2], const u32x4 (&pd)[2], auto&& body) {
+    const uint16_t* qtt = lds_t[pb][0];
+    const uint16_t* dtt = lds_t[pb][1];
+    constexpr int NOP = 4 * NB;
+    auto operand = [&](int i) {
+      const int blk = i >> 2, which = i & 3;
+      const uint16_t* t = (which < 2) ? dtt : qtt;
+      return ld16(t + blk * 32 * kTq + ((which & 1) ? tr_off1 : tr_off0));
+    };
+    u32x4 f[4];
+    f[0] = operand(0);
+    f[1] = operand(1);
+    f[2] = operand(2);
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      if (i + 3 < NOP) f[(i + 3) & 3] = operand(i + 3);
+      const int blk = i >> 2, which = i & 3;
+      if (which < 2) dvt[blk] = mfma32(f[i & 3], pp[which], dvt[blk]);
+      else dkt[blk] = mfma32(f[i & 3], pd[which & 1], dkt[blk]);
+      if (which == 3) body(blk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  u32x4 pp[2] = {}, pd[2] = {};  // packed P and dS of the previous tile
+  int buf = 0, pbuf = 0;
+  bool have_prev = false;
   while (have) {
     QTileIter nxt = cur;
     const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
+    const int nbuf = (buf + 1 == kBufs) ? 0 : buf + 1;
     if (have_next) {
       if (tid < kTq) load_stats(a, nxt, g, tid, st_lse, st_dl);
-      dma_tiles<D>(lds_q[buf ^ 1], lds_do[buf ^ 1], lds_qt[buf ^ 1], lds_dot[buf ^ 1], a, nxt, g,
-                   wave, lane);
+      dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, g, wave, lane);
     }
 
     // Every wave runs every tile of the loop: tiles that a wave's keys do not see (at the
     // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
     const int nq = min(kTq, cur.ch.len - cur.qt * kTq);
     const int tile_pos0 = cur.ch.pos0 + cur.qt * kTq;
+    const float* bias_h =
+        BIAS ? a.bias + (int64_t)(g * a.group + cur.hh) * a.bias_len * a.bias_len : nullptr;
+
+    // S and dP of this tile; each A operand is read one k-step ahead.
+    f32x16 s = {}, dp = {};
     {
-      const uint16_t* lq = lds_q[buf] + nat_off;
-      const uint16_t* ld = lds_do[buf] + nat_off;
-      // S, then dP: each A operand is read two k-steps ahead of its product (the
-      // scheduling barriers keep the compiler from hoisting every read at once).
-      f32x16 s = {}, dp = {};
-      {
-        u32x4 f[3];
-        f[0] = ld16(lq);
-        f[1] = ld16(lq + 16);
+      const uint16_t* qtt = lds_t[buf][0];
+      const uint16_t* dtt = lds_t[buf][1];
+      auto tr_a = [&](const uint16_t* t, int st) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[0]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[1]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+      };
+      u32x4 fq = tr_a(qtt, 0), fd = tr_a(dtt, 0);
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          if (st + 2 < NS) f[(st + 2) % 3] = ld16(lq + (st + 2) * 16);
-          else f[(st + 2) % 3] = ld16(ld + (st + 2 - NS) * 16);
-          s = mfma32(f[st % 3], kf[st], s);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int st = 0; st < NS; ++st) {
+        u32x4 nq_ = fq, nd_ = fd;
+        if (st + 1 < NS) {
+          nq_ = tr_a(qtt, st + 1);
+          nd_ = tr_a(dtt, st + 1);
         }
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          if (st + 2 < NS) f[(NS + st + 2) % 3] = ld16(ld + (st + 2) * 16);
-          dp = mfma32(f[(NS + st) % 3], vf[st], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      const bool need_mask = (nk < 32) || (nq < kTq) || (CAUSAL && tile_pos0 < wkey0 + 31);
-      const float* bias_h =
-          BIAS ? a.bias + (int64_t)(g * a.group + cur.hh) * a.bias_len * a.bias_len : nullptr;
-      if (need_mask)
-        softmax_grad<true, CAUSAL, BIAS>(s, dp, lds_lse[buf], lds_dl[buf], hl, a.scale_log2, key,
-                                         key_ok, nq, tile_pos0, bias_h, a.bias_len);
-      else
-        softmax_grad<false, CAUSAL, BIAS>(s, dp, lds_lse[buf], lds_dl[buf], hl, a.scale_log2, key,
-                                          key_ok, nq, tile_pos0, bias_h, a.bias_len);
-      // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
-      const u32x4 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 8);
-      const u32x4 ds0 = to_bf16x8(dp, 0), ds1 = to_bf16x8(dp, 8);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint16_t* qtt = lds_qt[buf];
-      const uint16_t* dtt = lds_dot[buf];
-      // dV^T and dK^T: the A operands form one stream (per block: dO^T step 0 and 1, then
-      // Q^T step 0 and 1), each read three products ahead.
-      {
-        constexpr int NOP = 4 * NB;
-        auto operand = [&](int i) {
-          const int blk = i >> 2, which = i & 3;
-          const uint16_t* t = (which < 2) ? dtt : qtt;
-          return ld16(t + blk * 32 * kTq + ((which & 1) ? tr_off1 : tr_off0));
-        };
-        u32x4 f[4];
-        f[0] = operand(0);
-        f[1] = operand(1);
-        f[2] = operand(2);
-#pragma unroll
-        for (int i = 0; i < NOP; ++i) {
-          if (i + 3 < NOP) f[(i + 3) & 3] = operand(i + 3);
-          const int blk = i >> 2, which = i & 3;
-          if (which < 2) dvt[blk] = mfma32(f[i & 3], which ? p1 : p0, dvt[blk]);
-          else dkt[blk] = mfma32(f[i & 3], (which & 1) ? ds1 : ds0, dkt[blk]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        s = mfma32(fq, kf[st], s);
+        dp = mfma32(fd, vf[st], dp);
+        fq = nq_;
+        fd = nd_;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+
+    // Softmax of this tile, between the dV/dK products of the previous one.
+    const float* lse = lds_lse[buf];
+    const float* dl = lds_dl[buf];
+    auto sm_block = [&](int blk) {
+      softmax_part<EPB, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok, nq,
+                                      tile_pos0, bias_h, a.bias_len);
+    };
+    if (PIPE && have_prev) {
+      dvdk(pbuf, pp, pd, sm_block);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) sm_block(blk);
+    }
+    // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
+    pp[0] = to_bf16x8(s, 0);
+    pp[1] = to_bf16x8(s, 8);
+    pd[0] = to_bf16x8(dp, 0);
+    pd[1] = to_bf16x8(dp, 8);
+    if (!PIPE) dvdk(buf, pp, pd, [](int) {});
+
     wait_vm_all();
     if (have_next && tid < kTq) {
-      lds_lse[buf ^ 1][tid] = st_lse * kLog2e;
-      lds_dl[buf ^ 1][tid] = st_dl;
+      lds_lse[nbuf][tid] = st_lse * kLog2e;
+      lds_dl[nbuf][tid] = st_dl;
     }
     __syncthreads();
     cur = nxt;
     have = have_next;
-    buf ^= 1;
+    have_prev = true;
+    pbuf = buf;
+    buf = nbuf;
   }
+  if (PIPE && have_prev) dvdk(pbuf, pp, pd, [](int) {});
 
   if (!key_ok) return;
   // element r of block blk is dimension 32 blk + 8 (r / 4) + 4 hl + r % 4

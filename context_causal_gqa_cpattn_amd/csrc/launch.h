@@ -40,9 +40,6 @@ hipError_t launch_dbias_reduce(const float* partial, float* out, int64_t n, int 
 
 // Rows of a chunk handled by one pre-pass workgroup (one query tile).
 constexpr int kPrepassRows = 32;
-// Elements of a row-major 32-row query tile with one 16-byte pad granule per row,
-// rounded up to whole 64-lane DMA instructions (1 KB).
-constexpr int nat_tile_elems(int D) { return (32 * (D / 8 + 1) + 63) / 64 * 64 * 8; }
 // Keys per dK/dV workgroup (four waves of 32 keys).
 constexpr int kDkdvKeys = 128;
 // dBias tile: 128 query positions x 64 keys per workgroup.

@@ -115,9 +115,7 @@ int cpattn_version(void);
  * or cpattn_bwd (op = CPATTN_OP_BWD) needs for `p`.  The backward workspace holds,
  * each part starting on a 256-byte boundary: Delta (fp32 [hq, q_rows], at offset
  * 0); Q^T and dO^T as BF16 tiles [slot][hq][head_dim][32 queries, in an internal
- * order]; Q and dO as BF16 row-major tiles [slot][hq][E] with rows of head_dim + 8
- * elements (E = 32 (head_dim + 8) rounded up to a multiple of 512); the tiles have
- * ceil(q_rows/32) + num_chunks slots (tile t of chunk c is slot
+ * order] with ceil(q_rows/32) + num_chunks slots (tile t of chunk c is slot
  * floor(q_row_c / 32) + c + t; queries past the chunk end are zero); and, with a
  * bias, the per-partition dBias partial sums.  Returns 0 for an invalid
  * problem (check it with the entry point for the reason). */

@@ -106,9 +106,7 @@ def _ws_layout(hq, q_rows, num_chunks, head_dim):
     """Backward workspace bytes without dBias partials, from the layout the header states."""
     r256 = lambda x: (x + 255) // 256 * 256
     tiles = -(-q_rows // 32) + num_chunks
-    nat = -(-(32 * (head_dim + 8)) // 512) * 512
-    return (r256(hq * q_rows * 4) + 2 * r256(tiles * hq * head_dim * 32 * 2)
-            + 2 * r256(tiles * hq * nat * 2))
+    return r256(hq * q_rows * 4) + 2 * r256(tiles * hq * head_dim * 32 * 2)
 
 
 def test_workspace_sizes():
