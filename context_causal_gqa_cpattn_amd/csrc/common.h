@@ -134,30 +134,71 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
 // barrier, and is refilled only after the barrier that follows its last read.  M0
 // holds the LDS address (no compiler-generated code in these kernels uses M0); the
 // s_nop separates the M0 write from its use.
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, const void* lds) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)CPATTN_LDS(const void, lds));
+__device__ __forceinline__ void dma16_at(const char* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(l), "v"(off), "s"(base)
+               : "s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
+}
+
+// 32-bit LDS address of a shared-memory pointer that is the same in every lane.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)CPATTN_LDS(const void, p));
+}
+
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, const void* lds) {
+  dma16_at(base, off, lds_addr(lds));
+}
+
+// DMA a contiguous block of NI KB into LDS, instructions dealt round robin over NW waves.
+// Addresses are a scalar base plus the lane's 16-byte slot.
+template <int NI, int NW = 4>
+__device__ __forceinline__ void dma_flat(uint16_t* lds, const uint16_t* src, int wave, int lane) {
+  const char* b = uniform_ptr(src);
+  const uint32_t l0 = lds_addr(lds);
+  const uint32_t lo = (uint32_t)lane * 16u;
+  for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += NW)
+    dma16_at(b + i * 1024, lo, l0 + i * 1024);
 }
 
 // DMA an R-row tile: tile row r comes from base + min(r, nvalid-1) * rs (rows past
 // the valid ones repeat the last valid row: finite data, masked by the caller).
-// R rows of rs elements span less than 2 GiB (R * rs * 2 bytes), so the lane offset is
-// 32-bit.
+// Instruction i of the tile carries rows [i RPI, i RPI + RPI) (RPI = 64 / (D/8)); wave w
+// issues i = w, w + NW, ...  For a full tile the row part of each address is scalar and
+// the lane part (row within the instruction, swizzled granule) repeats with period 2
+// in the wave's instruction index, since the swizzle depends on the row mod 16; so the
+// lane parts are computed once.  R rows of rs elements span less than 2 GiB.
 template <int D, int R, int NW = 4, int KIND = 0>
 __device__ __forceinline__ void dma_rows(uint16_t* lds, const uint16_t* base, int64_t rs,
                                          int nvalid, int wave, int lane) {
   constexpr int G = D / 8;
-  constexpr int NI = R * G / 64;  // wave instructions per tile
+  constexpr int RPI = 64 / G;          // rows per instruction
+  constexpr int NI = R * G / 64;       // instructions per tile
+  constexpr int NK = (NI + NW - 1) / NW;
+  static_assert((2 * NW * RPI) % 16 == 0, "lane offsets repeat with period 2");
+  static_assert(KIND < 2, "swizzles of kinds 0 and 1 depend on the row mod 16 only");
   const char* b = uniform_ptr(base);
   const uint32_t rs_bytes = (uint32_t)(rs * 2);
-  for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += NW) {
-    const int idx = i * 64 + lane;
-    const int r = idx / G, p = idx % G;
-    const uint32_t row = (uint32_t)min(r, nvalid - 1);
-    dma16(b, row * rs_bytes + (uint32_t)((p ^ swz<D, KIND>(r)) * 16), lds + i * 512);
+  const uint32_t l0 = lds_addr(lds);
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = lane / G, p = lane % G;
+  if (nvalid >= R) {
+    uint32_t o[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      o[e] = (uint32_t)lr * rs_bytes + (uint32_t)((p ^ swz<D, KIND>((w + NW * e) * RPI + lr)) * 16);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int i = w + NW * k;
+      if (NI % NW == 0 || i < NI)
+        dma16_at(b + (uint64_t)(i * RPI) * rs_bytes, o[k & 1], l0 + i * 1024);
+    }
+  } else {
+    for (int i = w; i < NI; i += NW) {
+      const int r = i * RPI + lr;
+      const uint32_t row = (uint32_t)min(r, nvalid - 1);
+      dma16_at(b, row * rs_bytes + (uint32_t)((p ^ swz<D, KIND>(r)) * 16), l0 + i * 1024);
+    }
   }
 }
 

@@ -72,20 +72,12 @@ __device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_
 }
 
 
-// DMA a contiguous tile of NI KB.
-template <int NI>
-__device__ __forceinline__ void dma_flat(uint16_t* lds, const uint16_t* src, int wave, int lane) {
-  const char* b = uniform_ptr(src);
-  for (int i = __builtin_amdgcn_readfirstlane(wave); i < NI; i += kWaves)
-    dma16(b, (uint32_t)(i * 1024 + lane * 16), lds + i * 512);
-}
-
 template <int D>
 __device__ __forceinline__ void dma_tiles(uint16_t* lqt, uint16_t* ldot, const AttnArgs& a,
                                           const QTileIter& it, int g, int wave, int lane) {
   const int64_t unit = tile_slot(it.c, it.ch.q_row, it.qt) * a.hq + g * a.group + it.hh;
-  dma_flat<D * kTq * 2 / 1024>(lqt, a.qt + unit * D * kTq, wave, lane);
-  dma_flat<D * kTq * 2 / 1024>(ldot, a.dot + unit * D * kTq, wave, lane);
+  dma_flat<D * kTq * 2 / 1024, kWaves>(lqt, a.qt + unit * D * kTq, wave, lane);
+  dma_flat<D * kTq * 2 / 1024, kWaves>(ldot, a.dot + unit * D * kTq, wave, lane);
 }
 
 // LSE and Delta of tile row r (clamped to the valid rows), as loaded: the values are
