@@ -188,6 +188,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
   f32x16 dqt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
+  const TrOffsets<D> tro(lane);
 
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(const AttnArgs a) {
         const u32x4 dsf = to_bf16x8(dp[st >> 1], (st & 1) * 8);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          dqt[db] = mfma32(tr_frag<D>(kt, st * 16, db, lane), dsf, dqt[db]);
+          dqt[db] = mfma32(tr_frag_at<D>(kt, tro, st, db), dsf, dqt[db]);
       }
     }
     wait_vm_all();

@@ -224,6 +224,38 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t* t, int kr0, int db, int
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
+// Lane parts of the tr_frag addresses, computed once per kernel.  The fragment for
+// rows [16 st, +16) and columns [32 db, +32) of a tile sits at element
+// 16 st D + 128 (db / 4) + lo[db % 4] (and hi[...] for its second read): the swizzle
+// depends on the row mod 16 only and touches granule bits 0-3, so both st and db / 4
+// enter as constants.
+template <int D>
+struct TrOffsets {
+  static constexpr int NM = (D / 32) < 4 ? (D / 32) : 4;
+  int lo[NM], hi[NM];
+  __device__ __forceinline__ explicit TrOffsets(int lane) {
+    const int rr = (lane >> 5) * 4 + ((lane & 15) >> 2);
+    const int gsub = ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1);
+    const int off = (lane & 1) * 4;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int gl = 4 * m + gsub;
+      lo[m] = rr * D + ((gl ^ swz<D>(rr)) << 3) + off;
+      hi[m] = (rr + 8) * D + ((gl ^ swz<D>(rr + 8)) << 3) + off;
+    }
+  }
+};
+
+// tr_frag(t, 16 st, db, lane) with the lane parts precomputed.
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag_at(const uint16_t* t, const TrOffsets<D>& o, int st, int db) {
+  const uint16_t* b = t + st * 16 * D + (db >> 2) * 128;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + o.lo[db & 3]));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + o.hi[db & 3]));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
 // One 16x16x32 BF16 MFMA with fp32 accumulation.
 //  A (16 x 32): lane l holds row l%16, the 8 k-values of lane group l/16.
 //  B (32 x 16): lane l holds column l%16, the same 8 k-values.

@@ -27,11 +27,13 @@ namespace cpattn {
 
 constexpr int kBN = 64;  // keys per KV tile
 
-// Scores of one 64-key tile in base 2 (+ bias), masked when MASK; returns the lane max.
+// Scores of one 64-key tile in base 2 (+ bias), masked when MASK; returns the lane max
+// (four independent running maxima, so the chain is a quarter as long).
 // Element r of block kb is key key0 + 32 kb + 8 (r/4) + 4 kg + r%4.
 template <bool BIAS, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float* bias_row, int key0,
                                            int L, int qpos, int kg, int bias_len, float& mx) {
+  float mj[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -55,9 +57,10 @@ __device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float*
           x = ((key < L) && (!CAUSAL || key <= qpos)) ? x : -INFINITY;
         }
         s[kb][i * 4 + j] = x;
-        mx = fmaxf(mx, x);
+        mj[j] = fmaxf(mj[j], x);
       }
     }
+  mx = fmaxf(fmaxf(mx, fmaxf(mj[0], mj[1])), fmaxf(mj[2], mj[3]));
 }
 
 template <int D, bool CAUSAL, bool BIAS>
@@ -107,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  const TrOffsets<D> tro(lane);
   float m_run = -INFINITY, l_run = 0.f;
 
   const float* bias_row = nullptr;
@@ -177,16 +181,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
         m_run = m_new;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = exp2f_fast(s[kb][r] - m_use);
           s[kb][r] = p;
-          rs += p;
+          rs[r & 3] += p;
         }
-      l_run += rs;
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
       // O^T += V^T P^T over four 16-key steps; the V^T fragment of the next MFMA is
       // requested before the current one issues.
@@ -194,12 +198,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
         u32x4 pf[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) pf[st] = to_bf16x8(s[st >> 1], (st & 1) * 8);
-        u32x4 va = tr_frag<D>(vt, 0, 0, lane);
+        u32x4 va = tr_frag_at<D>(vt, tro, 0, 0);
 #pragma unroll
         for (int it = 0; it < 4 * NDB; ++it) {
           const int st = it / NDB, db = it % NDB;
           u32x4 nv = va;
-          if (it + 1 < 4 * NDB) nv = tr_frag<D>(vt, ((it + 1) / NDB) * 16, (it + 1) % NDB, lane);
+          if (it + 1 < 4 * NDB) nv = tr_frag_at<D>(vt, tro, (it + 1) / NDB, (it + 1) % NDB);
           oacc[db] = mfma32(va, pf[st], oacc[db]);
           va = nv;
         }
