@@ -94,8 +94,9 @@ __device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& i
 
 // P and dS of accumulator elements [r0, r0 + n) of a lane, in place (s -> P, dp -> dS).
 // Element r is query 8 (r / 4) + 4 hl + r % 4 of the tile; the lane's key is `key`.
-// The mask is applied on every tile (a few VALU operations that issue under the MFMAs).
-template <int N, bool CAUSAL, bool BIAS>
+// With MASK the causal / length mask is applied (pipelined tiles always apply it: the
+// few VALU operations issue under the MFMAs).
+template <int N, bool MASK, bool CAUSAL, bool BIAS>
 __device__ __forceinline__ void softmax_part(f32x16& s, f32x16& dp, int r0, const float* lse,
                                              const float* dl, int hl, float c, int key,
                                              bool key_ok, int nq, int tile_pos0,
@@ -108,8 +109,11 @@ __device__ __forceinline__ void softmax_part(f32x16& s, f32x16& dp, int r0, cons
       x = fmaf(bias_h[(int64_t)min(tile_pos0 + qi, bias_len - 1) * bias_len + min(key, bias_len - 1)],
                kLog2e, x);
     x -= lse[qi];
-    const bool vis = key_ok && qi < nq && (!CAUSAL || key <= tile_pos0 + qi);
-    const float p = exp2f_fast(vis ? x : -INFINITY);
+    if (MASK) {
+      const bool vis = key_ok && qi < nq && (!CAUSAL || key <= tile_pos0 + qi);
+      x = vis ? x : -INFINITY;
+    }
+    const float p = exp2f_fast(x);
     s[r] = p;
     dp[r] = p * (dp[r] - dl[qi]);
   }
@@ -277,14 +281,17 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     const float* lse = lds_lse[buf];
     const float* dl = lds_dl[buf];
     auto sm_block = [&](int blk) {
-      softmax_part<EPB, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok, nq,
-                                      tile_pos0, bias_h, a.bias_len);
+      softmax_part<EPB, true, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
+                                            nq, tile_pos0, bias_h, a.bias_len);
     };
     if (PIPE && have_prev) {
       dvdk(pbuf, pp, pd, sm_block);
-    } else {
+    } else if (PIPE || (nk < 32) || (nq < kTq) || (CAUSAL && tile_pos0 < wkey0 + 31)) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) sm_block(blk);
+    } else {  // a tile every key of the wave sees: no mask
+      softmax_part<16, false, CAUSAL, BIAS>(s, dp, 0, lse, dl, hl, a.scale_log2, key, key_ok, nq,
+                                            tile_pos0, bias_h, a.bias_len);
     }
     // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
     pp[0] = to_bf16x8(s, 0);
