@@ -126,11 +126,13 @@ __device__ __forceinline__ void ds_tile(f32x16 (&s)[2], f32x16 (&dp)[2], float c
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kk = kbi + j;
-        float x = s[kb][i * 4 + j] * c;
-        if (BIAS) x = fmaf(bias_row[min(kk, bias_len - 1)], kLog2e, x);
-        bool vis = true;
-        if (MASK) vis = (kk < L) && (!CAUSAL || kk <= qpos);
-        const float p = vis ? exp2f_fast(x - lse2) : 0.f;
+        float x;
+        if (BIAS)
+          x = fmaf(bias_row[min(kk, bias_len - 1)], kLog2e, s[kb][i * 4 + j] * c) - lse2;
+        else
+          x = fmaf(s[kb][i * 4 + j], c, -lse2);
+        if (MASK) x = ((kk < L) && (!CAUSAL || kk <= qpos)) ? x : -INFINITY;
+        const float p = exp2f_fast(x);  // branch-free: a masked score is exp2(-inf) = 0
         dp[kb][i * 4 + j] = p * (dp[kb][i * 4 + j] - dlt);
       }
     }

@@ -104,11 +104,12 @@ __device__ __forceinline__ void softmax_part(f32x16& s, f32x16& dp, int r0, cons
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int r = r0 + k, qi = 8 * (r >> 2) + 4 * hl + (r & 3);
-    float x = s[r] * c;
+    float x;
     if (BIAS)
       x = fmaf(bias_h[(int64_t)min(tile_pos0 + qi, bias_len - 1) * bias_len + min(key, bias_len - 1)],
-               kLog2e, x);
-    x -= lse[qi];
+               kLog2e, s[r] * c) - lse[qi];
+    else
+      x = fmaf(s[r], c, -lse[qi]);
     if (MASK) {
       const bool vis = key_ok && qi < nq && (!CAUSAL || key <= tile_pos0 + qi);
       x = vis ? x : -INFINITY;
