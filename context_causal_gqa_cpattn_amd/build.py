@@ -38,6 +38,7 @@ def _hipcc() -> str:
 FILE_FLAGS = {
     "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
