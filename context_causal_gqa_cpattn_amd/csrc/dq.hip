@@ -31,6 +31,12 @@ constexpr int kRows = 16;    // query rows per wave
 constexpr int kWavesQ = 8;   // waves per workgroup
 constexpr int kThreadsQ = kWavesQ * 64;
 
+// K and V tiles are stored with the kind-1 granule swizzle (granule p of row r at
+// p ^ (2 (r mod 8) + (r / 8) mod 2)): sixteen consecutive rows read at one granule hit
+// sixteen bank groups (the S^T / dP^T operands), and so do eight consecutive rows read at
+// two adjacent granules (each transposing read below).
+constexpr int kSwz = 1;
+
 // Lane parts of the transposing reads that gather the K^T A operand (16 dimensions x
 // 32 keys) from the row-major, swizzled K tile.  In 16-lane group g, source lane
 // 4 j + m reads key row k0 + 4 g + j (k0 = 32 ks + 16 r for read r of key step ks) at
@@ -46,7 +52,7 @@ struct KtOffsets {
     const int row = 4 * g + j;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      off[b] = row * D + (((2 * b + (m >> 1)) ^ swz<D>(row)) << 3) + 4 * (m & 1);
+      off[b] = row * D + (((2 * b + (m >> 1)) ^ swz<D, kSwz>(row)) << 3) + 4 * (m & 1);
   }
 };
 
@@ -143,8 +149,8 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)kvh * D;
 
   if (n_tiles > 0) {
-    dma_rows<D, kKeys, kWavesQ>(lds_k[0], kbase, kv_stride, L, wave, lane);
-    dma_rows<D, kKeys, kWavesQ>(lds_v[0], vbase, kv_stride, L, wave, lane);
+    dma_rows<D, kKeys, kWavesQ, kSwz>(lds_k[0], kbase, kv_stride, L, wave, lane);
+    dma_rows<D, kKeys, kWavesQ, kSwz>(lds_v[0], vbase, kv_stride, L, wave, lane);
   }
   wait_vm_all();
   __syncthreads();
@@ -154,8 +160,8 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) {
       const int64_t nxt = (int64_t)(key0 + kKeys) * kv_stride;
-      dma_rows<D, kKeys, kWavesQ>(lds_k[buf ^ 1], kbase + nxt, kv_stride, L - key0 - kKeys, wave, lane);
-      dma_rows<D, kKeys, kWavesQ>(lds_v[buf ^ 1], vbase + nxt, kv_stride, L - key0 - kKeys, wave, lane);
+      dma_rows<D, kKeys, kWavesQ, kSwz>(lds_k[buf ^ 1], kbase + nxt, kv_stride, L - key0 - kKeys, wave, lane);
+      dma_rows<D, kKeys, kWavesQ, kSwz>(lds_v[buf ^ 1], vbase + nxt, kv_stride, L - key0 - kKeys, wave, lane);
     }
     if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
       const uint16_t* kt = lds_k[buf];
@@ -171,8 +177,8 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
       for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          s[kb] = mfma16(lds_row16<D>(kt, 16 * kb + q, 4 * st + g), qf[st], s[kb]);
-          dp[kb] = mfma16(lds_row16<D>(vt, 16 * kb + q, 4 * st + g), dof[st], dp[kb]);
+          s[kb] = mfma16(lds_row16<D, kSwz>(kt, 16 * kb + q, 4 * st + g), qf[st], s[kb]);
+          dp[kb] = mfma16(lds_row16<D, kSwz>(vt, 16 * kb + q, 4 * st + g), dof[st], dp[kb]);
         }
       const bool need_mask = (key0 + kKeys > L) || (CAUSAL && key0 + kKeys - 1 > wave_first_pos);
       if (need_mask)
