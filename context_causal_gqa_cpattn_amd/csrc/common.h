@@ -113,7 +113,15 @@ __device__ __forceinline__ int swz(int r) {
   if (KIND == 1) return (((r & 7) << 1) | ((r >> 3) & 1)) & (G - 1);
   // KIND 2: rows read sixteen at a time as {8a + 4b' + c : a, c in 0..3} for a fixed b'
   // (the dK/dV query order) land in sixteen distinct bank groups.
-  return ((r & 3) | (((r >> 3) & 3) << 2)) & (G - 1);
+  if (KIND == 2) return ((r & 3) | (((r >> 3) & 3) << 2)) & (G - 1);
+  // KIND 3: kind 1 with bit 2 of the row flipped by bit 3 before the shift.  A 16-byte
+  // read serves its 64 lanes in four passes of 16; in each 32-lane half, the lanes whose
+  // quad index (lane bits 2-4) has even parity form one pass.  When lane group g of 16
+  // lanes reads rows r0 + [0, 16) at one granule per group, a pass holds rows
+  // {0-3, 12-15} of one group and rows 4-11 of the next, and this swizzle maps the two
+  // sets to complementary bank groups.  Eight consecutive rows x two adjacent granules
+  // (a transposing read) stay conflict-free, as under kind 1.
+  return (((((r & 7) ^ ((r >> 1) & 4)) << 1) | ((r >> 3) & 1))) & (G - 1);
 }
 
 // A pointer that is the same in every lane, forced into scalar registers.
@@ -176,7 +184,7 @@ __device__ __forceinline__ void dma_rows(uint16_t* lds, const uint16_t* base, in
   constexpr int NI = R * G / 64;       // instructions per tile
   constexpr int NK = (NI + NW - 1) / NW;
   static_assert((2 * NW * RPI) % 16 == 0, "lane offsets repeat with period 2");
-  static_assert(KIND < 2, "swizzles of kinds 0 and 1 depend on the row mod 16 only");
+  static_assert(KIND != 2, "swizzles of kinds 0, 1 and 3 depend on the row mod 16 only");
   const char* b = uniform_ptr(base);
   const uint32_t rs_bytes = (uint32_t)(rs * 2);
   const uint32_t l0 = lds_addr(lds);

@@ -31,11 +31,11 @@ constexpr int kRows = 16;    // query rows per wave
 constexpr int kWavesQ = 8;   // waves per workgroup
 constexpr int kThreadsQ = kWavesQ * 64;
 
-// K and V tiles are stored with the kind-1 granule swizzle (granule p of row r at
-// p ^ (2 (r mod 8) + (r / 8) mod 2)): sixteen consecutive rows read at one granule hit
-// sixteen bank groups (the S^T / dP^T operands), and so do eight consecutive rows read at
-// two adjacent granules (each transposing read below).
-constexpr int kSwz = 1;
+// K and V tiles are stored with the kind-3 granule swizzle: the S^T / dP^T operand reads
+// (lane group g of 16 lanes reads sixteen consecutive rows at granule 4 st + g) and the
+// transposing reads below (eight consecutive rows x two adjacent granules per 32 lanes)
+// are both free of bank conflicts.
+constexpr int kSwz = 3;
 
 // Lane parts of the transposing reads that gather the K^T A operand (16 dimensions x
 // 32 keys) from the row-major, swizzled K tile.  In 16-lane group g, source lane
