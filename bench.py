@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--recompute-dq", action="store_true",
+                    help="dQ forms S, P and dP again instead of multiplying the stored dS")
     return ap.parse_args()
 
 
@@ -173,7 +175,10 @@ def main():
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     dbias = torch.empty_like(bias) if bias is not None else None
-    ws = torch.empty(max(cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
+    # With room for it (head_dim >= 64), dK/dV stores dS and dQ multiplies the stored dS.
+    ws_ds = 0 if args.recompute_dq else cp.workspace_size(prob, cp.OP_BWD_DS)
+    use_ds = ws_ds > 0
+    ws = torch.empty(max(ws_ds, cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
     err = cp.new_dev_err()
 
     names = ["fwd", "validate", "prepass", "dkdv", "dq"] + (["dbias"] if bias is not None else [])
@@ -189,9 +194,14 @@ def main():
         mark(2)
         cp.bwd_prepass(prob, lay, q, o, do, ws, err)
         mark(3)
-        cp.bwd_dkdv(prob, lay, q, k, v, bias, lse, do, ws, dk, dv, False, err)
-        mark(4)
-        cp.bwd_dq(prob, lay, q, k, v, bias, lse, do, ws, dq, err)
+        if use_ds:
+            cp.bwd_dkdv_ds(prob, lay, q, k, v, bias, lse, do, ws, dk, dv, False, err)
+            mark(4)
+            cp.bwd_dq_ds(prob, lay, k, ws, dq, err)
+        else:
+            cp.bwd_dkdv(prob, lay, q, k, v, bias, lse, do, ws, dk, dv, False, err)
+            mark(4)
+            cp.bwd_dq(prob, lay, q, k, v, bias, lse, do, ws, dq, err)
         mark(5)
         if bias is not None:
             cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, ws, dbias, err)
@@ -235,6 +245,16 @@ def main():
     pre_bytes = (3 * w.q_valid_rows().sum() * w.hq * D * 2 + 4 * w.q_valid_rows().sum() * w.hq
                  + 2 * n_tiles * w.hq * 32 * D * 2)
 
+    # stored dS: one 2 KB block per (32-query tile, head, 32-key block with a visible pair),
+    # written by dK/dV and read by dQ
+    ds_bytes = 0
+    for b, r0, pos0, n in w.chunks:
+        L = int(w.seq_lens[b])
+        for t in range(-(-int(n) // 32)):
+            last = int(pos0) + min(32 * (t + 1), int(n)) - 1
+            ds_bytes += -(-min(L, last + 1 if w.causal else L) // 32)
+    ds_bytes *= w.hq * 2048
+
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -257,6 +277,8 @@ def main():
         "bwd_tflops": round(bwd_tflops, 2),
         "kernel_ms": {n: round(x, 4) for n, x in per_kernel.items()},
         "prepass_gbs": round(pre_bytes / (per_kernel["prepass"] * 1e-3) / 1e9, 1),
+        "dq_path": "stored dS" if use_ds else "recompute",
+        "ds_bytes_per_step": ds_bytes if use_ds else 0,
         "layout_copy": copy,
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),

@@ -5,7 +5,7 @@ kernels behind include/cpattn.h.  PyTorch provides device memory and the current
 stream.  There is no fallback: if the library or a GPU is missing, calls raise.
 
 Names follow the C entry points: fwd, bwd, bwd_prepass, bwd_dkdv, bwd_dq,
-bwd_dbias, validate, pack, unpack.
+bwd_dbias, bwd_dkdv_ds, bwd_dq_ds, validate, pack, unpack.
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcpattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
-OP_FWD, OP_BWD = 0, 1
+OP_FWD, OP_BWD, OP_BWD_DS = 0, 1, 2
 DEV_ERR_BITS = {
     0x01: "ESEQ_LEN", 0x02: "ESEQ_RANGE", 0x04: "ECHUNK_SEQ", 0x08: "ECHUNK_ROWS",
     0x10: "ECHUNK_POS", 0x20: "EBIAS", 0x40: "ELAYOUT",
@@ -29,7 +29,8 @@ DEV_ERR_BITS = {
 EXPORTS = [
     "cpattn_status_str", "cpattn_last_error", "cpattn_version", "cpattn_workspace_size",
     "cpattn_validate", "cpattn_fwd", "cpattn_bwd", "cpattn_bwd_prepass", "cpattn_bwd_dkdv",
-    "cpattn_bwd_dq", "cpattn_bwd_dbias", "cpattn_pack", "cpattn_unpack",
+    "cpattn_bwd_dq", "cpattn_bwd_dbias", "cpattn_bwd_dkdv_ds", "cpattn_bwd_dq_ds", "cpattn_pack",
+    "cpattn_unpack",
 ]
 
 
@@ -88,6 +89,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                             ctypes.c_int, _vp, _vp],
         "cpattn_bwd_dq": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
         "cpattn_bwd_dbias": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
+        "cpattn_bwd_dkdv_ds": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp,
+                               ctypes.c_int, _vp, _vp],
+        "cpattn_bwd_dq_ds": [P, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
         "cpattn_pack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
         "cpattn_unpack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
     }
@@ -230,8 +234,12 @@ def fwd(q, k, v, layout: Layout, causal: bool = True, scale: Optional[float] = N
 
 def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optional[float] = None,
         bias=None, dq=None, dk=None, dv=None, dkv_accumulate: bool = False, want_dbias: bool = True,
-        dbias=None, ws=None, dev_err=None, stream=None):
-    """dQ, dK, dV (bf16) and dBias (fp32, when a bias is given)."""
+        dbias=None, ws=None, dev_err=None, stream=None, store_ds: Optional[bool] = None):
+    """dQ, dK, dV (bf16) and dBias (fp32, when a bias is given).
+
+    store_ds: size the workspace for the stored-dS backward (dK/dV stores dS, dQ
+    multiplies it); None = whenever the head dim allows it.  A given `ws` decides
+    by its size, as in the C entry point."""
     torch = _torch()
     lib = load()
     prob = _prob_for(q, k, v, layout, causal, scale, bias)
@@ -251,6 +259,10 @@ def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optiona
     if bias is not None and want_dbias and dbias is None:
         dbias = torch.empty_like(bias)
     need = workspace_size(prob, OP_BWD)
+    if store_ds is not False and ws is None:
+        need = max(need, workspace_size(prob, OP_BWD_DS))
+        if store_ds and need == workspace_size(prob, OP_BWD):
+            raise ValueError("the stored-dS backward needs head_dim >= 64")
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if dev_err is None:
@@ -284,6 +296,24 @@ def bwd_dq(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dq, dev_er
     _check(lib.cpattn_bwd_dq(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
                              _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
                              _ptr(do), _ptr(ws), ws.numel(), _ptr(dq), _ptr(dev_err), _stream(stream)))
+
+
+def bwd_dkdv_ds(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dk, dv,
+                dkv_accumulate: bool, dev_err, stream=None):
+    """bwd_dkdv that also stores dS in the workspace (OP_BWD_DS bytes)."""
+    lib = load()
+    _check(lib.cpattn_bwd_dkdv_ds(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                                  _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(lse),
+                                  _ptr(do), _ptr(ws), ws.numel(), _ptr(dk), _ptr(dv),
+                                  1 if dkv_accumulate else 0, _ptr(dev_err), _stream(stream)))
+
+
+def bwd_dq_ds(prob: Problem, layout: Layout, k, ws, dq, dev_err, stream=None):
+    """dQ from the dS that bwd_dkdv_ds stored in `ws`."""
+    lib = load()
+    _check(lib.cpattn_bwd_dq_ds(ctypes.byref(prob), _ptr(k), _ptr(layout.seq_offsets), _ptr(layout.seq_lens),
+                                _ptr(layout.chunks), _ptr(ws), ws.numel(), _ptr(dq), _ptr(dev_err),
+                                _stream(stream)))
 
 
 def bwd_dbias(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dbias, dev_err, stream=None):

@@ -83,10 +83,13 @@ struct Plan {
   int64_t delta_bytes;  // rounded to 256
   int parts;            // dBias partitions
   int64_t partial_bytes;
-  // backward workspace: delta | Q^T tiles | dO^T tiles | dBias partials
+  // backward workspace: delta | Q^T tiles | dO^T tiles | dBias partials | dS blocks
   int64_t off_qt, off_dot, off_partials, ws_core;
-  dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias;
-  int bpc_fwd, bpc_prepass, kv_tiles;
+  bool ds_ok;            // the stored-dS backward applies (head_dim >= 64)
+  int64_t kb_max;        // 32-key blocks per (tile slot, head) in the dS store
+  int64_t off_ds, ds_bytes;
+  dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias, grid_dqds;
+  int bpc_fwd, bpc_prepass, bpc_dqds, kv_tiles;
 };
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -159,6 +162,16 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.off_partials = pl.off_dot + round256(tile_bytes);
   pl.ws_core = pl.off_partials;
   pl.grid_prepass = dim3((unsigned)gx_pre, (unsigned)p->hq);
+  // Stored dS: 2 KB per (tile slot, head, 32-key block), every slot sized for the longest
+  // sequence.
+  pl.ds_ok = D >= 64;
+  pl.kb_max = cdiv(p->max_kv_len, kDsBlockKeys);
+  pl.off_ds = pl.ws_core + pl.partial_bytes;
+  pl.ds_bytes = pl.ds_ok ? round256(max_tiles * p->hq * pl.kb_max * kDsBlockKeys * kPrepassRows * 2) : 0;
+  pl.bpc_dqds = (int)cdiv(p->max_chunk_len, (int64_t)kDqDsRows * (4 / pl.hpw));
+  const int64_t gx_dqds = (int64_t)p->num_chunks * pl.bpc_dqds * (p->hq / pl.hpw);
+  if (gx_dqds > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
+  pl.grid_dqds = dim3((unsigned)gx_dqds);
   return CPATTN_OK;
 }
 
@@ -241,6 +254,7 @@ size_t cpattn_workspace_size(const cpattn_problem* p, int op) {
   if (make_plan(p, pl)) return 0;
   if (op == CPATTN_OP_FWD) return 0;
   if (op == CPATTN_OP_BWD) return (size_t)(pl.ws_core + pl.partial_bytes);
+  if (op == CPATTN_OP_BWD_DS) return pl.ds_ok ? (size_t)(pl.off_ds + pl.ds_bytes) : 0;
   return 0;
 }
 
@@ -355,11 +369,13 @@ int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, 
 }
 
 int enqueue_dkdv(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dk, void* dv, int acc,
-                 hipStream_t s) {
+                 hipStream_t s, void* ds_out = nullptr) {
   if (empty(pl.grid_dkdv)) return CPATTN_OK;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
   a.accumulate = acc ? 1 : 0;
+  a.ds_out = (uint16_t*)ds_out;
+  a.kb_max = pl.kb_max;
   return hip_check(launch_dkdv(a, pl.D, p->causal != 0, pl.bias, pl.grid_dkdv, s), "dK/dV launch");
 }
 
@@ -368,6 +384,16 @@ int enqueue_dq(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dq, hi
   a.dq = (uint16_t*)dq;
   a.blocks_per_chunk = pl.bpc_fwd;
   return hip_check(launch_dq(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd1d, s), "dQ launch");
+}
+
+int enqueue_dq_ds(const cpattn_problem* p, const Plan& pl, AttnArgs a, const void* ws, void* dq,
+                  hipStream_t s) {
+  if (empty(pl.grid_dqds)) return CPATTN_OK;
+  a.dq = (uint16_t*)dq;
+  a.ds = (const uint16_t*)((const char*)ws + pl.off_ds);
+  a.kb_max = pl.kb_max;
+  a.blocks_per_chunk = pl.bpc_dqds;
+  return hip_check(launch_dq_ds(a, pl.D, p->causal != 0, pl.grid_dqds, s), "dQ (stored dS) launch");
 }
 
 int enqueue_dbias(const cpattn_problem* p, const Plan& pl, AttnArgs a, float* dbias, void* ws,
@@ -401,7 +427,9 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
   if (dbias && !pl.bias) return fail(CPATTN_EINVAL, "dbias given but bias_len is 0");
   if (dbias && !aligned(dbias, 16)) return fail(CPATTN_EINVAL, "dbias is not 16-byte aligned");
   if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
-  const int64_t need = pl.ws_core + (dbias ? pl.partial_bytes : 0);
+  // With room for the dS store, dK/dV stores dS and dQ multiplies it (no recompute).
+  const bool use_ds = pl.ds_ok && (int64_t)ws_bytes >= pl.off_ds + pl.ds_bytes;
+  const int64_t need = use_ds ? pl.off_ds + pl.ds_bytes : pl.ws_core + (dbias ? pl.partial_bytes : 0);
   if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
   if ((r = check_ptr(ws, need, 256, "ws"))) return r;
   const int64_t dbias_bytes = dbias ? pl.bias_bytes : 0;
@@ -418,8 +446,13 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
   if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
   if ((r = enqueue_prepass(p, pl, q_chunk_map, q, o, dout, ws, dev_err, s))) return r;
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
-  if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
-  if ((r = enqueue_dq(p, pl, a, dq, s))) return r;
+  if (use_ds) {
+    if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s, (char*)ws + pl.off_ds))) return r;
+    if ((r = enqueue_dq_ds(p, pl, a, ws, dq, s))) return r;
+  } else {
+    if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
+    if ((r = enqueue_dq(p, pl, a, dq, s))) return r;
+  }
   if (dbias) return enqueue_dbias(p, pl, a, dbias, ws, s);
   return CPATTN_OK;
 }
@@ -506,6 +539,57 @@ int cpattn_bwd_dq(const cpattn_problem* p, const void* q, const void* k, const v
   if ((r = alias_audit(rs))) return r;
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   return enqueue_dq(p, pl, a, dq, (hipStream_t)stream);
+}
+
+int cpattn_bwd_dkdv_ds(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                       const int32_t* seq_offsets, const int32_t* seq_lens,
+                       const int32_t* q_chunk_map, const float* bias, const float* lse,
+                       const void* dout, void* ws, size_t ws_bytes, void* dk, void* dv,
+                       int dkv_accumulate, const int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  std::vector<Range> rs;
+  if ((r = make_plan(p, pl))) return r;
+  if (!pl.ds_ok) return fail(CPATTN_EUNSUPPORTED, "the stored-dS backward needs head_dim >= 64");
+  if ((r = step_checks(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws,
+                       ws_bytes, pl.off_ds + pl.ds_bytes, dev_err, rs)))
+    return r;
+  if ((r = check_ptr(dk, pl.kv_bytes, 16, "dk")) || (r = check_ptr(dv, pl.kv_bytes, 16, "dv"))) return r;
+  if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
+  rs.push_back(rng("dk", dk, pl.kv_bytes, true));
+  rs.push_back(rng("dv", dv, pl.kv_bytes, true));
+  rs.push_back(rng("ws (dS area)", (char*)ws + pl.off_ds, pl.ds_bytes, true));
+  if ((r = alias_audit(rs))) return r;
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
+  return enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, (hipStream_t)stream, (char*)ws + pl.off_ds);
+}
+
+int cpattn_bwd_dq_ds(const cpattn_problem* p, const void* k, const int32_t* seq_offsets,
+                     const int32_t* seq_lens, const int32_t* q_chunk_map, const void* ws,
+                     size_t ws_bytes, void* dq, const int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if (!pl.ds_ok) return fail(CPATTN_EUNSUPPORTED, "the stored-dS backward needs head_dim >= 64");
+  if ((r = check_ptr(k, pl.kv_bytes, 16, "k")) || (r = check_ptr(dq, pl.q_bytes, 16, "dq"))) return r;
+  if ((r = check_descriptors(p, seq_offsets, seq_lens, q_chunk_map, dev_err))) return r;
+  const int64_t need = pl.off_ds + pl.ds_bytes;
+  if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
+  if ((r = check_ptr(ws, need, 256, "ws"))) return r;
+  std::vector<Range> rs = {rng("k", k, pl.kv_bytes, false),
+                           rng("ws (dS area)", (const char*)ws + pl.off_ds, pl.ds_bytes, false),
+                           rng("dq", dq, pl.q_bytes, true)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  if ((r = alias_audit(rs))) return r;
+  AttnArgs a = base_args(p, pl);
+  a.k = (const uint16_t*)k;
+  a.seq_offsets = seq_offsets;
+  a.seq_lens = seq_lens;
+  a.chunks = q_chunk_map;
+  a.dev_err = dev_err;
+  return enqueue_dq_ds(p, pl, a, ws, dq, (hipStream_t)stream);
 }
 
 int cpattn_bwd_dbias(const cpattn_problem* p, const void* q, const void* k, const void* v,

@@ -91,6 +91,15 @@ __device__ __forceinline__ void wait_vm_all() {
   asm volatile("" ::: "memory");
 }
 
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still pending
+// (vmcnt is 6 bits: bits 3-0 and 15-14 of the immediate).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
 // Physical block id -> logical work item, so that consecutive logical items (which
 // share K/V) run on the same XCD (blocks are dealt to the 8 XCDs round robin) and
 // hit that XCD's L2.
@@ -340,6 +349,9 @@ struct AttnArgs {
   uint16_t* dot_out;     // pre-pass output: transposed dO tiles
   const uint16_t* qt;    // transposed Q tiles [slot][hq][D][32]
   const uint16_t* dot;   // transposed dO tiles
+  uint16_t* ds_out;      // dK/dV: where to store dS blocks (null: not stored)
+  const uint16_t* ds;    // dQ from stored dS: the dS blocks
+  int64_t kb_max;        // 32-key blocks per (query tile slot, head) in the dS store
   const int32_t* seq_offsets;
   const int32_t* seq_lens;
   const int32_t* chunks;

@@ -307,6 +307,18 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       lds_dl[nbuf][tid] = st_dl;
     }
     __syncthreads();
+    // Stored dS for the dQ product: block (tile slot, head, key block of this wave), key row
+    // n, granules 2 e + hl (pd[e]).  Only blocks with a visible pair are stored; they are
+    // the blocks that dQ reads.  Issued after the step's wait for its copies, so that the
+    // stores complete during the next step instead of extending this one.
+    if (a.ds_out != nullptr && wkey0 < L && (!CAUSAL || wkey0 <= tile_pos0 + nq - 1)) {
+      const int64_t blk =
+          ((int64_t)tile_slot(cur.c, cur.ch.q_row, cur.qt) * a.hq + g * a.group + cur.hh) * a.kb_max +
+          (wkey0 >> 5);
+      uint16_t* dst = a.ds_out + blk * 1024 + n * 32 + hl * 8;
+      st16(dst, pd[0]);
+      st16(dst + 16, pd[1]);
+    }
     cur = nxt;
     have = have_next;
     have_prev = true;

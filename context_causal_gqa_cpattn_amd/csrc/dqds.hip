@@ -1,0 +1,202 @@
+// dQ from stored dS: the backward's last product when the workspace holds dS.
+//
+// Page "Optimize context parallel attention layouts and gradient accumulation":
+// "Changes" (GQA, causal THD with physical offsets) and "Related optimization work"
+// (the backward is where the providers differ).
+//
+// dK/dV already forms dS = P (dP - Delta) for every (32-key block, 32-query tile, query
+// head) that has a visible pair, and in this mode stores it in BF16, the precision in
+// which both dK and dQ multiply it.  dQ = scale dS K is then a product over the visible
+// key blocks alone: S, P and dP are not formed a second time.
+//
+// dS block (2 KB, written by dK/dV): 32 key rows of 64 bytes; granule v = 2 e + hl of key
+// row n holds queries 16 e + 8 (i / 4) + 4 hl + i % 4, i = 0..7 (the order in which a
+// 32x32 accumulator lane holds its rows).  Block kb of (query tile slot, head h) is at
+// ((slot hq + h) kb_max + kb) 2 KB of the dS area.
+//
+// Workgroup = (chunk, block of positions, hpw query heads that share one KV head), four
+// waves, one per SIMD.  A wave owns two 32-query tiles of one head and keeps dQ^T
+// (D x 64 queries, fp32) in accumulation registers.  Each 32-key step, the K tile
+// (32 x D, kind-0 swizzle) and every wave's two dS blocks are copied into LDS three
+// steps ahead (four stages: the dS stream comes from HBM).  With 32x32x16 MFMAs:
+//   dQ^T += K^T dS^T    A = K^T by transposing reads of the K tile (as V^T in the forward),
+//                       B = dS^T by transposing reads of the dS block.
+#include "common.h"
+#include "launch.h"
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kWavesS = 4;
+constexpr int kThreadsS = kWavesS * 64;
+constexpr int kStages = 4;
+constexpr int kBlk = 32;              // keys per dS block and per step
+constexpr int kBlkElems = 32 * 32;    // BF16 elements of a dS block
+
+// Lane part of the transposing reads that give the B operand dS^T of k-step st (16 keys
+// x 32 queries): lane l holds query l % 32 and keys 16 st + 8 (e / 4) + 4 (l / 32) + e % 4
+// for e = 0..7, the contracted order of the K^T operand.  In 16-lane group G of a read,
+// source lane 4 j + u gives the four queries of unit 4 (G % 2) + u at key row 4 (G / 2) + j
+// (+ 8 for the second read); unit U (queries 4 U .. 4 U + 3) is half (U / 2) % 2 of
+// granule 2 (U / 4) + U % 2.  The 32 lanes of one pass touch four key rows x four
+// granules, sixteen distinct bank groups.
+__device__ __forceinline__ int ds_tr_off(int lane) {
+  const int i = lane & 15, G = lane >> 4;
+  const int j = i >> 2, u = i & 3;
+  return (4 * (G >> 1) + j) * 32 + (2 * (G & 1) + (u & 1)) * 8 + (u >> 1) * 4;
+}
+
+__device__ __forceinline__ u32x4 ds_frag(const uint16_t* blk, int off, int st) {
+  const uint16_t* b = blk + st * 16 * 32 + off;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + 8 * 32));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+}  // namespace
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreadsS) void dq_ds_kernel(const AttnArgs a) {
+  constexpr int NDB = D / 32;
+  constexpr int KI = kBlk * D * 2 / 1024 / kWavesS;  // K-tile copy instructions per wave
+  constexpr int PER = KI + 4;                          // copy instructions per wave per step
+  static_assert(KI >= 1 && (kBlk * D * 2 / 1024) % kWavesS == 0, "K tile split evenly over the waves");
+  static_assert(2 * PER < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[kStages][kBlk * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s[kStages][kWavesS * 2 * kBlkElems];
+
+  if (*a.dev_err) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_hg = a.hq / a.hpw;
+  const int pb = logical % a.blocks_per_chunk;
+  const int rest = logical / a.blocks_per_chunk;
+  const int hg = rest % n_hg;
+  const int c = rest / n_hg;
+  const Chunk ch = load_chunk(a.chunks, c);
+  const int wg_pos = 64 * (kWavesS / a.hpw);  // positions per workgroup
+  const int wg_row0 = pb * wg_pos;
+  if (wg_row0 >= ch.len) return;  // uniform over the workgroup, before any barrier
+  const int h = hg * a.hpw + (wave % a.hpw);
+  const int kvh = h / a.group;
+  const int row0 = wg_row0 + (wave / a.hpw) * 64;  // first chunk row of this wave (a tile start)
+  const int L = a.seq_lens[ch.seq];
+  const int64_t koff = a.seq_offsets[ch.seq];
+  const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + wg_pos) - 1;
+  const int n_steps = (min(L, CAUSAL ? wg_last_pos + 1 : L) + kBlk - 1) / kBlk;
+
+  // The wave's two tiles: rows, key blocks with a visible pair, first dS block.
+  int nq[2], nkb[2];
+  const uint16_t* dsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = row0 + 32 * i;
+    nq[i] = max(0, min(32, ch.len - r));
+    const int last = ch.pos0 + r + nq[i] - 1;
+    nkb[i] = nq[i] > 0 ? (min(L, CAUSAL ? last + 1 : L) + kBlk - 1) / kBlk : 0;
+    dsrc[i] = a.ds;
+    if (nq[i] > 0)
+      dsrc[i] = a.ds + ((int64_t)tile_slot(c, ch.q_row, r / 32) * a.hq + h) * a.kb_max * kBlkElems;
+  }
+
+  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)kvh * D;
+  // Step kb into stage kb % kStages: the K tile (rows past L repeat the last key) and the
+  // wave's two dS blocks.  A block the tile does not use is still copied (from the
+  // start of the dS area, in bounds) so that every wave issues PER copies per step.
+  auto issue = [&](int kb) {
+    const int sb = kb % kStages;
+    dma_rows<D, kBlk, kWavesS, 0>(lds_k[sb], kbase + (int64_t)kb * kBlk * kv_stride, kv_stride,
+                                  L - kb * kBlk, wave, lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint16_t* src = kb < nkb[i] ? dsrc[i] + (int64_t)kb * kBlkElems : a.ds;
+      dma_flat<2, 1>(lds_s[sb] + (wave * 2 + i) * kBlkElems, src, 0, lane);
+    }
+  };
+
+  f32x16 acc[2][NDB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[i][db] = f32x16{};
+  const TrOffsets<D> tro(lane);
+  const int dso = ds_tr_off(lane);
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < n_steps) issue(s);
+
+  for (int kb = 0; kb < n_steps; ++kb) {
+    // steps issued after kb: min(kStages - 2, n_steps - 1 - kb)
+    const int ahead = n_steps - 1 - kb;
+    if (ahead >= 2) wait_vm<2 * PER>();
+    else if (ahead == 1) wait_vm<PER>();
+    else wait_vm<0>();
+    __syncthreads();  // stage kb is in LDS for every wave; stage kb - 1 is free
+    if (kb + kStages - 1 < n_steps) issue(kb + kStages - 1);
+
+    // A tile without a visible pair in this block multiplies zeros (its dS block was not
+    // written); no branch around the products, which would move the accumulators.
+    const bool act0 = kb < nkb[0], act1 = kb < nkb[1];
+    const int sb = kb % kStages;
+    const uint16_t* kt = lds_k[sb];
+    const uint16_t* s0 = lds_s[sb] + (wave * 2) * kBlkElems;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u32x4 b0 = ds_frag(s0, dso, st), b1 = ds_frag(s0 + kBlkElems, dso, st);
+      if (!act0) b0 = u32x4{0u, 0u, 0u, 0u};
+      if (!act1) b1 = u32x4{0u, 0u, 0u, 0u};
+      u32x4 ka = tr_frag_at<D>(kt, tro, st, 0);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        u32x4 nk = ka;
+        if (db + 1 < NDB) nk = tr_frag_at<D>(kt, tro, st, db + 1);
+        acc[0][db] = mfma32(ka, b0, acc[0][db]);
+        acc[1][db] = mfma32(ka, b1, acc[1][db]);
+        ka = nk;
+      }
+    }
+  }
+
+  // element r of block db is dimension 32 db + 8 (r / 4) + 4 (lane / 32) + r % 4 of query lane % 32
+  const int col = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bool ok = col < nq[i];
+    const int64_t qrow = (int64_t)ch.q_row + row0 + 32 * i + (ok ? col : 0);
+    uint16_t* op = a.dq + (qrow * a.hq + h) * D + (lane >> 5) * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const u32x2 w{pack_bf16x2(acc[i][db][4 * i4] * a.scale, acc[i][db][4 * i4 + 1] * a.scale),
+                      pack_bf16x2(acc[i][db][4 * i4 + 2] * a.scale, acc[i][db][4 * i4 + 3] * a.scale)};
+        if (ok) st8(op + db * 32 + i4 * 8, w);
+        __builtin_amdgcn_sched_barrier(0);  // one block's registers at a time
+      }
+  }
+}
+
+hipError_t launch_dq_ds(const AttnArgs& a, int D, bool causal, dim3 grid, hipStream_t s) {
+  if (causal) {
+    switch (D) {
+      case 64: hipLaunchKernelGGL((dq_ds_kernel<64, true>), grid, dim3(kThreadsS), 0, s, a); break;
+      case 128: hipLaunchKernelGGL((dq_ds_kernel<128, true>), grid, dim3(kThreadsS), 0, s, a); break;
+      case 256: hipLaunchKernelGGL((dq_ds_kernel<256, true>), grid, dim3(kThreadsS), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (D) {
+      case 64: hipLaunchKernelGGL((dq_ds_kernel<64, false>), grid, dim3(kThreadsS), 0, s, a); break;
+      case 128: hipLaunchKernelGGL((dq_ds_kernel<128, false>), grid, dim3(kThreadsS), 0, s, a); break;
+      case 256: hipLaunchKernelGGL((dq_ds_kernel<256, false>), grid, dim3(kThreadsS), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -34,12 +34,17 @@ hipError_t launch_fwd(const AttnArgs& a, int D, bool causal, bool bias, dim3 gri
 hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
+hipError_t launch_dq_ds(const AttnArgs& a, int D, bool causal, dim3 grid, hipStream_t s);
 hipError_t launch_dbias(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
 hipError_t launch_dbias_reduce(const float* partial, float* out, int64_t n, int parts,
                                const int32_t* dev_err, hipStream_t s);
 
 // Rows of a chunk handled by one pre-pass workgroup (one query tile).
 constexpr int kPrepassRows = 32;
+// Keys per stored dS block (one dK/dV wave) and query rows per dQ-from-dS workgroup
+// wave (two 32-query tiles).
+constexpr int kDsBlockKeys = 32;
+constexpr int kDqDsRows = 64;
 // Keys per dK/dV workgroup (four waves of 32 keys).
 constexpr int kDkdvKeys = 128;
 // dBias tile: 128 query positions x 64 keys per workgroup.

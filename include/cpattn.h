@@ -101,6 +101,7 @@ typedef struct cpattn_problem {
 
 #define CPATTN_OP_FWD 0
 #define CPATTN_OP_BWD 1
+#define CPATTN_OP_BWD_DS 2
 
 /* Text of a status code. */
 const char* cpattn_status_str(int status);
@@ -117,8 +118,15 @@ int cpattn_version(void);
  * 0); Q^T and dO^T as BF16 tiles [slot][hq][head_dim][32 queries, in an internal
  * order] with ceil(q_rows/32) + num_chunks slots (tile t of chunk c is slot
  * floor(q_row_c / 32) + c + t; queries past the chunk end are zero); and, with a
- * bias, the per-partition dBias partial sums.  Returns 0 for an invalid
- * problem (check it with the entry point for the reason). */
+ * bias, the per-partition dBias partial sums.
+ * op = CPATTN_OP_BWD_DS: the backward workspace followed by the dS store, BF16
+ * blocks of 32 keys x 32 queries (2 KB, internal order), one per (tile slot, query
+ * head, 32-key block < ceil(max_kv_len / 32)): with it dK/dV stores dS and dQ is a
+ * product with the stored dS instead of a second pass that forms S, P and dP
+ * again.  It is 2 bytes per (query row slot, head, key position up to max_kv_len):
+ * e.g. 36.5 GB for 128 chunks of 512 rows, 32 heads and max_kv_len 8192.  Head
+ * dims 64, 128 and 256 only (0 for head_dim 32).
+ * Returns 0 for an invalid problem (check it with the entry point for the reason). */
 size_t cpattn_workspace_size(const cpattn_problem* p, int op);
 
 /* The device promise check alone ("Changes": promised sequence lengths and
@@ -147,7 +155,11 @@ int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void
  *  read, this call's contribution is added in fp32 and the sum is rounded once.
  *  dbias (fp32, with a bias only, may be NULL to skip it) is STORED: the sum of
  *  dS over every chunk row, unscaled.  O and LSE are the forward's outputs.
- *  ws must hold cpattn_workspace_size(p, CPATTN_OP_BWD) bytes. */
+ *  ws must hold cpattn_workspace_size(p, CPATTN_OP_BWD) bytes.  When it holds
+ *  cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes (nonzero), dK/dV stores dS in
+ *  it and dQ multiplies the stored dS (cpattn_bwd_dkdv_ds, cpattn_bwd_dq_ds);
+ *  otherwise dQ forms S, P and dP again (cpattn_bwd_dkdv, cpattn_bwd_dq).  Both
+ *  give dQ = scale dS K with dS rounded to BF16 before the product. */
 int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
                const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
                const float* bias, const void* o, const float* lse, const void* dout,
@@ -166,7 +178,13 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
  *  cpattn_bwd_dkdv: dK/dV as in cpattn_bwd from the pre-pass results.
  *  cpattn_bwd_dq: dQ as in cpattn_bwd from the pre-pass results.
  *  cpattn_bwd_dbias: dBias as in cpattn_bwd from the pre-pass results; ws must
- *      also hold the partial sums. */
+ *      also hold the partial sums.
+ *  cpattn_bwd_dkdv_ds: cpattn_bwd_dkdv that also stores dS (BF16) in the dS store
+ *      of ws (cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes): every block with a
+ *      visible (key, query) pair, the others are left as they are.
+ *  cpattn_bwd_dq_ds: dQ = scale dS K from the dS store that cpattn_bwd_dkdv_ds
+ *      filled for the same problem and chunks (reads K and the dS store only).
+ *  Both return CPATTN_EUNSUPPORTED for head_dim 32. */
 int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
                        const void* o, const void* dout, void* ws, size_t ws_bytes,
                        const int32_t* dev_err, cpattn_stream_t stream);
@@ -185,6 +203,14 @@ int cpattn_bwd_dbias(const cpattn_problem* p, const void* q, const void* k, cons
                      const int32_t* q_chunk_map, const float* bias, const float* lse,
                      const void* dout, void* ws, size_t ws_bytes, float* dbias,
                      const int32_t* dev_err, cpattn_stream_t stream);
+int cpattn_bwd_dkdv_ds(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                       const int32_t* seq_offsets, const int32_t* seq_lens,
+                       const int32_t* q_chunk_map, const float* bias, const float* lse,
+                       const void* dout, void* ws, size_t ws_bytes, void* dk, void* dv,
+                       int dkv_accumulate, const int32_t* dev_err, cpattn_stream_t stream);
+int cpattn_bwd_dq_ds(const cpattn_problem* p, const void* k, const int32_t* seq_offsets,
+                     const int32_t* seq_lens, const int32_t* q_chunk_map, const void* ws,
+                     size_t ws_bytes, void* dq, const int32_t* dev_err, cpattn_stream_t stream);
 
 /* Layout copies ("Changes": vectorised BF16 pack/unpack copies that keep
  * physical sequence origins).  BHSD is [B, H, S_pitch, D]; THD is

@@ -156,3 +156,58 @@ def test_layout_copy_host_checks():
                            A + (3 << 24), None) == cp.EINVAL  # dst overlaps src
     assert lib.cpattn_unpack(None, A, 2, 4, 64, 128, 128, A + (2 << 24), A + (2 << 24) + 256,
                              A + (3 << 24), None) == cp.EINVAL
+
+
+def _ds_bytes(hq, q_rows, num_chunks, max_kv_len):
+    """dS store bytes from the layout the header states: 2 KB per (tile slot, head, 32-key block)."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    tiles = -(-q_rows // 32) + num_chunks
+    return r256(tiles * hq * (-(-max_kv_len // 32)) * 2048)
+
+
+def test_stored_ds_workspace_size():
+    lib = cp.load()
+    p = _prob()
+    assert lib.cpattn_workspace_size(ctypes.byref(p), cp.OP_BWD_DS) == \
+        _ws_layout(8, 64, 2, 128) + _ds_bytes(8, 64, 2, 64)
+    p3 = _prob(num_seqs=64, hq=32, hkv=8, head_dim=256, q_rows=64 * 1024, kv_rows=64 * 8192,
+               num_chunks=128, max_chunk_len=512, max_kv_len=8192)
+    ds3 = _ds_bytes(32, 64 * 1024, 128, 8192)
+    assert ds3 == 36_507_222_016  # the figure the header quotes
+    assert lib.cpattn_workspace_size(ctypes.byref(p3), cp.OP_BWD_DS) == \
+        _ws_layout(32, 64 * 1024, 128, 256) + ds3
+    # after the dBias partial sums when there is a bias
+    pb = _prob(head_dim=64, bias_len=256, causal=0, hq=4, hkv=4, num_chunks=64, q_rows=1 << 14,
+               kv_rows=1 << 14, max_chunk_len=256, max_kv_len=256)
+    assert lib.cpattn_workspace_size(ctypes.byref(pb), cp.OP_BWD_DS) == \
+        lib.cpattn_workspace_size(ctypes.byref(pb), cp.OP_BWD) + _ds_bytes(4, 1 << 14, 64, 256)
+    # not for head_dim 32, nor for an invalid problem
+    assert lib.cpattn_workspace_size(ctypes.byref(_prob(head_dim=32)), cp.OP_BWD_DS) == 0
+    assert lib.cpattn_workspace_size(ctypes.byref(_prob(hq=3)), cp.OP_BWD_DS) == 0
+
+
+def test_stored_ds_steps_check_workspace_and_aliases():
+    lib = cp.load()
+    p = _prob()
+    core = _ws_layout(8, 64, 2, 128)
+    full = lib.cpattn_workspace_size(ctypes.byref(p), cp.OP_BWD_DS)
+    q, k, v = A, A + (1 << 24), A + (2 << 24)
+    so, sl, cm = A + (3 << 24), A + (3 << 24) + 256, A + (3 << 24) + 512
+    lse, do, err, ws = A + (5 << 24), A + (8 << 24), A + (6 << 24), A + (12 << 24)
+    dk, dv, dq = A + (9 << 24), A + (10 << 24), A + (11 << 24)
+    args = [ctypes.byref(p), q, k, v, so, sl, cm, None, lse, do]
+    assert lib.cpattn_bwd_dkdv_ds(*args, ws, full - 1, dk, dv, 0, err, None) == cp.EINVAL
+    assert "workspace" in _err()
+    assert lib.cpattn_bwd_dkdv_ds(*args, ws, full, ws + core + 4096, dv, 0, err, None) == cp.EINVAL
+    assert "alias" in _err()  # dK inside the dS store
+    assert lib.cpattn_bwd_dkdv_ds(*args, ws, full, dk, dv, 2, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_dq_ds(ctypes.byref(p), k, so, sl, cm, ws, full - 1, dq, err, None) == cp.EINVAL
+    assert "workspace" in _err()
+    assert lib.cpattn_bwd_dq_ds(ctypes.byref(p), k, so, sl, cm, ws, full, ws + core + 512, err,
+                                None) == cp.EINVAL
+    assert "alias" in _err()  # dQ over the dS it reads
+    assert lib.cpattn_bwd_dq_ds(ctypes.byref(p), k, so, sl, cm, ws + 16, full, dq, err, None) == cp.EINVAL
+    p32 = _prob(head_dim=32)
+    args32 = [ctypes.byref(p32)] + args[1:]
+    assert lib.cpattn_bwd_dkdv_ds(*args32, ws, 1 << 30, dk, dv, 0, err, None) == cp.EUNSUPPORTED
+    assert lib.cpattn_bwd_dq_ds(ctypes.byref(p32), k, so, sl, cm, ws, 1 << 30, dq, err, None) == cp.EUNSUPPORTED

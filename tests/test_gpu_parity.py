@@ -14,11 +14,12 @@ from harness import (GpuRun, assert_close, compare, gather_rows_f64, host_f64, k
 pytestmark = pytest.mark.gpu
 
 
-def _run_and_compare(gpu_lib, w, seqs=None, kv_heads=None, label="", bar="configs"):
-    print(f"[case] {label or w.name} hq={w.hq} hkv={w.hkv} D={w.head_dim} C={w.num_chunks}", flush=True)
+def _run_and_compare(gpu_lib, w, seqs=None, kv_heads=None, label="", bar="configs", store_ds=None):
+    print(f"[case] {label or w.name} hq={w.hq} hkv={w.hkv} D={w.head_dim} C={w.num_chunks} "
+          f"store_ds={store_ds}", flush=True)
     run = GpuRun(gpu_lib, w)
     run.forward()
-    run.backward()
+    run.backward(store_ds=store_ds)
     info, ref, _ = compare(gpu_lib, run, seqs=seqs, kv_heads=kv_heads, label=label, bar=bar)
     if w.bias is not None and run.dbias is not None and seqs is None:
         info["dbias"] = assert_close(label + "dBias", run.dbias.cpu().numpy(), ref["dbias"], bar=bar)
@@ -27,8 +28,13 @@ def _run_and_compare(gpu_lib, w, seqs=None, kv_heads=None, label="", bar="config
 
 # ---------------------------------------------------------------- small, full comparison
 
-def test_config1_full(gpu_lib):
-    _run_and_compare(gpu_lib, W.make_config(1), label="cfg1 ")
+# Both dQ paths: multiplying the dS that dK/dV stored, and forming S, P and dP again.
+PATHS = {"stored_ds": None, "recompute": False}
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_config1_full(gpu_lib, path):
+    _run_and_compare(gpu_lib, W.make_config(1), label=f"cfg1 {path} ", store_ds=PATHS[path])
 
 
 SWEEP = [
@@ -60,12 +66,13 @@ def _chunks(lens, spec):
     return out
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("idx", range(len(SWEEP)))
-def test_small_sweep_full(gpu_lib, idx):
+def test_small_sweep_full(gpu_lib, idx, path):
     lens, hq, hkv, D, causal, spec = SWEEP[idx]
     w = W.make_custom(lens=lens, hq=hq, hkv=hkv, head_dim=D, causal=causal, chunks=_chunks(lens, spec),
                       seed=100 + idx, pad_kv_rows=5, pad_q_rows=3)
-    _run_and_compare(gpu_lib, w, label=f"sweep{idx} ", bar="pages")
+    _run_and_compare(gpu_lib, w, label=f"sweep{idx} {path} ", bar="pages", store_ds=PATHS[path])
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
@@ -84,9 +91,11 @@ def test_bias_unequal_lengths_and_partial_chunks(gpu_lib):
 
 # ---------------------------------------------------------------- named workloads, sampled
 
-def test_config2_sampled(gpu_lib):
+@pytest.mark.parametrize("path", PATHS)
+def test_config2_sampled(gpu_lib, path):
     w = W.make_config(2)
-    _run_and_compare(gpu_lib, w, seqs={0, 7}, kv_heads={0, 3, 7}, label="cfg2 ")
+    _run_and_compare(gpu_lib, w, seqs={0, 7}, kv_heads={0, 3, 7}, label=f"cfg2 {path} ",
+                     store_ds=PATHS[path])
 
 
 def test_config4_sampled_with_poisoned_padding(gpu_lib):
@@ -201,6 +210,40 @@ def test_sequence_without_chunks_gets_zero_dkdv(gpu_lib):
 def test_empty_chunk_and_zero_length_sequence(gpu_lib):
     w = _small_case(lens=[0, 90], chunks=[(1, 0, 0), (1, 10, 40)])
     _run_and_compare(gpu_lib, w, label="empty ")
+
+
+def test_stored_ds_steps_match_fused_entry_over_stale_workspace(gpu_lib):
+    """The step entry points (pre-pass, dK/dV storing dS, dQ from dS) give the fused
+    entry point's results bit for bit, with the workspace prefilled with NaN bytes:
+    no dS block that dK/dV did not write is read."""
+    import torch
+    w = _small_case(seed=21, lens=[300, 77], chunks=[(0, 0, 40), (0, 230, 70), (1, 5, 33)])
+    run = GpuRun(gpu_lib, w)
+    run.forward()
+    prob = gpu_lib.problem(run.layout, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal,
+                           w.scale, 0)
+    need = gpu_lib.workspace_size(prob, gpu_lib.OP_BWD_DS)
+    assert need > gpu_lib.workspace_size(prob, gpu_lib.OP_BWD)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    dq_f, dk_f, dv_f, _, err = gpu_lib.bwd(run.q, run.k, run.v, run.layout, run.o, run.lse, run.do,
+                                           causal=True, scale=w.scale, ws=ws)
+    gpu_lib.check(err)
+    ws.fill_(0xFF)
+    err = gpu_lib.new_dev_err()
+    dq, dk, dv = torch.empty_like(run.q), torch.empty_like(run.k), torch.empty_like(run.v)
+    gpu_lib.validate(prob, run.layout, err)
+    gpu_lib.bwd_prepass(prob, run.layout, run.q, run.o, run.do, ws, err)
+    gpu_lib.bwd_dkdv_ds(prob, run.layout, run.q, run.k, run.v, None, run.lse, run.do, ws, dk, dv,
+                        False, err)
+    gpu_lib.bwd_dq_ds(prob, run.layout, run.k, ws, dq, err)
+    torch.cuda.synchronize()
+    gpu_lib.check(err)
+    qi = torch.from_numpy(np.flatnonzero(rows_of(w))).cuda()
+    ki = torch.from_numpy(np.flatnonzero(kv_rows_of(w))).cuda()
+    for x, y in ((dq_f[qi], dq[qi]), (dk_f[ki], dk[ki]), (dv_f[ki], dv[ki])):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    run.dq, run.dk, run.dv = dq, dk, dv
+    compare(gpu_lib, run)
 
 
 def test_run_to_run_bitwise_identical(gpu_lib):
