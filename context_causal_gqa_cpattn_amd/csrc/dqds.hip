@@ -14,11 +14,15 @@
 // 32x32 accumulator lane holds its rows).  Block kb of (query tile slot, head h) is at
 // ((slot hq + h) kb_max + kb) 2 KB of the dS area.
 //
-// Workgroup = (chunk, block of positions, hpw query heads that share one KV head), four
-// waves, one per SIMD.  A wave owns two 32-query tiles of one head and keeps dQ^T
-// (D x 64 queries, fp32) in accumulation registers.  Each 32-key step, the K tile
-// (32 x D, kind-0 swizzle) and every wave's two dS blocks are copied into LDS three
-// steps ahead (four stages: the dS stream comes from HBM).  With 32x32x16 MFMAs:
+// Workgroup = (chunk, block of positions, hpw query heads that share one KV head) with
+// four slots of (head, two 32-query tiles).  For D >= 128 two waves share a slot, each
+// keeping half of dQ^T (D/2 x 64 queries, fp32) in registers, two waves per SIMD (one
+// wave's copies and LDS reads issue while the other's MFMAs run); for D = 64 one wave
+// per slot.  Each 32-key step, the K tile (32 x D, kind-0 swizzle) and the slots' dS
+// blocks are copied into LDS three steps ahead (four stages: the dS stream comes from
+// HBM); the copy instructions are spread between the step's MFMAs rather than issued
+// together after the barrier, where all waves would queue on the address unit at once.
+// With 32x32x16 MFMAs:
 //   dQ^T += K^T dS^T    A = K^T by transposing reads of the K tile (as V^T in the forward),
 //                       B = dS^T by transposing reads of the dS block.
 #include "common.h"
@@ -28,11 +32,19 @@ namespace cpattn {
 
 namespace {
 
-constexpr int kWavesS = 4;
-constexpr int kThreadsS = kWavesS * 64;
 constexpr int kStages = 4;
 constexpr int kBlk = 32;              // keys per dS block and per step
 constexpr int kBlkElems = 32 * 32;    // BF16 elements of a dS block
+constexpr int kSlots = 4;             // (head, two-tile) slots per workgroup
+
+// Waves per workgroup: each slot's D columns are split over kSplit waves, two waves per
+// SIMD for D >= 128 (128 accumulation registers each), one for D = 64.
+template <int D>
+struct DsCfg {
+  static constexpr int kSplit = D >= 128 ? 2 : 1;
+  static constexpr int kWaves = kSlots * kSplit;
+  static constexpr int kThreads = kWaves * 64;
+};
 
 // Lane part of the transposing reads that give the B operand dS^T of k-step st (16 keys
 // x 32 queries): lane l holds query l % 32 and keys 16 st + 8 (e / 4) + 4 (l / 32) + e % 4
@@ -58,17 +70,20 @@ __device__ __forceinline__ u32x4 ds_frag(const uint16_t* blk, int off, int st) {
 }  // namespace
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreadsS) void dq_ds_kernel(const AttnArgs a) {
-  constexpr int NDB = D / 32;
-  constexpr int KI = kBlk * D * 2 / 1024 / kWavesS;  // K-tile copy instructions per wave
-  constexpr int PER = KI + 4;                          // copy instructions per wave per step
-  static_assert(KI >= 1 && (kBlk * D * 2 / 1024) % kWavesS == 0, "K tile split evenly over the waves");
+__global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArgs a) {
+  constexpr int kSplit = DsCfg<D>::kSplit;
+  constexpr int kWaves = DsCfg<D>::kWaves;
+  constexpr int NDB = D / 32 / kSplit;                 // 32-row blocks of dQ^T per wave
+  constexpr int KI = kBlk * D * 2 / 1024 / kWaves;     // K-tile copy instructions per wave
+  constexpr int PER = KI + 4 / kSplit;                 // copy instructions per wave per step
+  static_assert(KI >= 1 && (kBlk * D * 2 / 1024) % kWaves == 0, "K tile split evenly over the waves");
   static_assert(2 * PER < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k[kStages][kBlk * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s[kStages][kWavesS * 2 * kBlkElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s[kStages][kSlots * 2 * kBlkElems];
 
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = wave / kSplit, part = wave % kSplit;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int n_hg = a.hq / a.hpw;
   const int pb = logical % a.blocks_per_chunk;
@@ -76,18 +91,18 @@ __global__ __launch_bounds__(kThreadsS) void dq_ds_kernel(const AttnArgs a) {
   const int hg = rest % n_hg;
   const int c = rest / n_hg;
   const Chunk ch = load_chunk(a.chunks, c);
-  const int wg_pos = 64 * (kWavesS / a.hpw);  // positions per workgroup
+  const int wg_pos = 64 * (kSlots / a.hpw);  // positions per workgroup
   const int wg_row0 = pb * wg_pos;
   if (wg_row0 >= ch.len) return;  // uniform over the workgroup, before any barrier
-  const int h = hg * a.hpw + (wave % a.hpw);
+  const int h = hg * a.hpw + (slot % a.hpw);
   const int kvh = h / a.group;
-  const int row0 = wg_row0 + (wave / a.hpw) * 64;  // first chunk row of this wave (a tile start)
+  const int row0 = wg_row0 + (slot / a.hpw) * 64;  // first chunk row of this slot (a tile start)
   const int L = a.seq_lens[ch.seq];
   const int64_t koff = a.seq_offsets[ch.seq];
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + wg_pos) - 1;
   const int n_steps = (min(L, CAUSAL ? wg_last_pos + 1 : L) + kBlk - 1) / kBlk;
 
-  // The wave's two tiles: rows, key blocks with a visible pair, first dS block.
+  // The slot's two tiles: rows, key blocks with a visible pair, first dS block.
   int nq[2], nkb[2];
   const uint16_t* dsrc[2];
 #pragma unroll
@@ -103,78 +118,120 @@ __global__ __launch_bounds__(kThreadsS) void dq_ds_kernel(const AttnArgs a) {
 
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)kvh * D;
-  // Step kb into stage kb % kStages: the K tile (rows past L repeat the last key) and the
-  // wave's two dS blocks.  A block the tile does not use is still copied (from the
-  // start of the dS area, in bounds) so that every wave issues PER copies per step.
-  auto issue = [&](int kb) {
-    const int sb = kb % kStages;
-    dma_rows<D, kBlk, kWavesS, 0>(lds_k[sb], kbase + (int64_t)kb * kBlk * kv_stride, kv_stride,
-                                  L - kb * kBlk, wave, lane);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint16_t* src = kb < nkb[i] ? dsrc[i] + (int64_t)kb * kBlkElems : a.ds;
-      dma_flat<2, 1>(lds_s[sb] + (wave * 2 + i) * kBlkElems, src, 0, lane);
+  // Copy instruction p (0 <= p < PER) of this wave for step kb into stage kb % kStages:
+  // the K tile (rows past L repeat the last key), then the slot's dS blocks (with two
+  // waves per slot, wave `part` copies tile `part`).  A block the tile does not use is
+  // still copied (from the start of the dS area, in bounds) so that every wave issues
+  // PER copies per step; steps past the last re-copy the last step into a free stage.
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t rs_bytes = (uint32_t)(kv_stride * 2);
+  auto issue_one = [&](int kb_req, int p) {
+    const int kb = min(kb_req, n_steps - 1);
+    const int sb = kb_req % kStages;
+    if (p < KI) {
+      constexpr int G = D / 8, RPI = 64 / G;
+      const int i = wu + kWaves * p;    // instruction of the tile
+      const int r = i * RPI + lane / G;  // tile row of this lane
+      const int row = min(r, L - kb * kBlk - 1);
+      const char* b = uniform_ptr(kbase + (int64_t)kb * kBlk * kv_stride);
+      dma16_at(b, (uint32_t)row * rs_bytes + (uint32_t)(((lane % G) ^ swz<D, 0>(r)) * 16),
+               lds_addr(lds_k[sb]) + i * 1024);
+    } else {
+      const int q = p - KI;
+      const int ti = kSplit == 2 ? part : (q >> 1);
+      const int half = q & 1;
+      const uint16_t* src = kb < nkb[ti] ? dsrc[ti] + (int64_t)kb * kBlkElems : a.ds;
+      dma16_at(uniform_ptr(src) + half * 1024, (uint32_t)lane * 16u,
+               lds_addr(lds_s[sb] + (slot * 2 + ti) * kBlkElems) + half * 1024);
     }
   };
-
   f32x16 acc[2][NDB];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[i][db] = f32x16{};
-  const TrOffsets<D> tro(lane);
+    for (int j = 0; j < NDB; ++j) acc[i][j] = f32x16{};
+  // Transposing-read offsets of this wave's K^T blocks db = part * NDB + j.
+  int klo[NDB], khi[NDB];
+  {
+    const TrOffsets<D> tro(lane);
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      const int db = part * NDB + j;
+      int lo = tro.lo[0], hi = tro.hi[0];
+#pragma unroll
+      for (int m = 1; m < TrOffsets<D>::NM; ++m)
+        if ((db & 3) == m) {
+          lo = tro.lo[m];
+          hi = tro.hi[m];
+        }
+      klo[j] = lo + (db >> 2) * 128;
+      khi[j] = hi + (db >> 2) * 128;
+    }
+  }
+  auto kfrag = [&](const uint16_t* kt, int st, int j) {
+    const uint16_t* b = kt + st * 16 * D;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + klo[j]));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + khi[j]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
   const int dso = ds_tr_off(lane);
 
+  if (n_steps > 0) {
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < n_steps) issue(s);
+    for (int s = 0; s < kStages - 1; ++s)
+#pragma unroll
+      for (int p = 0; p < PER; ++p) issue_one(s, p);
+  }
 
   for (int kb = 0; kb < n_steps; ++kb) {
-    // steps issued after kb: min(kStages - 2, n_steps - 1 - kb)
-    const int ahead = n_steps - 1 - kb;
-    if (ahead >= 2) wait_vm<2 * PER>();
-    else if (ahead == 1) wait_vm<PER>();
-    else wait_vm<0>();
-    __syncthreads();  // stage kb is in LDS for every wave; stage kb - 1 is free
-    if (kb + kStages - 1 < n_steps) issue(kb + kStages - 1);
+    wait_vm<(kStages - 2) * PER>();  // stage kb has landed (later stages may be in flight)
+    __syncthreads();                 // stage kb is in LDS for every wave; stage kb - 1 is free
 
     // A tile without a visible pair in this block multiplies zeros (its dS block was not
-    // written); no branch around the products, which would move the accumulators.
-    const bool act0 = kb < nkb[0], act1 = kb < nkb[1];
+    // written); no branch around the products, which would move the accumulators.  The
+    // copies of step kb + kStages - 1 are spread between the products.
+    const uint32_t m0 = kb < nkb[0] ? ~0u : 0u, m1 = kb < nkb[1] ? ~0u : 0u;
     const int sb = kb % kStages;
     const uint16_t* kt = lds_k[sb];
-    const uint16_t* s0 = lds_s[sb] + (wave * 2) * kBlkElems;
+    const uint16_t* s0 = lds_s[sb] + (slot * 2) * kBlkElems;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      u32x4 b0 = ds_frag(s0, dso, st), b1 = ds_frag(s0 + kBlkElems, dso, st);
-      if (!act0) b0 = u32x4{0u, 0u, 0u, 0u};
-      if (!act1) b1 = u32x4{0u, 0u, 0u, 0u};
-      u32x4 ka = tr_frag_at<D>(kt, tro, st, 0);
+      const u32x4 t0 = ds_frag(s0, dso, st), t1 = ds_frag(s0 + kBlkElems, dso, st);
+      const u32x4 b0 = {t0[0] & m0, t0[1] & m0, t0[2] & m0, t0[3] & m0};
+      const u32x4 b1 = {t1[0] & m1, t1[1] & m1, t1[2] & m1, t1[3] & m1};
+      u32x4 ka = kfrag(kt, st, 0);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int j = 0; j < NDB; ++j) {
+        const int it = st * NDB + j;
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+          if (p * 2 * NDB / PER == it) issue_one(kb + kStages - 1, p);
         u32x4 nk = ka;
-        if (db + 1 < NDB) nk = tr_frag_at<D>(kt, tro, st, db + 1);
-        acc[0][db] = mfma32(ka, b0, acc[0][db]);
-        acc[1][db] = mfma32(ka, b1, acc[1][db]);
+        if (j + 1 < NDB) nk = kfrag(kt, st, j + 1);
+        acc[0][j] = mfma32(ka, b0, acc[0][j]);
+        acc[1][j] = mfma32(ka, b1, acc[1][j]);
         ka = nk;
       }
     }
   }
+  wait_vm<0>();  // no copy into LDS outlives the workgroup
 
-  // element r of block db is dimension 32 db + 8 (r / 4) + 4 (lane / 32) + r % 4 of query lane % 32
+  // element r of block j is dimension 32 (part NDB + j) + 8 (r / 4) + 4 (lane / 32) + r % 4
+  // of query lane % 32
   const int col = lane & 31;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const bool ok = col < nq[i];
     const int64_t qrow = (int64_t)ch.q_row + row0 + 32 * i + (ok ? col : 0);
-    uint16_t* op = a.dq + (qrow * a.hq + h) * D + (lane >> 5) * 4;
+    uint16_t* op = a.dq + (qrow * a.hq + h) * D + part * NDB * 32 + (lane >> 5) * 4;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int j = 0; j < NDB; ++j)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const u32x2 w{pack_bf16x2(acc[i][db][4 * i4] * a.scale, acc[i][db][4 * i4 + 1] * a.scale),
-                      pack_bf16x2(acc[i][db][4 * i4 + 2] * a.scale, acc[i][db][4 * i4 + 3] * a.scale)};
-        if (ok) st8(op + db * 32 + i4 * 8, w);
+        const u32x2 w{pack_bf16x2(acc[i][j][4 * i4] * a.scale, acc[i][j][4 * i4 + 1] * a.scale),
+                      pack_bf16x2(acc[i][j][4 * i4 + 2] * a.scale, acc[i][j][4 * i4 + 3] * a.scale)};
+        if (ok) st8(op + j * 32 + i4 * 8, w);
         __builtin_amdgcn_sched_barrier(0);  // one block's registers at a time
       }
   }
@@ -183,16 +240,16 @@ __global__ __launch_bounds__(kThreadsS) void dq_ds_kernel(const AttnArgs a) {
 hipError_t launch_dq_ds(const AttnArgs& a, int D, bool causal, dim3 grid, hipStream_t s) {
   if (causal) {
     switch (D) {
-      case 64: hipLaunchKernelGGL((dq_ds_kernel<64, true>), grid, dim3(kThreadsS), 0, s, a); break;
-      case 128: hipLaunchKernelGGL((dq_ds_kernel<128, true>), grid, dim3(kThreadsS), 0, s, a); break;
-      case 256: hipLaunchKernelGGL((dq_ds_kernel<256, true>), grid, dim3(kThreadsS), 0, s, a); break;
+      case 64: hipLaunchKernelGGL((dq_ds_kernel<64, true>), grid, dim3(DsCfg<64>::kThreads), 0, s, a); break;
+      case 128: hipLaunchKernelGGL((dq_ds_kernel<128, true>), grid, dim3(DsCfg<128>::kThreads), 0, s, a); break;
+      case 256: hipLaunchKernelGGL((dq_ds_kernel<256, true>), grid, dim3(DsCfg<256>::kThreads), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (D) {
-      case 64: hipLaunchKernelGGL((dq_ds_kernel<64, false>), grid, dim3(kThreadsS), 0, s, a); break;
-      case 128: hipLaunchKernelGGL((dq_ds_kernel<128, false>), grid, dim3(kThreadsS), 0, s, a); break;
-      case 256: hipLaunchKernelGGL((dq_ds_kernel<256, false>), grid, dim3(kThreadsS), 0, s, a); break;
+      case 64: hipLaunchKernelGGL((dq_ds_kernel<64, false>), grid, dim3(DsCfg<64>::kThreads), 0, s, a); break;
+      case 128: hipLaunchKernelGGL((dq_ds_kernel<128, false>), grid, dim3(DsCfg<128>::kThreads), 0, s, a); break;
+      case 256: hipLaunchKernelGGL((dq_ds_kernel<256, false>), grid, dim3(DsCfg<256>::kThreads), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
   }
