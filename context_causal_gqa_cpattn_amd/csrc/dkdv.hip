@@ -239,10 +239,28 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     QTileIter nxt = cur;
     const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
     const int nbuf = (buf + 1 == kBufs) ? 0 : buf + 1;
-    if (have_next) {
-      if (tid < kTq) load_stats(a, nxt, g, tid, st_lse, st_dl);
-      dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, g, wave, lane);
+    // Tile copies of the next step: for D >= 128 one instruction every other S/dP k-step
+    // (every wave issues D / 32 of them; without a next tile the current one is re-copied
+    // into the free buffer), for smaller D all at once.
+    constexpr bool SPREAD = D >= 128;
+    constexpr int TI = D * kTq * 2 / 1024 / kWaves;  // copies per wave per tensor
+    const char* cb[2];
+    uint32_t cl[2];
+    if (SPREAD) {
+      const QTileIter& src = have_next ? nxt : cur;
+      const int64_t unit = tile_slot(src.c, src.ch.q_row, src.qt) * a.hq + g * a.group + src.hh;
+      cb[0] = uniform_ptr(a.qt + unit * D * kTq);
+      cb[1] = uniform_ptr(a.dot + unit * D * kTq);
+      cl[0] = lds_addr(lds_t[nbuf][0]);
+      cl[1] = lds_addr(lds_t[nbuf][1]);
     }
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    auto copy_one = [&](int p) {  // p < 2 TI: tensor p / TI, instruction w + kWaves (p % TI)
+      const int which = p / TI, i = wu + kWaves * (p % TI);
+      dma16_at(cb[which] + i * 1024, (uint32_t)lane * 16u, cl[which] + i * 1024);
+    };
+    if (have_next && tid < kTq) load_stats(a, nxt, g, tid, st_lse, st_dl);
+    if (!SPREAD && have_next) dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, g, wave, lane);
 
     // Every wave runs every tile of the loop: tiles that a wave's keys do not see (at the
     // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
@@ -265,6 +283,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       u32x4 fq = tr_a(qtt, 0), fd = tr_a(dtt, 0);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
+        if (SPREAD && (st & 1) == 0) copy_one(st >> 1);
         u32x4 nq_ = fq, nd_ = fd;
         if (st + 1 < NS) {
           nq_ = tr_a(qtt, st + 1);

@@ -127,14 +127,46 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   wait_vm_all();
   __syncthreads();
 
+  // Copies of the next tile, one instruction at a time between the S^T products: NST per
+  // wave (K then V, NST / 2 each).  Copy p of a tensor is tile instruction i = w + 4 p,
+  // rows i RPI + lane / G (clamped to the valid rows), swizzled granule of the row.
+  // The last tile re-copies itself into the free buffer so that the loop has no branch.
+  constexpr int G = D / 8, RPI = 64 / G;
+  static_assert(2 * (kBN * G / 64 / 4) == NST, "one copy per S^T k-step");
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const int lane_row = lane / G;
+  const uint32_t rs_bytes = (uint32_t)(kv_stride * 2);
+  uint32_t gran[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) gran[e] = (uint32_t)(((lane % G) ^ swz<D>((wu + 4 * e) * RPI + lane_row)) * 16);
+  struct CopyStep {
+    const char* bk;
+    const char* bv;
+    uint32_t lk, lv;
+    int last_row;
+  };
+  auto copy_step = [&](int t_next, int buf_next) {
+    const int tsrc = min(t_next, n_tiles - 1);
+    CopyStep c;
+    c.bk = uniform_ptr(kbase + (int64_t)tsrc * kBN * kv_stride);
+    c.bv = uniform_ptr(vbase + (int64_t)tsrc * kBN * kv_stride);
+    c.lk = lds_addr(lds_k[buf_next]);
+    c.lv = lds_addr(lds_v[buf_next]);
+    c.last_row = L - tsrc * kBN - 1;
+    return c;
+  };
+  auto copy_one = [&](const CopyStep& c, int p) {
+    const bool is_v = p >= NST / 2;
+    const int pp = is_v ? p - NST / 2 : p;
+    const int i = wu + 4 * pp;
+    const int row = min(i * RPI + lane_row, c.last_row);
+    dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
+  };
+
   for (int t = 0; t < n_tiles; ++t) {
     const int key0 = t * kBN;
     const int buf = t & 1;
-    if (t + 1 < n_tiles) {
-      const int64_t nxt = (int64_t)(key0 + kBN) * kv_stride;
-      dma_rows<D, kBN>(lds_k[buf ^ 1], kbase + nxt, kv_stride, L - key0 - kBN, wave, lane);
-      dma_rows<D, kBN>(lds_v[buf ^ 1], vbase + nxt, kv_stride, L - key0 - kBN, wave, lane);
-    }
+    const CopyStep cs = copy_step(t + 1, buf ^ 1);
 
     if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
       // scheduling hint: interleave the step's MFMAs with its LDS reads and VALU work
@@ -154,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
             na = lds_row16<D>(kt, col, (st + 1) * 2 + kg);
             nb = lds_row16<D>(kt, 32 + col, (st + 1) * 2 + kg);
           }
+          copy_one(cs, st);
           s[0] = mfma32(ka, qf[st], s[0]);
           s[1] = mfma32(kb_, qf[st], s[1]);
           ka = na;
@@ -211,6 +244,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
           va = nv;
         }
       }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NST; ++p) copy_one(cs, p);
     }
     wait_vm_all();
     __syncthreads();
