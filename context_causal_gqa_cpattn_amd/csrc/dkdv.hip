@@ -335,8 +335,9 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
           ((int64_t)tile_slot(cur.c, cur.ch.q_row, cur.qt) * a.hq + g * a.group + cur.hh) * a.kb_max +
           (wkey0 >> 5);
       uint16_t* dst = a.ds_out + blk * 1024 + n * 32 + hl * 8;
-      st16(dst, pd[0]);
-      st16(dst + 16, pd[1]);
+      // streaming stores: dS is read back only by the dQ product, long after
+      __builtin_nontemporal_store(pd[0], reinterpret_cast<u32x4*>(dst));
+      __builtin_nontemporal_store(pd[1], reinterpret_cast<u32x4*>(dst + 16));
     }
     cur = nxt;
     have = have_next;
