@@ -5,7 +5,8 @@ kernels behind include/cpattn.h.  PyTorch provides device memory and the current
 stream.  There is no fallback: if the library or a GPU is missing, calls raise.
 
 Names follow the C entry points: fwd, bwd, bwd_prepass, bwd_dkdv, bwd_dq,
-bwd_dbias, bwd_dkdv_ds, bwd_dq_ds, validate, pack, unpack.
+bwd_dbias, bwd_dkdv_ds, bwd_dq_ds, fwd_window, merge, bwd_window, validate, pack,
+unpack.
 """
 from __future__ import annotations
 
@@ -30,7 +31,7 @@ EXPORTS = [
     "cpattn_status_str", "cpattn_last_error", "cpattn_version", "cpattn_workspace_size",
     "cpattn_validate", "cpattn_fwd", "cpattn_bwd", "cpattn_bwd_prepass", "cpattn_bwd_dkdv",
     "cpattn_bwd_dq", "cpattn_bwd_dbias", "cpattn_bwd_dkdv_ds", "cpattn_bwd_dq_ds", "cpattn_pack",
-    "cpattn_unpack",
+    "cpattn_unpack", "cpattn_fwd_window", "cpattn_merge", "cpattn_bwd_window",
 ]
 
 
@@ -92,6 +93,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "cpattn_bwd_dkdv_ds": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp,
                                ctypes.c_int, _vp, _vp],
         "cpattn_bwd_dq_ds": [P, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
+        "cpattn_fwd_window": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, i32, i32, _vp, _vp, _vp, _vp],
+        "cpattn_merge": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+        "cpattn_bwd_window": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, i32, i32, ctypes.c_int,
+                              _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, sz, _vp, _vp],
         "cpattn_pack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
         "cpattn_unpack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
     }
@@ -273,6 +278,72 @@ def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optiona
                           1 if dkv_accumulate else 0, _ptr(ws), ws.numel(), _ptr(dev_err),
                           _stream(stream)))
     return dq, dk, dv, dbias, dev_err
+
+
+def fwd_window(q, k, v, layout: Layout, kv_lo: int, kv_hi: int, causal: bool = True,
+               scale: Optional[float] = None, bias=None, o=None, lse=None, dev_err=None, stream=None):
+    """Partial O (bf16) and LSE (fp32) over the keys at positions [kv_lo, kv_hi)."""
+    torch = _torch()
+    lib = load()
+    prob = _prob_for(q, k, v, layout, causal, scale, bias)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((prob.hq, prob.q_rows), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (prob.hq, prob.q_rows))
+    if dev_err is None:
+        dev_err = new_dev_err(q.device)
+    _check(lib.cpattn_fwd_window(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                                 _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), int(kv_lo), int(kv_hi),
+                                 _ptr(o), _ptr(lse), _ptr(dev_err), _stream(stream)))
+    return o, lse, dev_err
+
+
+def merge(prob: Problem, layout: Layout, o_a, lse_a, o_b, lse_b, o=None, lse=None, dev_err=None,
+          stream=None):
+    """Merge two partial results over disjoint key sets; o/lse default to o_a/lse_a (in place)."""
+    lib = load()
+    if o is None:
+        o = o_a
+    if lse is None:
+        lse = lse_a
+    if dev_err is None:
+        dev_err = new_dev_err(o_a.device)
+    _check(lib.cpattn_merge(ctypes.byref(prob), _ptr(layout.chunks), _ptr(o_a), _ptr(lse_a), _ptr(o_b),
+                            _ptr(lse_b), _ptr(o), _ptr(lse), _ptr(dev_err), _stream(stream)))
+    return o, lse
+
+
+def bwd_window(q, k, v, layout: Layout, o, lse, do, kv_lo: int, kv_hi: int, causal: bool = True,
+               scale: Optional[float] = None, bias=None, prepass: bool = True, dq=None,
+               dq_accumulate: bool = False, dk=None, dv=None, dkv_accumulate: bool = False, ws=None,
+               dev_err=None, stream=None):
+    """The key window [kv_lo, kv_hi)'s dQ share (store or add) and its keys' dK/dV."""
+    torch = _torch()
+    lib = load()
+    prob = _prob_for(q, k, v, layout, causal, scale, bias)
+    if dq is None:
+        if dq_accumulate:
+            raise ValueError("dq_accumulate needs an existing dq")
+        dq = torch.empty_like(q)
+    if dk is None:
+        if dkv_accumulate:
+            raise ValueError("dkv_accumulate needs existing dk/dv")
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    need = workspace_size(prob, OP_BWD)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if dev_err is None:
+        dev_err = new_dev_err(q.device)
+    _check(lib.cpattn_bwd_window(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                                 _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(o), _ptr(lse),
+                                 _ptr(do), int(kv_lo), int(kv_hi), 1 if prepass else 0, _ptr(dq),
+                                 1 if dq_accumulate else 0, _ptr(dk), _ptr(dv), 1 if dkv_accumulate else 0,
+                                 _ptr(ws), ws.numel(), _ptr(dev_err), _stream(stream)))
+    return dq, dk, dv, ws, dev_err
 
 
 def bwd_prepass(prob: Problem, layout: Layout, q, o, do, ws, dev_err, stream=None):

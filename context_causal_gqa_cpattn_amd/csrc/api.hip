@@ -8,6 +8,7 @@
 // with first-gradient reuse" (pointer-alias audits outside the timed region).
 // Page on the ws2 tensor/sequence/context-parallel block ("Scope / Known
 // limitations"): unsupported shapes and dtypes raise instead of falling back.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -189,6 +190,9 @@ AttnArgs base_args(const cpattn_problem* p, const Plan& pl) {
   a.parts = pl.parts;
   a.scale = p->scale;
   a.scale_log2 = p->scale * kLog2e;
+  a.kv_lo = 0;
+  a.kv_hi = INT_MAX;
+  a.dq_accumulate = 0;
   return a;
 }
 
@@ -271,10 +275,11 @@ int cpattn_validate(const cpattn_problem* p, const int32_t* seq_offsets, const i
   return run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, (hipStream_t)stream);
 }
 
-int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
-               const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
-               const float* bias, void* o, float* lse, void* ws, size_t ws_bytes,
-               int32_t* dev_err, cpattn_stream_t stream) {
+namespace {
+int fwd_impl(const cpattn_problem* p, const void* q, const void* k, const void* v,
+             const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
+             const float* bias, int32_t kv_lo, int32_t kv_hi, void* o, float* lse,
+             int32_t* dev_err, cpattn_stream_t stream) {
   g_last_error.clear();
   Plan pl;
   int r;
@@ -285,9 +290,8 @@ int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void
       (r = check_ptr(bias, pl.bias_bytes, 16, "bias")))
     return r;
   if (!pl.bias && bias) return fail(CPATTN_EINVAL, "bias given but bias_len is 0");
+  if (kv_lo < 0 || kv_hi < kv_lo) return fail(CPATTN_EINVAL, "key window [%d, %d) is invalid", kv_lo, kv_hi);
   if ((r = check_descriptors(p, seq_offsets, seq_lens, q_chunk_map, dev_err))) return r;
-  (void)ws;
-  (void)ws_bytes;
   std::vector<Range> rs = {rng("q", q, pl.q_bytes, false), rng("k", k, pl.kv_bytes, false),
                            rng("v", v, pl.kv_bytes, false), rng("bias", bias, pl.bias_bytes, false),
                            rng("o", o, pl.q_bytes, true), rng("lse", lse, pl.stat_bytes, true)};
@@ -309,7 +313,71 @@ int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void
   a.chunks = q_chunk_map;
   a.dev_err = dev_err;
   a.blocks_per_chunk = pl.bpc_fwd;
+  a.kv_lo = kv_lo;
+  a.kv_hi = kv_hi;
   return hip_check(launch_fwd(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd1d, s), "forward launch");
+}
+}  // namespace
+
+int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
+               const int32_t* seq_offsets, const int32_t* seq_lens, const int32_t* q_chunk_map,
+               const float* bias, void* o, float* lse, void* ws, size_t ws_bytes,
+               int32_t* dev_err, cpattn_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return fwd_impl(p, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, 0, INT_MAX, o, lse, dev_err,
+                  stream);
+}
+
+int cpattn_fwd_window(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                      const int32_t* seq_offsets, const int32_t* seq_lens,
+                      const int32_t* q_chunk_map, const float* bias, int32_t kv_lo, int32_t kv_hi,
+                      void* o, float* lse, int32_t* dev_err, cpattn_stream_t stream) {
+  return fwd_impl(p, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, kv_lo, kv_hi, o, lse, dev_err,
+                  stream);
+}
+
+int cpattn_merge(const cpattn_problem* p, const int32_t* q_chunk_map, const void* o_a,
+                 const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                 const int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = check_ptr(o_a, pl.q_bytes, 16, "o_a")) || (r = check_ptr(o_b, pl.q_bytes, 16, "o_b")) ||
+      (r = check_ptr(o, pl.q_bytes, 16, "o")) || (r = check_ptr(lse_a, pl.stat_bytes, 4, "lse_a")) ||
+      (r = check_ptr(lse_b, pl.stat_bytes, 4, "lse_b")) || (r = check_ptr(lse, pl.stat_bytes, 4, "lse")) ||
+      (r = check_ptr(q_chunk_map, (uint64_t)p->num_chunks * 16, 16, "q_chunk_map")) ||
+      (r = check_ptr(dev_err, 4, 4, "dev_err")))
+    return r;
+  // o may be o_a and lse may be lse_a (the running result updated in place); every other
+  // overlap is rejected.
+  std::vector<Range> rs = {rng("o_b", o_b, pl.q_bytes, false), rng("lse_b", lse_b, pl.stat_bytes, false),
+                           rng("o", o, pl.q_bytes, true), rng("lse", lse, pl.stat_bytes, true),
+                           rng("q_chunk_map", q_chunk_map, (uint64_t)p->num_chunks * 16, false),
+                           rng("dev_err", dev_err, 4, false)};
+  if (o_a != o) rs.push_back(rng("o_a", o_a, pl.q_bytes, false));
+  if (lse_a != lse) rs.push_back(rng("lse_a", lse_a, pl.stat_bytes, false));
+  if ((r = alias_audit(rs))) return r;
+  const int pairs_per_wg = kThreads / (pl.D / 8);
+  const int64_t bpc = cdiv((int64_t)p->max_chunk_len * p->hq, pairs_per_wg);
+  const int64_t gx = (int64_t)p->num_chunks * bpc;
+  if (gx > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
+  if (gx == 0) return CPATTN_OK;
+  MergeArgs m{};
+  m.o_a = (const uint16_t*)o_a;
+  m.lse_a = lse_a;
+  m.o_b = (const uint16_t*)o_b;
+  m.lse_b = lse_b;
+  m.o = (uint16_t*)o;
+  m.lse = lse;
+  m.chunks = q_chunk_map;
+  m.dev_err = dev_err;
+  m.q_rows = p->q_rows;
+  m.hq = p->hq;
+  m.D = pl.D;
+  m.blocks_per_chunk = (int)bpc;
+  return hip_check(launch_merge(m, dim3((unsigned)gx), (hipStream_t)stream), "merge launch");
 }
 
 // ---------------------------------------------------------------- backward steps
@@ -455,6 +523,51 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
   }
   if (dbias) return enqueue_dbias(p, pl, a, dbias, ws, s);
   return CPATTN_OK;
+}
+
+int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                      const int32_t* seq_offsets, const int32_t* seq_lens,
+                      const int32_t* q_chunk_map, const float* bias, const void* o, const float* lse,
+                      const void* dout, int32_t kv_lo, int32_t kv_hi, int prepass, void* dq,
+                      int dq_accumulate, void* dk, void* dv, int dkv_accumulate, void* ws,
+                      size_t ws_bytes, int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, seq_offsets, seq_lens, q_chunk_map,
+                             dev_err)))
+    return r;
+  if ((r = check_ptr(o, pl.q_bytes, 16, "o")) || (r = check_ptr(dq, pl.q_bytes, 16, "dq")) ||
+      (r = check_ptr(dk, pl.kv_bytes, 16, "dk")) || (r = check_ptr(dv, pl.kv_bytes, 16, "dv")))
+    return r;
+  if (kv_lo < 0 || kv_hi < kv_lo) return fail(CPATTN_EINVAL, "key window [%d, %d) is invalid", kv_lo, kv_hi);
+  if ((prepass != 0 && prepass != 1) || (dq_accumulate != 0 && dq_accumulate != 1) ||
+      (dkv_accumulate != 0 && dkv_accumulate != 1))
+    return fail(CPATTN_EINVAL, "prepass, dq_accumulate and dkv_accumulate must be 0 or 1");
+  if ((int64_t)ws_bytes < pl.ws_core)
+    return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)pl.ws_core);
+  if ((r = check_ptr(ws, pl.ws_core, 256, "ws"))) return r;
+  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),        rng("k", k, pl.kv_bytes, false),
+                           rng("v", v, pl.kv_bytes, false),        rng("bias", bias, pl.bias_bytes, false),
+                           rng("o", o, pl.q_bytes, false),         rng("lse", lse, pl.stat_bytes, false),
+                           rng("dout", dout, pl.q_bytes, false),   rng("dq", dq, pl.q_bytes, true),
+                           rng("dk", dk, pl.kv_bytes, true),       rng("dv", dv, pl.kv_bytes, true),
+                           rng("ws", ws, pl.ws_core, prepass != 0)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, prepass != 0);
+  if ((r = alias_audit(rs))) return r;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (prepass) {
+    if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
+    if ((r = enqueue_prepass(p, pl, q_chunk_map, q, o, dout, ws, dev_err, s))) return r;
+  }
+  AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
+  a.kv_lo = kv_lo;
+  a.kv_hi = kv_hi;
+  a.dq_accumulate = dq_accumulate;
+  if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
+  return enqueue_dq(p, pl, a, dq, s);
 }
 
 int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,

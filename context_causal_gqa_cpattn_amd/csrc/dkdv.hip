@@ -145,12 +145,14 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   const int b = rest / a.hkv;
   const int L = a.seq_lens[b];
   const int wg_key0 = kt * kDkdvKeys;
-  if (wg_key0 >= L) return;  // uniform over the workgroup, before any barrier
+  // no key of the tile in the sequence or in the key window [kv_lo, kv_hi)
+  if (wg_key0 >= L || wg_key0 >= a.kv_hi || wg_key0 + kDkdvKeys <= a.kv_lo) return;
   const int64_t koff = a.seq_offsets[b];
   const int wkey0 = wg_key0 + wave * 32;
   const int nk = max(0, min(32, L - wkey0));
   const int key = wkey0 + n;  // this lane's key (column of S, dP, dK^T, dV^T)
-  const bool key_ok = n < nk;
+  const bool key_ok = n < nk && key >= a.kv_lo && key < a.kv_hi;  // in the sequence and the window
+  const bool wave_in_window = wkey0 >= a.kv_lo && wkey0 + 32 <= a.kv_hi;
 
   // K and V as B operands: lane (hl, n) holds key n, dimensions 16 st + 8 hl + [0, 8).
   // Lanes past the sequence end load its last key (finite values; their P and dS are 0).
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     };
     if (PIPE && have_prev) {
       dvdk(pbuf, pp, pd, sm_block);
-    } else if (PIPE || (nk < 32) || (nq < kTq) || (CAUSAL && tile_pos0 < wkey0 + 31)) {
+    } else if (PIPE || (nk < 32) || !wave_in_window || (nq < kTq) || (CAUSAL && tile_pos0 < wkey0 + 31)) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) sm_block(blk);
     } else {  // a tile every key of the wave sees: no mask

@@ -66,11 +66,12 @@ __device__ __forceinline__ u32x4 kt_frag(const uint16_t* kt, const KtOffsets<D>&
 }
 
 // dS^T = P^T (dP^T - Delta) for one 64-key tile, in place in dp (lane = query).
-// Element j of block kb is key key0 + 16 kb + 4 g + j.
+// Element j of block kb is key key0 + 16 kb + 4 g + j; with MASK, keys outside [lo, hi)
+// (and past the query position when causal) give 0.
 template <bool BIAS, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void ds_tile(const f32x4 (&s)[4], f32x4 (&dp)[4], float c,
-                                        const float* bias_row, int key0, int L, int qpos, int g,
-                                        int bias_len, float lse2, float dlt) {
+                                        const float* bias_row, int key0, int lo, int hi, int qpos,
+                                        int g, int bias_len, float lse2, float dlt) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -81,7 +82,7 @@ __device__ __forceinline__ void ds_tile(const f32x4 (&s)[4], f32x4 (&dp)[4], flo
         x = fmaf(bias_row[min(kk, bias_len - 1)], kLog2e, s[kb][j] * c) - lse2;
       else
         x = fmaf(s[kb][j], c, -lse2);
-      if (MASK) x = ((kk < L) && (!CAUSAL || kk <= qpos)) ? x : -INFINITY;
+      if (MASK) x = ((kk >= lo) && (kk < hi) && (!CAUSAL || kk <= qpos)) ? x : -INFINITY;
       const float p = exp2f_fast(x);  // a masked score is exp2(-inf) = 0
       dp[kb][j] = p * (dp[kb][j] - dlt);
     }
@@ -116,8 +117,13 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   const int L = a.seq_lens[ch.seq];
   const int64_t koff = a.seq_offsets[ch.seq];
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + wg_pos) - 1;
-  const int kv_end = CAUSAL ? min(L, wg_last_pos + 1) : L;
-  const int n_tiles = (kv_end + kKeys - 1) / kKeys;
+  // Keys [kv_lo, kv_end): the key window (the whole sequence without one), cut at the
+  // workgroup's last position when causal.
+  const int kv_lo = a.kv_lo;
+  const int kv_hi = min(L, a.kv_hi);
+  const int kv_end = min(CAUSAL ? min(L, wg_last_pos + 1) : L, kv_hi);
+  const int t_first = kv_lo / kKeys;               // first tile (absolute index)
+  const int n_tiles = (kv_end + kKeys - 1) / kKeys;  // one past the last tile
   const int wave_first_pos = ch.pos0 + row0;
   const int wave_last_pos = wave_first_pos + nrows - 1;
   const int qpos = wave_first_pos + q;
@@ -148,16 +154,17 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)kvh * D;
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)kvh * D;
 
-  if (n_tiles > 0) {
-    dma_rows<D, kKeys, kWavesQ, kSwz>(lds_k[0], kbase, kv_stride, L, wave, lane);
-    dma_rows<D, kKeys, kWavesQ, kSwz>(lds_v[0], vbase, kv_stride, L, wave, lane);
+  if (n_tiles > t_first) {
+    const int64_t first = (int64_t)t_first * kKeys * kv_stride;
+    dma_rows<D, kKeys, kWavesQ, kSwz>(lds_k[0], kbase + first, kv_stride, L - t_first * kKeys, wave, lane);
+    dma_rows<D, kKeys, kWavesQ, kSwz>(lds_v[0], vbase + first, kv_stride, L - t_first * kKeys, wave, lane);
   }
   wait_vm_all();
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = t_first; t < n_tiles; ++t) {
     const int key0 = t * kKeys;
-    const int buf = t & 1;
+    const int buf = (t - t_first) & 1;
     if (t + 1 < n_tiles) {
       const int64_t nxt = (int64_t)(key0 + kKeys) * kv_stride;
       dma_rows<D, kKeys, kWavesQ, kSwz>(lds_k[buf ^ 1], kbase + nxt, kv_stride, L - key0 - kKeys, wave, lane);
@@ -180,11 +187,14 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
           s[kb] = mfma16(lds_row16<D, kSwz>(kt, 16 * kb + q, 4 * st + g), qf[st], s[kb]);
           dp[kb] = mfma16(lds_row16<D, kSwz>(vt, 16 * kb + q, 4 * st + g), dof[st], dp[kb]);
         }
-      const bool need_mask = (key0 + kKeys > L) || (CAUSAL && key0 + kKeys - 1 > wave_first_pos);
+      const bool need_mask = (key0 + kKeys > kv_hi) || (key0 < kv_lo) ||
+                             (CAUSAL && key0 + kKeys - 1 > wave_first_pos);
       if (need_mask)
-        ds_tile<BIAS, true, CAUSAL>(s, dp, a.scale_log2, bias_row, key0, L, qpos, g, a.bias_len, lse2, dlt);
+        ds_tile<BIAS, true, CAUSAL>(s, dp, a.scale_log2, bias_row, key0, kv_lo, kv_hi, qpos, g, a.bias_len,
+                                    lse2, dlt);
       else
-        ds_tile<BIAS, false, CAUSAL>(s, dp, a.scale_log2, bias_row, key0, L, qpos, g, a.bias_len, lse2, dlt);
+        ds_tile<BIAS, false, CAUSAL>(s, dp, a.scale_log2, bias_row, key0, kv_lo, kv_hi, qpos, g, a.bias_len,
+                                     lse2, dlt);
       // dQ^T += K^T dS^T over two 32-key steps; k-position 8 g + e of step ks is key
       // 32 ks + 16 (e / 4) + 4 g + e % 4, i.e. element e % 4 of blocks 2 ks and 2 ks + 1.
 #pragma unroll
@@ -201,12 +211,23 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   }
 
   if (!qok) return;
-  // element j of block db is dimension 16 db + 4 g + j
+  // element j of block db is dimension 16 db + 4 g + j; with dq_accumulate the existing
+  // BF16 value is added in fp32 and the sum rounded once (a key window's contribution)
   uint16_t* op = a.dq + (qrow * a.hq + h) * D + g * 4;
+  if (a.dq_accumulate) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    st8(op + db * 16, u32x2{pack_bf16x2(dqt[db][0] * a.scale, dqt[db][1] * a.scale),
-                            pack_bf16x2(dqt[db][2] * a.scale, dqt[db][3] * a.scale)});
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2 old = ld8(op + db * 16);
+      st8(op + db * 16,
+          u32x2{pack_bf16x2(fmaf(dqt[db][0], a.scale, bf16_lo(old[0])), fmaf(dqt[db][1], a.scale, bf16_hi(old[0]))),
+                pack_bf16x2(fmaf(dqt[db][2], a.scale, bf16_lo(old[1])), fmaf(dqt[db][3], a.scale, bf16_hi(old[1])))});
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      st8(op + db * 16, u32x2{pack_bf16x2(dqt[db][0] * a.scale, dqt[db][1] * a.scale),
+                              pack_bf16x2(dqt[db][2] * a.scale, dqt[db][3] * a.scale)});
+  }
 }
 
 hipError_t launch_dq(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s) {

@@ -27,12 +27,14 @@ namespace cpattn {
 
 constexpr int kBN = 64;  // keys per KV tile
 
-// Scores of one 64-key tile in base 2 (+ bias), masked when MASK; returns the lane max
-// (four independent running maxima, so the chain is a quarter as long).
+// Scores of one 64-key tile in base 2 (+ bias), masked when MASK (keys outside
+// [lo, hi), and past the query position when causal); returns the lane max (four
+// independent running maxima, so the chain is a quarter as long).
 // Element r of block kb is key key0 + 32 kb + 8 (r/4) + 4 kg + r%4.
 template <bool BIAS, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float* bias_row, int key0,
-                                           int L, int qpos, int kg, int bias_len, float& mx) {
+                                           int L, int lo, int hi, int qpos, int kg, int bias_len,
+                                           float& mx) {
   float mj[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -54,7 +56,7 @@ __device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float*
         if (BIAS) x = fmaf(bv[j], kLog2e, x);
         if (MASK) {
           const int key = kbi + j;
-          x = ((key < L) && (!CAUSAL || key <= qpos)) ? x : -INFINITY;
+          x = ((key >= lo) && (key < hi) && (!CAUSAL || key <= qpos)) ? x : -INFINITY;
         }
         s[kb][i * 4 + j] = x;
         mj[j] = fmaxf(mj[j], x);
@@ -92,8 +94,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   const int64_t koff = a.seq_offsets[ch.seq];
 
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + 32 * segs) - 1;
-  const int kv_end = CAUSAL ? min(L, wg_last_pos + 1) : L;
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  // Keys [kv_lo, kv_end) are visible to some row of the workgroup: the key window
+  // (the whole sequence without one) cut at the last position when causal.
+  const int kv_lo = a.kv_lo;
+  const int kv_hi = min(L, a.kv_hi);
+  const int kv_end = min(CAUSAL ? min(L, wg_last_pos + 1) : L, kv_hi);
+  const int t_first = kv_lo / kBN;                // first tile (absolute index)
+  const int n_tiles = (kv_end + kBN - 1) / kBN;   // one past the last tile
   const int wave_first_pos = ch.pos0 + row0;
   const int wave_last_pos = wave_first_pos + nrows - 1;
   const int qpos = wave_first_pos + col;  // this lane's query position
@@ -120,9 +127,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)g * D;
 
-  if (n_tiles > 0) {
-    dma_rows<D, kBN>(lds_k[0], kbase, kv_stride, L, wave, lane);
-    dma_rows<D, kBN>(lds_v[0], vbase, kv_stride, L, wave, lane);
+  if (n_tiles > t_first) {
+    const int64_t first = (int64_t)t_first * kBN * kv_stride;
+    dma_rows<D, kBN>(lds_k[0], kbase + first, kv_stride, L - t_first * kBN, wave, lane);
+    dma_rows<D, kBN>(lds_v[0], vbase + first, kv_stride, L - t_first * kBN, wave, lane);
   }
   wait_vm_all();
   __syncthreads();
@@ -163,9 +171,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
   };
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = t_first; t < n_tiles; ++t) {
     const int key0 = t * kBN;
-    const int buf = t & 1;
+    const int buf = (t - t_first) & 1;
     const CopyStep cs = copy_step(t + 1, buf ^ 1);
 
     if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
@@ -196,13 +204,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 
       // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.  The
       // masked and unmasked tiles take separate, wave-uniform paths.
-      const bool need_mask = (key0 + kBN > L) || (CAUSAL && key0 + kBN - 1 > wave_first_pos);
+      const bool need_mask = (key0 + kBN > kv_hi) || (key0 < kv_lo) ||
+                             (CAUSAL && key0 + kBN - 1 > wave_first_pos);
       float mx = -INFINITY;
       if (need_mask) {
         asm volatile("" ::: "memory");
-        scale_tile<BIAS, true, CAUSAL>(s, a.scale_log2, bias_row, key0, L, qpos, kg, a.bias_len, mx);
+        scale_tile<BIAS, true, CAUSAL>(s, a.scale_log2, bias_row, key0, L, kv_lo, kv_hi, qpos, kg,
+                                       a.bias_len, mx);
       } else {
-        scale_tile<BIAS, false, CAUSAL>(s, a.scale_log2, bias_row, key0, L, qpos, kg, a.bias_len, mx);
+        scale_tile<BIAS, false, CAUSAL>(s, a.scale_log2, bias_row, key0, L, kv_lo, kv_hi, qpos, kg,
+                                        a.bias_len, mx);
       }
       mx = fmaxf(mx, xor32(mx));
       // Lazy rescale: move the reference max only when it grows by more than 8 (x256).
@@ -253,8 +264,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   }
 
   if (col >= nrows) return;
+  // A row with no visible key in the window: O = 0 and LSE = -inf (merges as nothing).
   const float l = l_run + xor32(l_run);
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   uint16_t* op = a.o_out + ((int64_t)(ch.q_row + row0 + col) * a.hq + h) * D + kg * 4;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -265,7 +277,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       w[1] = pack_bf16x2(oacc[db][i * 4 + 2] * inv, oacc[db][i * 4 + 3] * inv);
       st8(op + db * 32 + i * 8, w);
     }
-  if (kg == 0) a.lse_out[(int64_t)h * a.q_rows + ch.q_row + row0 + col] = (m_run + log2f_fast(l)) * kLn2;
+  if (kg == 0)
+    a.lse_out[(int64_t)h * a.q_rows + ch.q_row + row0 + col] = l > 0.f ? (m_run + log2f_fast(l)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL, bool BIAS>

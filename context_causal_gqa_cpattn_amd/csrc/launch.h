@@ -28,7 +28,20 @@ struct LayoutArgs {
   int unpack;  // 0: BHSD -> THD, 1: THD -> BHSD
 };
 
+struct MergeArgs {
+  const uint16_t* o_a;  // partial O over key set A, [q_rows, hq, D] BF16
+  const float* lse_a;   // its LSE, [hq, q_rows]
+  const uint16_t* o_b;
+  const float* lse_b;
+  uint16_t* o;          // merged O (may be o_a)
+  float* lse;           // merged LSE (may be lse_a)
+  const int32_t* chunks;
+  const int32_t* dev_err;
+  int64_t q_rows;
+  int hq, D, blocks_per_chunk;
+};
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
 hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s);

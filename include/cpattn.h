@@ -145,6 +145,29 @@ int cpattn_fwd(const cpattn_problem* p, const void* q, const void* k, const void
                const float* bias, void* o, float* lse, void* ws, size_t ws_bytes,
                int32_t* dev_err, cpattn_stream_t stream);
 
+/* Forward over a key window ("Private C++ FROST P2P": CP over point-to-point steps,
+ * each attending to one K/V block): as cpattn_fwd with the visible keys further
+ * restricted to sequence positions [kv_lo, kv_hi).  O (BF16) is the softmax over
+ * the window's visible keys applied to V and LSE (fp32) their log-sum-exp; a row
+ * with no visible key in the window gets O = 0 and LSE = -inf.  Two results over
+ * disjoint windows combine with cpattn_merge.  kv_lo = 0, kv_hi >= every L_b is
+ * cpattn_fwd.  EINVAL for kv_lo < 0 or kv_hi < kv_lo. */
+int cpattn_fwd_window(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                      const int32_t* seq_offsets, const int32_t* seq_lens,
+                      const int32_t* q_chunk_map, const float* bias, int32_t kv_lo, int32_t kv_hi,
+                      void* o, float* lse, int32_t* dev_err, cpattn_stream_t stream);
+
+/* Merge of two partial results over disjoint key sets A and B (the ring step's LSE
+ * correction): on every chunk row and head, LSE = log(e^lse_a + e^lse_b) and
+ * O = e^(lse_a - LSE) o_a + e^(lse_b - LSE) o_b in fp32, rounded to BF16 once; rows
+ * whose two LSEs are -inf get O = 0, LSE = -inf.  o may equal o_a and lse may equal
+ * lse_a (the running result updated in place); any other overlap is EINVAL.  Does
+ * not validate (call cpattn_validate first on the same stream with the same dev_err);
+ * does nothing when *dev_err is set. */
+int cpattn_merge(const cpattn_problem* p, const int32_t* q_chunk_map, const void* o_a,
+                 const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                 const int32_t* dev_err, cpattn_stream_t stream);
+
 /* Backward: validate, the Delta pre-pass, dK/dV, then dQ.
  *  dQ (BF16) is written on chunk rows.
  *  dK/dV (BF16) are the sums over all chunks of each sequence and over the
@@ -165,6 +188,24 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
                const float* bias, const void* o, const float* lse, const void* dout,
                void* dq, void* dk, void* dv, float* dbias, int dkv_accumulate,
                void* ws, size_t ws_bytes, int32_t* dev_err, cpattn_stream_t stream);
+
+/* Backward over a key window: the contribution of the keys at sequence positions
+ * [kv_lo, kv_hi), with O and LSE the complete forward results (merged over all
+ * windows), so P = exp(S - LSE) and Delta = rowsum(dO * O) are those of the whole
+ * attention.  dK/dV are written for the window's valid keys only (STORE, or ADD with
+ * dkv_accumulate = 1; other rows untouched).  dQ gets the window's share of
+ * scale dS K: STORE (dq_accumulate = 0) or added to the existing BF16 values and
+ * rounded once (dq_accumulate = 1), so dQ summed over disjoint windows covering
+ * every key is the full dQ.  prepass = 1 validates and runs the Delta pre-pass into
+ * ws (cpattn_workspace_size(p, CPATTN_OP_BWD) bytes, without the dBias partials);
+ * prepass = 0 reuses the pre-pass results an earlier call left in ws for the same O,
+ * dO and chunks.  dS is formed again for dQ (no dS store), and no dBias is produced. */
+int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                      const int32_t* seq_offsets, const int32_t* seq_lens,
+                      const int32_t* q_chunk_map, const float* bias, const void* o, const float* lse,
+                      const void* dout, int32_t kv_lo, int32_t kv_hi, int prepass, void* dq,
+                      int dq_accumulate, void* dk, void* dv, int dkv_accumulate, void* ws,
+                      size_t ws_bytes, int32_t* dev_err, cpattn_stream_t stream);
 
 /* The backward's steps one by one, for callers that schedule them (and for
  * timing each kernel).  None of them validates: call cpattn_validate first on

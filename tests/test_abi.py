@@ -211,3 +211,31 @@ def test_stored_ds_steps_check_workspace_and_aliases():
     args32 = [ctypes.byref(p32)] + args[1:]
     assert lib.cpattn_bwd_dkdv_ds(*args32, ws, 1 << 30, dk, dv, 0, err, None) == cp.EUNSUPPORTED
     assert lib.cpattn_bwd_dq_ds(ctypes.byref(p32), k, so, sl, cm, ws, 1 << 30, dq, err, None) == cp.EUNSUPPORTED
+
+
+def test_window_and_merge_host_checks():
+    lib = cp.load()
+    p = _prob()
+    q, k, v = A, A + (1 << 24), A + (2 << 24)
+    so, sl, cm = A + (3 << 24), A + (3 << 24) + 256, A + (3 << 24) + 512
+    o, lse, do, err, ws = A + (4 << 24), A + (5 << 24), A + (8 << 24), A + (6 << 24), A + (12 << 24)
+    dk, dv, dq = A + (9 << 24), A + (10 << 24), A + (11 << 24)
+    fa = [ctypes.byref(p), q, k, v, so, sl, cm, None]
+    assert lib.cpattn_fwd_window(*fa, -1, 10, o, lse, err, None) == cp.EINVAL and "window" in _err()
+    assert lib.cpattn_fwd_window(*fa, 10, 5, o, lse, err, None) == cp.EINVAL and "window" in _err()
+    assert lib.cpattn_fwd_window(*fa, 0, 10, q + 4096, lse, err, None) == cp.EINVAL and "alias" in _err()
+    # merge: in place on (o_a, lse_a) is allowed by the host checks; other overlaps are not
+    o2, l2 = A + (13 << 24), A + (14 << 24)
+    assert lib.cpattn_merge(ctypes.byref(p), cm, o, lse, o2, l2, o2 + 4096, lse, err, None) == cp.EINVAL
+    assert "alias" in _err()
+    assert lib.cpattn_merge(ctypes.byref(p), cm, o, lse, o2, l2, o, l2, err, None) == cp.EINVAL
+    assert "alias" in _err()
+    assert lib.cpattn_merge(ctypes.byref(p), cm, o, lse, None, l2, o, lse, err, None) == cp.EINVAL
+    core = _ws_layout(8, 64, 2, 128)
+    ba = [ctypes.byref(p), q, k, v, so, sl, cm, None, o, lse, do]
+    assert lib.cpattn_bwd_window(*ba, 5, 1, 1, dq, 0, dk, dv, 0, ws, core, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_window(*ba, 0, 8, 2, dq, 0, dk, dv, 0, ws, core, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_window(*ba, 0, 8, 1, dq, 0, dk, dv, 0, ws, core - 1, err, None) == cp.EINVAL
+    assert "workspace" in _err()
+    assert lib.cpattn_bwd_window(*ba, 0, 8, 1, dk + 64, 0, dk, dv, 0, ws, core, err, None) == cp.EINVAL
+    assert "alias" in _err()
