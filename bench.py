@@ -12,7 +12,8 @@ HBM.  `roofline` reports the dominant kernel, timed with HIP events on the
 stream it runs on; `cpu_baseline` times the FP64 oracle on a bounded sample of
 the same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu] [--no-ring]
+                       [--recompute-dq]
 """
 from __future__ import annotations
 
@@ -55,6 +56,7 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-ring", action="store_true", help="skip the key-window ring-step timing")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="dQ forms S, P and dP again instead of multiplying the stored dS")
     return ap.parse_args()
@@ -112,6 +114,63 @@ def layout_copy_rates(cp, torch, reps=10):
         out[name + "_ms"] = round(ms, 4)
     cp.check(err)
     out["bytes_per_call"] = 2 * x.numel() * 2
+    return out
+
+
+def ring_step_rates(cp, torch, w, q, k, v, do, bias, lay, flop, windows=8, reps=2):
+    """The workload split into `windows` key windows of equal length, as a ring of steps.
+
+    Forward: one window forward per step, each merged into the running (O, LSE).
+    Backward: one window backward per step (the pre-pass once), dQ added over the
+    steps.  Timed separately from the main step (not part of `value`)."""
+    Lmax = int(max(w.seq_lens))
+    edges = [Lmax * i // windows for i in range(windows)] + [1 << 30]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.q_rows), dtype=torch.float32, device="cuda")
+    o_w = torch.empty_like(q)
+    lse_w = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    prob = cp.problem(lay, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal, w.scale, w.bias_len)
+    ws = torch.empty(max(cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
+    err = cp.new_dev_err()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def fwd():
+        for i in range(windows):
+            lo, hi = edges[i], edges[i + 1]
+            if i == 0:
+                cp.fwd_window(q, k, v, lay, lo, hi, causal=w.causal, scale=w.scale, bias=bias, o=o, lse=lse,
+                              dev_err=err)
+            else:
+                cp.fwd_window(q, k, v, lay, lo, hi, causal=w.causal, scale=w.scale, bias=bias, o=o_w,
+                              lse=lse_w, dev_err=err)
+                cp.merge(prob, lay, o, lse, o_w, lse_w, dev_err=err)
+
+    def bwd():
+        for i in range(windows):
+            cp.bwd_window(q, k, v, lay, o, lse, do, edges[i], edges[i + 1], causal=w.causal, scale=w.scale,
+                          bias=bias, prepass=(i == 0), dq=dq, dq_accumulate=(i > 0), dk=dk, dv=dv, ws=ws,
+                          dev_err=err)
+
+    def merges():
+        for _ in range(windows - 1):
+            cp.merge(prob, lay, o, lse, o_w, lse_w, dev_err=err)
+
+    out = {"windows": windows}
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    for name, fn in (("fwd", fwd), ("bwd", bwd), ("merges", merges)):
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 3)
+    cp.check(err)
+    out["tflops"] = round(flop / ((out["fwd_ms"] + out["bwd_ms"]) * 1e-3) / 1e12, 2)
+    out["merge_gbs"] = round(3 * q.numel() * 2 * (windows - 1) / (out["merges_ms"] * 1e-3) / 1e9, 1)
     return out
 
 
@@ -226,6 +285,8 @@ def main():
     ms = wall * 1e3 / args.steps
 
     copy = layout_copy_rates(cp, torch)
+    ring = None if args.no_ring else ring_step_rates(
+        cp, torch, w, q, k, v, do, bias, lay, visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq * 14 * w.head_dim)
 
     pairs = visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq
     D = w.head_dim
@@ -280,6 +341,7 @@ def main():
         "dq_path": "stored dS" if use_ds else "recompute",
         "ds_bytes_per_step": ds_bytes if use_ds else 0,
         "layout_copy": copy,
+        "ring_step": ring,
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
