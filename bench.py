@@ -13,7 +13,7 @@ stream it runs on; `cpu_baseline` times the FP64 oracle on a bounded sample of
 the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu] [--no-ring]
-                       [--recompute-dq]
+                       [--no-heads] [--recompute-dq]
 """
 from __future__ import annotations
 
@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-ring", action="store_true", help="skip the key-window ring-step timing")
+    ap.add_argument("--no-heads", action="store_true", help="skip the head-group (strided view) timing")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="dQ forms S, P and dP again instead of multiplying the stored dS")
     return ap.parse_args()
@@ -174,6 +175,58 @@ def ring_step_rates(cp, torch, w, q, k, v, do, bias, lay, flop, windows=8, reps=
     return out
 
 
+def head_group_rates(cp, torch, w, q, k, v, do, bias, lay, flop, groups=(16, 8, 4), reps=2):
+    """The step run as head-group calls on strided views (query heads [h0, h0 + Hg) and
+    their KV heads), one workspace sized for a group serving every group call.
+
+    The backward workspace grows with the heads of a call (the stored dS above all), so
+    a group call needs Hg / Hq of the full call's.  Timed separately from the main step
+    (not part of `value`)."""
+    G = w.hq // w.hkv
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.q_rows), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    err = cp.new_dev_err()
+
+    def ws_need(Hg):
+        pg = cp.problem(lay, w.q_rows, w.kv_rows, Hg, Hg // G, w.head_dim, w.causal, w.scale, w.bias_len,
+                        w.hq, w.hkv)
+        return max(cp.workspace_size(pg, cp.OP_BWD), cp.workspace_size(pg, cp.OP_BWD_DS))
+
+    groups = [g for g in groups if g < w.hq and w.hq % g == 0 and g % G == 0]
+    if not groups:
+        return None
+    ws = torch.empty(max(ws_need(g) for g in groups), dtype=torch.uint8, device="cuda")
+    out = {"full_call_workspace_bytes": max(cp.workspace_size(cp.problem(
+        lay, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal, w.scale, w.bias_len), op)
+        for op in (cp.OP_BWD, cp.OP_BWD_DS))}
+
+    def run(Hg):
+        for h0 in range(0, w.hq, Hg):
+            hs, gs = slice(h0, h0 + Hg), slice(h0 // G, (h0 + Hg) // G)
+            bv = None if bias is None else bias[hs]
+            cp.fwd(q[:, hs], k[:, gs], v[:, gs], lay, causal=w.causal, scale=w.scale, bias=bv, o=o[:, hs],
+                   lse=lse[hs], dev_err=err)
+            cp.bwd(q[:, hs], k[:, gs], v[:, gs], lay, o[:, hs], lse[hs], do[:, hs], causal=w.causal,
+                   scale=w.scale, bias=bv, dq=dq[:, hs], dk=dk[:, gs], dv=dv[:, gs], want_dbias=False, ws=ws,
+                   dev_err=err)
+
+    for Hg in groups:
+        run(Hg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run(Hg)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"H{Hg}"] = {"calls": w.hq // Hg, "ms_per_step": round(ms, 3),
+                         "tflops": round(flop / (ms * 1e-3) / 1e12, 2), "workspace_bytes": ws_need(Hg)}
+    cp.check(err)
+    return out
+
+
 def cpu_baseline(w, q, k, v, do, bias, budget_s):
     """The FP64 oracle, as it stands, on whole (sequence, KV-head group) samples."""
     import oracle
@@ -288,6 +341,9 @@ def main():
     ring = None if args.no_ring else ring_step_rates(
         cp, torch, w, q, k, v, do, bias, lay, visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq * 14 * w.head_dim)
 
+    heads = None if args.no_heads else head_group_rates(
+        cp, torch, w, q, k, v, do, bias, lay, visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq * 14 * w.head_dim)
+
     pairs = visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq
     D = w.head_dim
     flop = pairs * 14 * D
@@ -342,6 +398,7 @@ def main():
         "ds_bytes_per_step": ds_bytes if use_ds else 0,
         "layout_copy": copy,
         "ring_step": ring,
+        "head_groups": heads,
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

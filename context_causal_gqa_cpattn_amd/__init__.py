@@ -54,7 +54,8 @@ class Problem(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64),
         ("num_chunks", ctypes.c_int32), ("max_chunk_len", ctypes.c_int32),
         ("max_kv_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("bias_len", ctypes.c_int32),
+        ("bias_len", ctypes.c_int32), ("q_head_pitch", ctypes.c_int32),
+        ("kv_head_pitch", ctypes.c_int32),
     ]
 
 
@@ -131,16 +132,39 @@ def _stream(stream=None) -> Optional[int]:
     return s.cuda_stream
 
 
-def _need(t, name, dtype, shape=None):
-    torch = _torch()
+def _need(t, name, dtype, shape=None, pitch=None):
+    """Device, dtype and shape checks.  With `pitch`, t is [rows, heads, D] and may be a
+    head slice of a larger [rows, pitch, D] tensor (row stride pitch*D); else contiguous."""
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if pitch is None:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    elif head_pitch(t, name) != pitch:
+        raise ValueError(f"{name} has {head_pitch(t, name)} heads per row in memory, expected {pitch}")
+
+
+def head_pitch(t, name="tensor") -> int:
+    """Heads per row in memory of a [rows, heads, D] tensor or head slice of one."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [rows, heads, head_dim]")
+    rows, heads, D = t.shape
+    if t.stride(2) != 1 or (heads > 1 and t.stride(1) != D):
+        raise ValueError(f"{name} needs contiguous heads and head dims")
+    if rows <= 1:
+        return heads
+    if t.stride(0) % D or t.stride(0) // D < heads:
+        raise ValueError(f"{name} row stride {t.stride(0)} is not a whole number of heads >= {heads}")
+    return t.stride(0) // D
+
+
+def _like(t):
+    """A new tensor with t's shape and strides (a head slice's pitch is kept)."""
+    return _torch().empty_strided(tuple(t.shape), tuple(t.stride()), dtype=t.dtype, device=t.device)
 
 
 @dataclasses.dataclass
@@ -168,10 +192,12 @@ def make_layout(seq_offsets: Sequence[int], seq_lens: Sequence[int], chunks, dev
 
 
 def problem(layout: Layout, q_rows: int, kv_rows: int, hq: int, hkv: int, head_dim: int,
-            causal: bool = True, scale: Optional[float] = None, bias_len: int = 0) -> Problem:
+            causal: bool = True, scale: Optional[float] = None, bias_len: int = 0,
+            q_head_pitch: int = 0, kv_head_pitch: int = 0) -> Problem:
     return Problem(layout.num_seqs, hq, hkv, head_dim, q_rows, kv_rows, layout.num_chunks,
                    layout.max_chunk_len, layout.max_kv_len, 1 if causal else 0,
-                   (1.0 / math.sqrt(head_dim)) if scale is None else float(scale), bias_len)
+                   (1.0 / math.sqrt(head_dim)) if scale is None else float(scale), bias_len,
+                   q_head_pitch, kv_head_pitch)
 
 
 def new_dev_err(device="cuda"):
@@ -198,17 +224,20 @@ def _shapes(q, k, v):
 
 
 def _prob_for(q, k, v, layout, causal, scale, bias):
+    """The problem of q, k, v; each may be a head slice of a larger tensor (head pitch)."""
     torch = _torch()
     q_rows, hq, kv_rows, hkv, D = _shapes(q, k, v)
-    for n, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, n, torch.bfloat16)
+    qp, kvp = head_pitch(q, "q"), head_pitch(k, "k")
+    _need(q, "q", torch.bfloat16, pitch=qp)
+    _need(k, "k", torch.bfloat16, pitch=kvp)
+    _need(v, "v", torch.bfloat16, pitch=kvp)
     bias_len = 0
     if bias is not None:
         _need(bias, "bias", torch.float32)
         if bias.dim() != 3 or bias.shape[0] != hq or bias.shape[1] != bias.shape[2]:
             raise ValueError("bias must be [hq, bias_len, bias_len]")
         bias_len = int(bias.shape[1])
-    return problem(layout, q_rows, kv_rows, hq, hkv, D, causal, scale, bias_len)
+    return problem(layout, q_rows, kv_rows, hq, hkv, D, causal, scale, bias_len, qp, kvp)
 
 
 def validate(prob: Problem, layout: Layout, dev_err, stream=None):
@@ -224,10 +253,10 @@ def fwd(q, k, v, layout: Layout, causal: bool = True, scale: Optional[float] = N
     lib = load()
     prob = _prob_for(q, k, v, layout, causal, scale, bias)
     if o is None:
-        o = torch.empty_like(q)
+        o = _like(q)
     if lse is None:
         lse = torch.empty((prob.hq, prob.q_rows), dtype=torch.float32, device=q.device)
-    _need(o, "o", torch.bfloat16, q.shape)
+    _need(o, "o", torch.bfloat16, q.shape, prob.q_head_pitch)
     _need(lse, "lse", torch.float32, (prob.hq, prob.q_rows))
     if dev_err is None:
         dev_err = new_dev_err(q.device)
@@ -248,19 +277,20 @@ def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optiona
     torch = _torch()
     lib = load()
     prob = _prob_for(q, k, v, layout, causal, scale, bias)
-    _need(o, "o", torch.bfloat16, q.shape)
-    _need(do, "do", torch.bfloat16, q.shape)
+    _need(o, "o", torch.bfloat16, q.shape, prob.q_head_pitch)
+    _need(do, "do", torch.bfloat16, q.shape, prob.q_head_pitch)
     _need(lse, "lse", torch.float32, (prob.hq, prob.q_rows))
     if dq is None:
-        dq = torch.empty_like(q)
+        dq = _like(q)
     if dk is None:
         if dkv_accumulate:
             raise ValueError("dkv_accumulate needs existing dk/dv")
-        dk = torch.empty_like(k)
+        dk = _like(k)
     if dv is None:
-        dv = torch.empty_like(v)
-    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        _need(t, n, torch.bfloat16, ref.shape)
+        dv = _like(v)
+    for n, t, ref, pt in (("dq", dq, q, prob.q_head_pitch), ("dk", dk, k, prob.kv_head_pitch),
+                          ("dv", dv, v, prob.kv_head_pitch)):
+        _need(t, n, torch.bfloat16, ref.shape, pt)
     if bias is not None and want_dbias and dbias is None:
         dbias = torch.empty_like(bias)
     need = workspace_size(prob, OP_BWD)
@@ -287,10 +317,10 @@ def fwd_window(q, k, v, layout: Layout, kv_lo: int, kv_hi: int, causal: bool = T
     lib = load()
     prob = _prob_for(q, k, v, layout, causal, scale, bias)
     if o is None:
-        o = torch.empty_like(q)
+        o = _like(q)
     if lse is None:
         lse = torch.empty((prob.hq, prob.q_rows), dtype=torch.float32, device=q.device)
-    _need(o, "o", torch.bfloat16, q.shape)
+    _need(o, "o", torch.bfloat16, q.shape, prob.q_head_pitch)
     _need(lse, "lse", torch.float32, (prob.hq, prob.q_rows))
     if dev_err is None:
         dev_err = new_dev_err(q.device)
@@ -326,13 +356,13 @@ def bwd_window(q, k, v, layout: Layout, o, lse, do, kv_lo: int, kv_hi: int, caus
     if dq is None:
         if dq_accumulate:
             raise ValueError("dq_accumulate needs an existing dq")
-        dq = torch.empty_like(q)
+        dq = _like(q)
     if dk is None:
         if dkv_accumulate:
             raise ValueError("dkv_accumulate needs existing dk/dv")
-        dk = torch.empty_like(k)
+        dk = _like(k)
     if dv is None:
-        dv = torch.empty_like(v)
+        dv = _like(v)
     need = workspace_size(prob, OP_BWD)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

@@ -42,9 +42,26 @@ int hip_check(hipError_t e, const char* what) {
 
 struct Range {
   const char* name;
-  uintptr_t lo, hi;  // [lo, hi)
+  uintptr_t lo, hi;  // span [lo, hi)
   bool output;
+  int64_t pitch = 0;  // > 0: the bytes are rows of `row` bytes every `pitch` bytes
+  int64_t row = 0;
 };
+
+int64_t floor_div(int64_t x, int64_t y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
+
+// Whether two ranges share a byte.  Two row sets with one pitch (head slices of one
+// tensor) are tested exactly: rows i of A and j of B meet iff -row_b < d + (j - i) pitch
+// < row_a with d = lo_b - lo_a; any other pair is tested by its spans.
+bool overlaps(const Range& a, const Range& b) {
+  if (!(a.lo < b.hi && b.lo < a.hi)) return false;
+  if (a.pitch <= 0 || a.pitch != b.pitch) return true;
+  const int64_t P = a.pitch, d = (int64_t)(b.lo - a.lo);
+  const int64_t na = ((int64_t)(a.hi - a.lo) - a.row) / P + 1, nb = ((int64_t)(b.hi - b.lo) - b.row) / P + 1;
+  const int64_t m_lo = std::max(floor_div(-b.row - d, P) + 1, 1 - na);
+  const int64_t m_hi = std::min(-floor_div(d - a.row, P) - 1, nb - 1);
+  return m_lo <= m_hi;
+}
 
 // Every output range must be disjoint from every other range.
 int alias_audit(const std::vector<Range>& rs) {
@@ -53,7 +70,7 @@ int alias_audit(const std::vector<Range>& rs) {
     for (size_t j = 0; j < rs.size(); ++j) {
       if (i == j || rs[j].lo == rs[j].hi) continue;
       if (rs[j].output && j < i) continue;  // output pairs checked once
-      if (rs[i].lo < rs[j].hi && rs[j].lo < rs[i].hi)
+      if (overlaps(rs[i], rs[j]))
         return fail(CPATTN_EINVAL, "pointer alias: output %s overlaps %s %s", rs[i].name,
                     rs[j].output ? "output" : "input", rs[j].name);
     }
@@ -64,6 +81,14 @@ int alias_audit(const std::vector<Range>& rs) {
 Range rng(const char* name, const void* p, uint64_t bytes, bool out) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
   return Range{name, lo, p ? lo + bytes : lo, out};
+}
+
+// rows of `row` bytes every `pitch` bytes; `span` = bytes from the first to the last byte
+Range rng_rows(const char* name, const void* p, int64_t span, int64_t pitch, int64_t row, bool out) {
+  Range r = rng(name, p, span, out);
+  r.pitch = pitch;
+  r.row = row;
+  return r;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -77,8 +102,13 @@ int check_ptr(const void* p, uint64_t bytes, size_t align, const char* name) {
 
 constexpr int64_t kGridMax = 0x7fffffff;
 
+struct Plan;
+Range rq(const Plan& pl, const char* name, const void* p, bool out);
+Range rkv(const Plan& pl, const char* name, const void* p, bool out);
+
 struct Plan {
-  int D, G, hpw;
+  int D, G, hpw, hq, hkv;
+  int64_t qp, kvp;  // heads per row in memory (Q side, K/V side)
   bool bias;
   int64_t q_bytes, kv_bytes, stat_bytes, bias_bytes;
   int64_t delta_bytes;  // rounded to 256
@@ -95,6 +125,13 @@ struct Plan {
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Range rq(const Plan& pl, const char* name, const void* p, bool out) {
+  return rng_rows(name, p, pl.q_bytes, pl.qp * pl.D * 2, (int64_t)pl.hq * pl.D * 2, out);
+}
+Range rkv(const Plan& pl, const char* name, const void* p, bool out) {
+  return rng_rows(name, p, pl.kv_bytes, pl.kvp * pl.D * 2, (int64_t)pl.hkv * pl.D * 2, out);
+}
 
 int make_plan(const cpattn_problem* p, Plan& pl) {
   if (!p) return fail(CPATTN_EINVAL, "problem is NULL");
@@ -121,8 +158,19 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.D = D;
   pl.G = p->hq / p->hkv;
   pl.hpw = (pl.G % 4 == 0) ? 4 : (pl.G % 2 == 0) ? 2 : 1;
-  pl.q_bytes = p->q_rows * p->hq * (int64_t)D * 2;
-  pl.kv_bytes = p->kv_rows * p->hkv * (int64_t)D * 2;
+  if (p->q_head_pitch < 0 || (p->q_head_pitch > 0 && p->q_head_pitch < p->hq) || p->kv_head_pitch < 0 ||
+      (p->kv_head_pitch > 0 && p->kv_head_pitch < p->hkv))
+    return fail(CPATTN_EINVAL, "head pitches (%d, %d) below the head counts (%d, %d)", p->q_head_pitch,
+                p->kv_head_pitch, p->hq, p->hkv);
+  pl.hq = p->hq;
+  pl.hkv = p->hkv;
+  pl.qp = p->q_head_pitch > 0 ? p->q_head_pitch : p->hq;
+  pl.kvp = p->kv_head_pitch > 0 ? p->kv_head_pitch : p->hkv;
+  // a K/V tile's row offsets are 32-bit byte offsets (64 rows x 4096 heads x 512 B < 2^32)
+  if (pl.qp > 4096 || pl.kvp > 4096) return fail(CPATTN_EUNSUPPORTED, "more than 4096 heads per row");
+  // bytes from the first element of a Q-side (K/V-side) tensor to the end of its last head
+  pl.q_bytes = p->q_rows > 0 ? ((p->q_rows - 1) * pl.qp + p->hq) * (int64_t)D * 2 : 0;
+  pl.kv_bytes = p->kv_rows > 0 ? ((p->kv_rows - 1) * pl.kvp + p->hkv) * (int64_t)D * 2 : 0;
   pl.stat_bytes = (int64_t)p->hq * p->q_rows * 4;
   pl.bias_bytes = pl.bias ? (int64_t)p->hq * p->bias_len * p->bias_len * 4 : 0;
   pl.delta_bytes = round256(pl.stat_bytes);
@@ -190,6 +238,8 @@ AttnArgs base_args(const cpattn_problem* p, const Plan& pl) {
   a.parts = pl.parts;
   a.scale = p->scale;
   a.scale_log2 = p->scale * kLog2e;
+  a.q_pitch = pl.qp;
+  a.kv_pitch = pl.kvp;
   a.kv_lo = 0;
   a.kv_hi = INT_MAX;
   a.dq_accumulate = 0;
@@ -292,9 +342,9 @@ int fwd_impl(const cpattn_problem* p, const void* q, const void* k, const void* 
   if (!pl.bias && bias) return fail(CPATTN_EINVAL, "bias given but bias_len is 0");
   if (kv_lo < 0 || kv_hi < kv_lo) return fail(CPATTN_EINVAL, "key window [%d, %d) is invalid", kv_lo, kv_hi);
   if ((r = check_descriptors(p, seq_offsets, seq_lens, q_chunk_map, dev_err))) return r;
-  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false), rng("k", k, pl.kv_bytes, false),
-                           rng("v", v, pl.kv_bytes, false), rng("bias", bias, pl.bias_bytes, false),
-                           rng("o", o, pl.q_bytes, true), rng("lse", lse, pl.stat_bytes, true)};
+  std::vector<Range> rs = {rq(pl, "q", q, false), rkv(pl, "k", k, false),
+                           rkv(pl, "v", v, false), rng("bias", bias, pl.bias_bytes, false),
+                           rq(pl, "o", o, true), rng("lse", lse, pl.stat_bytes, true)};
   add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, true);
   if ((r = alias_audit(rs))) return r;
 
@@ -352,11 +402,11 @@ int cpattn_merge(const cpattn_problem* p, const int32_t* q_chunk_map, const void
     return r;
   // o may be o_a and lse may be lse_a (the running result updated in place); every other
   // overlap is rejected.
-  std::vector<Range> rs = {rng("o_b", o_b, pl.q_bytes, false), rng("lse_b", lse_b, pl.stat_bytes, false),
-                           rng("o", o, pl.q_bytes, true), rng("lse", lse, pl.stat_bytes, true),
+  std::vector<Range> rs = {rq(pl, "o_b", o_b, false), rng("lse_b", lse_b, pl.stat_bytes, false),
+                           rq(pl, "o", o, true), rng("lse", lse, pl.stat_bytes, true),
                            rng("q_chunk_map", q_chunk_map, (uint64_t)p->num_chunks * 16, false),
                            rng("dev_err", dev_err, 4, false)};
-  if (o_a != o) rs.push_back(rng("o_a", o_a, pl.q_bytes, false));
+  if (o_a != o) rs.push_back(rq(pl, "o_a", o_a, false));
   if (lse_a != lse) rs.push_back(rng("lse_a", lse_a, pl.stat_bytes, false));
   if ((r = alias_audit(rs))) return r;
   const int pairs_per_wg = kThreads / (pl.D / 8);
@@ -375,6 +425,7 @@ int cpattn_merge(const cpattn_problem* p, const int32_t* q_chunk_map, const void
   m.dev_err = dev_err;
   m.q_rows = p->q_rows;
   m.hq = p->hq;
+  m.q_pitch = pl.qp;
   m.D = pl.D;
   m.blocks_per_chunk = (int)bpc;
   return hip_check(launch_merge(m, dim3((unsigned)gx), (hipStream_t)stream), "merge launch");
@@ -501,11 +552,11 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
   if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
   if ((r = check_ptr(ws, need, 256, "ws"))) return r;
   const int64_t dbias_bytes = dbias ? pl.bias_bytes : 0;
-  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),        rng("k", k, pl.kv_bytes, false),
-                           rng("v", v, pl.kv_bytes, false),        rng("bias", bias, pl.bias_bytes, false),
-                           rng("o", o, pl.q_bytes, false),         rng("lse", lse, pl.stat_bytes, false),
-                           rng("dout", dout, pl.q_bytes, false),   rng("dq", dq, pl.q_bytes, true),
-                           rng("dk", dk, pl.kv_bytes, true),       rng("dv", dv, pl.kv_bytes, true),
+  std::vector<Range> rs = {rq(pl, "q", q, false),        rkv(pl, "k", k, false),
+                           rkv(pl, "v", v, false),        rng("bias", bias, pl.bias_bytes, false),
+                           rq(pl, "o", o, false),         rng("lse", lse, pl.stat_bytes, false),
+                           rq(pl, "dout", dout, false),   rq(pl, "dq", dq, true),
+                           rkv(pl, "dk", dk, true),       rkv(pl, "dv", dv, true),
                            rng("dbias", dbias, dbias_bytes, true), rng("ws", ws, need, true)};
   add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, true);
   if ((r = alias_audit(rs))) return r;
@@ -548,11 +599,11 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
   if ((int64_t)ws_bytes < pl.ws_core)
     return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)pl.ws_core);
   if ((r = check_ptr(ws, pl.ws_core, 256, "ws"))) return r;
-  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false),        rng("k", k, pl.kv_bytes, false),
-                           rng("v", v, pl.kv_bytes, false),        rng("bias", bias, pl.bias_bytes, false),
-                           rng("o", o, pl.q_bytes, false),         rng("lse", lse, pl.stat_bytes, false),
-                           rng("dout", dout, pl.q_bytes, false),   rng("dq", dq, pl.q_bytes, true),
-                           rng("dk", dk, pl.kv_bytes, true),       rng("dv", dv, pl.kv_bytes, true),
+  std::vector<Range> rs = {rq(pl, "q", q, false),        rkv(pl, "k", k, false),
+                           rkv(pl, "v", v, false),        rng("bias", bias, pl.bias_bytes, false),
+                           rq(pl, "o", o, false),         rng("lse", lse, pl.stat_bytes, false),
+                           rq(pl, "dout", dout, false),   rq(pl, "dq", dq, true),
+                           rkv(pl, "dk", dk, true),       rkv(pl, "dv", dv, true),
                            rng("ws", ws, pl.ws_core, prepass != 0)};
   add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, prepass != 0);
   if ((r = alias_audit(rs))) return r;
@@ -585,8 +636,8 @@ int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_
   if ((int64_t)ws_bytes < pl.ws_core)
     return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)pl.ws_core);
   if ((r = check_ptr(ws, pl.ws_core, 256, "ws"))) return r;
-  std::vector<Range> rs = {rng("q", q, pl.q_bytes, false), rng("o", o, pl.q_bytes, false),
-                           rng("dout", dout, pl.q_bytes, false),
+  std::vector<Range> rs = {rq(pl, "q", q, false), rq(pl, "o", o, false),
+                           rq(pl, "dout", dout, false),
                            rng("q_chunk_map", q_chunk_map, (uint64_t)p->num_chunks * 16, false),
                            rng("dev_err", dev_err, 4, false), rng("ws", ws, pl.ws_core, true)};
   if ((r = alias_audit(rs))) return r;
@@ -603,9 +654,9 @@ int step_checks(const cpattn_problem* p, const Plan& pl, const void* q, const vo
   if ((r = bwd_common_checks(p, pl, q, k, v, bias, lse, dout, so, sl, cm, dev_err))) return r;
   if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
   if ((r = check_ptr(ws, need, 256, "ws"))) return r;
-  rs = {rng("q", q, pl.q_bytes, false),       rng("k", k, pl.kv_bytes, false),
-        rng("v", v, pl.kv_bytes, false),       rng("bias", bias, pl.bias_bytes, false),
-        rng("lse", lse, pl.stat_bytes, false), rng("dout", dout, pl.q_bytes, false),
+  rs = {rq(pl, "q", q, false),       rkv(pl, "k", k, false),
+        rkv(pl, "v", v, false),       rng("bias", bias, pl.bias_bytes, false),
+        rng("lse", lse, pl.stat_bytes, false), rq(pl, "dout", dout, false),
         rng("ws (pre-pass results)", ws, pl.ws_core, false)};
   add_descriptor_ranges(rs, p, so, sl, cm, dev_err, false);
   return CPATTN_OK;
@@ -627,8 +678,8 @@ int cpattn_bwd_dkdv(const cpattn_problem* p, const void* q, const void* k, const
     return r;
   if ((r = check_ptr(dk, pl.kv_bytes, 16, "dk")) || (r = check_ptr(dv, pl.kv_bytes, 16, "dv"))) return r;
   if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
-  rs.push_back(rng("dk", dk, pl.kv_bytes, true));
-  rs.push_back(rng("dv", dv, pl.kv_bytes, true));
+  rs.push_back(rkv(pl, "dk", dk, true));
+  rs.push_back(rkv(pl, "dv", dv, true));
   if ((r = alias_audit(rs))) return r;
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   return enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, (hipStream_t)stream);
@@ -648,7 +699,7 @@ int cpattn_bwd_dq(const cpattn_problem* p, const void* q, const void* k, const v
                        ws_bytes, pl.ws_core, dev_err, rs)))
     return r;
   if ((r = check_ptr(dq, pl.q_bytes, 16, "dq"))) return r;
-  rs.push_back(rng("dq", dq, pl.q_bytes, true));
+  rs.push_back(rq(pl, "dq", dq, true));
   if ((r = alias_audit(rs))) return r;
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   return enqueue_dq(p, pl, a, dq, (hipStream_t)stream);
@@ -670,8 +721,8 @@ int cpattn_bwd_dkdv_ds(const cpattn_problem* p, const void* q, const void* k, co
     return r;
   if ((r = check_ptr(dk, pl.kv_bytes, 16, "dk")) || (r = check_ptr(dv, pl.kv_bytes, 16, "dv"))) return r;
   if (dkv_accumulate != 0 && dkv_accumulate != 1) return fail(CPATTN_EINVAL, "dkv_accumulate must be 0 or 1");
-  rs.push_back(rng("dk", dk, pl.kv_bytes, true));
-  rs.push_back(rng("dv", dv, pl.kv_bytes, true));
+  rs.push_back(rkv(pl, "dk", dk, true));
+  rs.push_back(rkv(pl, "dv", dv, true));
   rs.push_back(rng("ws (dS area)", (char*)ws + pl.off_ds, pl.ds_bytes, true));
   if ((r = alias_audit(rs))) return r;
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
@@ -691,9 +742,9 @@ int cpattn_bwd_dq_ds(const cpattn_problem* p, const void* k, const int32_t* seq_
   const int64_t need = pl.off_ds + pl.ds_bytes;
   if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
   if ((r = check_ptr(ws, need, 256, "ws"))) return r;
-  std::vector<Range> rs = {rng("k", k, pl.kv_bytes, false),
+  std::vector<Range> rs = {rkv(pl, "k", k, false),
                            rng("ws (dS area)", (const char*)ws + pl.off_ds, pl.ds_bytes, false),
-                           rng("dq", dq, pl.q_bytes, true)};
+                           rq(pl, "dq", dq, true)};
   add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
   if ((r = alias_audit(rs))) return r;
   AttnArgs a = base_args(p, pl);

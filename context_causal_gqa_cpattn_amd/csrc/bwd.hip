@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(const AttnArgs a) {
   const int qg = task / DG, dg = task % DG;  // qg: output granule; dg varies fastest
   // the 8 queries of output granule qg, in stored order
   const int qbase = (qg >> 1) * 16, qsub = (qg & 1) * 8;
-  const int64_t rs = (int64_t)a.hq * D;
+  const int64_t rs = a.q_pitch * D;
   const int64_t off = ((int64_t)ch.q_row + r0) * rs + (int64_t)h * D + dg * 8;
   const uint16_t* src = (tensor ? a.dout : a.q) + off;
   u32x4 rows[8], cols[8];

@@ -352,6 +352,8 @@ struct AttnArgs {
   uint16_t* ds_out;      // dK/dV: where to store dS blocks (null: not stored)
   const uint16_t* ds;    // dQ from stored dS: the dS blocks
   int64_t kb_max;        // 32-key blocks per (query tile slot, head) in the dS store
+  int64_t q_pitch;       // heads per row in memory: Q, O, dO, dQ
+  int64_t kv_pitch;      // heads per row in memory: K, V, dK, dV
   int kv_lo, kv_hi;      // key window [kv_lo, kv_hi) in sequence positions (0, INT_MAX: all)
   int dq_accumulate;     // dQ (recompute path): 0 store, 1 add to the existing values
   const int32_t* seq_offsets;

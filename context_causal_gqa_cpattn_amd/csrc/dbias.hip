@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(const AttnArgs a) {
       }
   }
   f32x16 acc[2] = {f32x16{}, f32x16{}};
-  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const int64_t kv_stride = a.kv_pitch * D;
 
   if (wpos0 < BL) {
     for (int c = c_begin; c < c_end; ++c) {
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(const AttnArgs a) {
       const bool qok = qpos >= ch.pos0 && qpos < ch.pos0 + ch.len;
       const int64_t qrow = (int64_t)ch.q_row + (qpos - ch.pos0);
       u32x4 qf[NST], dof[NST];
-      const int64_t qoff = (qrow * a.hq + h) * D + kg * 8;
+      const int64_t qoff = (qrow * a.q_pitch + h) * D + kg * 8;
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         qf[st] = qok ? ld16(a.q + qoff + st * 16) : u32x4{0u, 0u, 0u, 0u};

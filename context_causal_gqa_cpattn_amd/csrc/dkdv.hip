@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
 
   // K and V as B operands: lane (hl, n) holds key n, dimensions 16 st + 8 hl + [0, 8).
   // Lanes past the sequence end load its last key (finite values; their P and dS are 0).
-  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const int64_t kv_stride = a.kv_pitch * D;
   u32x4 kf[NS], vf[NS];
   {
     const int64_t off = (koff + min(key, L - 1)) * kv_stride + (int64_t)g * D + hl * 8;

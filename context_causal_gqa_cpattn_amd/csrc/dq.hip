@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   // Q^T and dO^T as B operands: lane (g, q) holds query q, dimensions 32 st + 8 g + [0, 8).
   u32x4 qf[NST], dof[NST];
   {
-    const int64_t off = (qrow * a.hq + h) * D + g * 8;
+    const int64_t off = (qrow * a.q_pitch + h) * D + g * 8;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       qf[st] = qok ? ld16(a.q + off + st * 32) : u32x4{0u, 0u, 0u, 0u};
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   for (int db = 0; db < NDB; ++db) dqt[db] = f32x4{};
   const KtOffsets<D> kto(lane);
 
-  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const int64_t kv_stride = a.kv_pitch * D;
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)kvh * D;
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)kvh * D;
 
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   if (!qok) return;
   // element j of block db is dimension 16 db + 4 g + j; with dq_accumulate the existing
   // BF16 value is added in fp32 and the sum rounded once (a key window's contribution)
-  uint16_t* op = a.dq + (qrow * a.hq + h) * D + g * 4;
+  uint16_t* op = a.dq + (qrow * a.q_pitch + h) * D + g * 4;
   if (a.dq_accumulate) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
       dsrc[i] = a.ds + ((int64_t)tile_slot(c, ch.q_row, r / 32) * a.hq + h) * a.kb_max * kBlkElems;
   }
 
-  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const int64_t kv_stride = a.kv_pitch * D;
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)kvh * D;
   // Copy instruction p (0 <= p < PER) of this wave for step kb into stage kb % kStages:
   // the K tile (rows past L repeat the last key), then the slot's dS blocks (with two
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   for (int i = 0; i < 2; ++i) {
     const bool ok = col < nq[i];
     const int64_t qrow = (int64_t)ch.q_row + row0 + 32 * i + (ok ? col : 0);
-    uint16_t* op = a.dq + (qrow * a.hq + h) * D + part * NDB * 32 + (lane >> 5) * 4;
+    uint16_t* op = a.dq + (qrow * a.q_pitch + h) * D + part * NDB * 32 + (lane >> 5) * 4;
 #pragma unroll
     for (int j = 0; j < NDB; ++j)
 #pragma unroll

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   // Q^T as B operand: lane holds query `col`, dims [16*st + 8*kg, +8).
   u32x4 qf[NST];
   {
-    const uint16_t* qp = a.q + ((int64_t)(ch.q_row + row0 + col) * a.hq + h) * D + kg * 8;
+    const uint16_t* qp = a.q + ((int64_t)(ch.q_row + row0 + col) * a.q_pitch + h) * D + kg * 8;
 #pragma unroll
     for (int st = 0; st < NST; ++st)
       qf[st] = (col < nrows) ? ld16(qp + st * 16) : u32x4{0u, 0u, 0u, 0u};
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   const float* bias_row = nullptr;
   if (BIAS) bias_row = a.bias + ((int64_t)h * a.bias_len + min(qpos, a.bias_len - 1)) * a.bias_len;
 
-  const int64_t kv_stride = (int64_t)a.hkv * D;
+  const int64_t kv_stride = a.kv_pitch * D;
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)g * D;
 
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   // A row with no visible key in the window: O = 0 and LSE = -inf (merges as nothing).
   const float l = l_run + xor32(l_run);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* op = a.o_out + ((int64_t)(ch.q_row + row0 + col) * a.hq + h) * D + kg * 4;
+  uint16_t* op = a.o_out + ((int64_t)(ch.q_row + row0 + col) * a.q_pitch + h) * D + kg * 4;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -38,6 +38,7 @@ struct MergeArgs {
   const int32_t* chunks;
   const int32_t* dev_err;
   int64_t q_rows;
+  int64_t q_pitch;      // heads per row in memory
   int hq, D, blocks_per_chunk;
 };
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);

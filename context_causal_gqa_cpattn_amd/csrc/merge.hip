@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
   const int64_t si = (int64_t)h * a.q_rows + row;
   const float la = a.lse_a[si], lb = a.lse_b[si];
   const float m = fmaxf(la, lb);
-  const int64_t off = (row * a.hq + h) * a.D + (threadIdx.x % per_pair) * 8;
+  const int64_t off = (row * a.q_pitch + h) * a.D + (threadIdx.x % per_pair) * 8;
   const u32x4 va = ld16(a.o_a + off), vb = ld16(a.o_b + off);
   float wa = 0.f, wb = 0.f, lse = -INFINITY;
   if (m > -INFINITY) {

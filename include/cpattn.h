@@ -97,7 +97,16 @@ typedef struct cpattn_problem {
   float scale;           /* score scale, usually 1/sqrt(head_dim) */
   int32_t bias_len;      /* 0: no bias; else bias is fp32 [hq, bias_len, bias_len]
                             indexed [h, query position, key position]; needs causal = 0 */
+  int32_t q_head_pitch;  /* heads per row in the memory of Q, O, dO, dQ (0: hq); >= hq */
+  int32_t kv_head_pitch; /* heads per row in the memory of K, V, dK, dV (0: hkv); >= hkv */
 } cpattn_problem;
+/* Head pitches let one call cover a group of heads of larger tensors in place ("First-
+ * gradient buffer reuse" / head partitioning: H16/H8 head-group calls on strided
+ * views that reuse one workspace): pass pointers to the group's first query head and
+ * first KV head, hq/hkv the group's head counts, and the full tensors' heads per row
+ * as the pitches.  Row r, head h of Q is then at q + (r * q_head_pitch + h) * D.  LSE
+ * and Delta stay [hq, q_rows] per call (a head slice of a larger LSE is contiguous);
+ * the workspace scales with the call's hq. */
 
 #define CPATTN_OP_FWD 0
 #define CPATTN_OP_BWD 1

@@ -239,3 +239,49 @@ def test_window_and_merge_host_checks():
     assert "workspace" in _err()
     assert lib.cpattn_bwd_window(*ba, 0, 8, 1, dk + 64, 0, dk, dv, 0, ws, core, err, None) == cp.EINVAL
     assert "alias" in _err()
+
+
+def test_head_pitch_bounds():
+    assert _fwd(_prob(q_head_pitch=4)) == cp.EINVAL and "pitch" in _err()
+    assert _fwd(_prob(kv_head_pitch=1)) == cp.EINVAL and "pitch" in _err()
+    assert _fwd(_prob(q_head_pitch=-1)) == cp.EINVAL
+    assert _fwd(_prob(q_head_pitch=4097)) == cp.EUNSUPPORTED and "4096" in _err()
+    # a head slice's span: rows 0..q_rows-1 at pitch 16 heads end 8 heads into the last row
+    hd = 128 * 2
+    span = (63 * 16 + 8) * hd
+    assert _fwd(_prob(q_head_pitch=16), o=A + span - 16) == cp.EINVAL and "alias" in _err()
+
+
+def _bwd_alias_msg(prob, q, k, v, dq, dk, dv):
+    """The alias error of a backward call whose workspace overlaps seq_offsets on purpose
+    (so the call never gets past its host checks): it names the first overlapping
+    output in the order dq, dk, dv, ws."""
+    lib = cp.load()
+    need = lib.cpattn_workspace_size(ctypes.byref(prob), cp.OP_BWD)
+    so, sl, cm = A + (3 << 24), A + (3 << 24) + 256, A + (3 << 24) + 512
+    o, lse, do, err = A + (4 << 24), A + (5 << 24), A + (8 << 24), A + (6 << 24)
+    r = lib.cpattn_bwd(ctypes.byref(prob), q, k, v, so, sl, cm, None, o, lse, do, dq, dk, dv, None, 0, so,
+                       need, err, None)
+    assert r == cp.EINVAL
+    return _err()
+
+
+def test_alias_audit_is_exact_for_head_slices_of_one_tensor():
+    hd = 128 * 2
+    p = _prob(q_head_pitch=16, kv_head_pitch=4)
+    q, k = A, A + (1 << 24)
+    dk, dv = A + (9 << 24), A + (10 << 24)
+    last = "output ws overlaps input seq_offsets"
+    # dQ as the other 8 heads of Q's 16-head tensor shares no byte with Q
+    for dq in (q + 8 * hd, q + 24 * hd):
+        msg = _bwd_alias_msg(p, q, k, k + 2 * hd, dq, dk, dv)
+        assert last in msg, msg
+    # interleaved slices that do share heads or rows are found
+    for dq in (q + 4 * hd, q + 16 * hd, q + 31 * hd):
+        msg = _bwd_alias_msg(p, q, k, k + 2 * hd, dq, dk, dv)
+        assert "output dq overlaps input q" in msg, msg
+    # K and V as the two halves of one packed [rows, 2 hkv, D] tensor, and dK, dV the same
+    msg = _bwd_alias_msg(p, q, k, k + 2 * hd, A + (11 << 24), dk, dk + 2 * hd)
+    assert last in msg, msg
+    msg = _bwd_alias_msg(p, q, k, k + 2 * hd, A + (11 << 24), dk, dk + 1 * hd)
+    assert "output dk overlaps output dv" in msg, msg
