@@ -194,14 +194,17 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.parts = 1;
   pl.partial_bytes = 0;
   if (pl.bias) {
-    const int64_t tiles = cdiv(p->bias_len, kDbiasKeys) * cdiv(p->bias_len, kDbiasPos) * p->hq;
-    int64_t parts = cdiv(2048, tiles);
-    parts = std::max<int64_t>(1, std::min<int64_t>({parts, 16, std::max(1, p->num_chunks)}));
-    if ((int64_t)p->hq * parts > 65535) parts = std::max<int64_t>(1, 65535 / p->hq);
+    // The rows are reduced in `parts` units of consecutive chunks, each unit's partial
+    // summed in chunk order and the units' partials added in unit order.  The unit
+    // count depends on the bias size and the chunk count only, never on the heads of
+    // the call, so head-group calls and the call over all heads give the same bits.
+    const int64_t tiles_per_head = cdiv(p->bias_len, kDbiasKeys) * cdiv(p->bias_len, kDbiasPos);
+    const int64_t parts = std::max<int64_t>(
+        1, std::min<int64_t>({cdiv(512, tiles_per_head), 16, std::max(1, p->num_chunks)}));
     pl.parts = (int)parts;
     if (pl.parts > 1) pl.partial_bytes = round256((int64_t)pl.parts * pl.bias_bytes);
-    pl.grid_dbias = dim3((unsigned)cdiv(p->bias_len, kDbiasKeys), (unsigned)cdiv(p->bias_len, kDbiasPos),
-                         (unsigned)(p->hq * pl.parts));
+    pl.grid_dbias = dim3((unsigned)(cdiv(p->bias_len, kDbiasKeys) * pl.parts),
+                         (unsigned)cdiv(p->bias_len, kDbiasPos), (unsigned)p->hq);
   }
   // Transposed 32-query tiles: at most ceil(q_rows/32) + C of them.
   const int64_t max_tiles = cdiv(p->q_rows, kPrepassRows) + p->num_chunks;

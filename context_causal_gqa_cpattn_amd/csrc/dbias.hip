@@ -6,9 +6,10 @@
 // the pair tensor, so its gradient is a reduction over rows.
 //
 // A workgroup owns a 128-position x 64-key tile of one head's dBias and walks one
-// partition of the chunk list, keeping the tile's partial sum in registers; the
-// partitions' partial tiles are summed by a second kernel in a fixed order, so the
-// result does not depend on scheduling.
+// unit (a fixed range of consecutive chunks) of the chunk list in order, keeping the
+// tile's partial sum in registers; a second kernel adds the units' partial tiles in
+// unit order.  The unit count depends on the bias size and the chunk count only, so
+// the result depends neither on scheduling nor on how the heads are split over calls.
 #include "common.h"
 #include "launch.h"
 
@@ -21,10 +22,11 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 5, col = lane & 31;
   const int BL = a.bias_len;
-  const int key0 = blockIdx.x * kDbiasKeys;
+  const int key_tiles = (BL + kDbiasKeys - 1) / kDbiasKeys;
+  const int key0 = (blockIdx.x % key_tiles) * kDbiasKeys;
+  const int part = blockIdx.x / key_tiles;
   const int wpos0 = blockIdx.y * kDbiasPos + wave * 32;
-  const int h = blockIdx.z % a.hq;
-  const int part = blockIdx.z / a.hq;
+  const int h = blockIdx.z;
   const int per = (a.num_chunks + a.parts - 1) / a.parts;
   const int c_begin = part * per, c_end = min(a.num_chunks, c_begin + per);
   const int g = h / a.group;
