@@ -6,3 +6,4 @@ this package.  It shares no code with the HIP library or its binding.
 from .softmax_attention import attention, block_terms, visible_pairs  # noqa: F401
 from . import layout  # noqa: F401
 from . import window  # noqa: F401
+from . import a2a  # noqa: F401

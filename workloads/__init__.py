@@ -335,3 +335,49 @@ def draw_on_device(w: Workload, seed: int, device="cuda", poison_padding: bool =
             if bool(m.any()):
                 t[m] = float("nan")
     return q, k, v, do, bias
+
+
+def a2a_rank_maps(seq_lens, cp: int, pad_rows: int = 0):
+    """Chunk maps of the load-balanced rank shares of an all-to-all (A2A) swap.
+
+    Every sequence is cut into 2 cp chunks, chunk k covering positions
+    [floor(k L / 2cp), floor((k + 1) L / 2cp)); rank r holds chunks r and
+    2cp - 1 - r of every sequence, packed back to back in sequence order from row 0
+    of its block.  Returns (maps, rows_per_rank): maps[r] is int32 [2 B, 4] of
+    {seq, q_row, pos0, len} and rows_per_rank the longest rank's row count plus
+    `pad_rows` (every block of the exchange has that many rows)."""
+    lens = np.asarray(seq_lens, np.int64)
+    n = 2 * cp
+    maps, most = [], 0
+    for r in range(cp):
+        rows, q = [], 0
+        for b, L in enumerate(lens):
+            for k in (r, n - 1 - r):
+                p0, p1 = (k * L) // n, ((k + 1) * L) // n
+                rows.append((b, q, p0, p1 - p0))
+                q += p1 - p0
+        maps.append(np.asarray(rows, np.int32).reshape(-1, 4))
+        most = max(most, q)
+    return maps, most + pad_rows
+
+
+def make_a2a(lens, H: int, D: int, cp: int, seed: int, kv_pitch=None, pad_rows: int = 0,
+             pad_block_rows: int = 0):
+    """A sequence-ordered THD tensor [rows, H, D] (BF16 bits, NaN padding) and the A2A
+    rank maps over it: dict(full, seq_offsets, seq_lens, maps, rows_per_rank)."""
+    lens = np.asarray(lens, np.int32)
+    B = len(lens)
+    if kv_pitch is None:
+        off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+        rows = int(lens.sum()) + pad_rows
+    else:
+        off = (np.arange(B) * kv_pitch).astype(np.int32)
+        rows = B * kv_pitch + pad_rows
+    rng = np.random.Generator(np.random.PCG64(seed))
+    full = draw_bf16(rng, (rows, H, D))
+    valid = np.zeros(rows, bool)
+    for o, L in zip(off, lens):
+        valid[o:o + L] = True
+    full[~valid] = BF16_NAN
+    maps, rpr = a2a_rank_maps(lens, cp, pad_block_rows)
+    return dict(full=full, seq_offsets=off, seq_lens=lens, maps=maps, rows_per_rank=rpr, valid=valid)
