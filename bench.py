@@ -13,7 +13,7 @@ stream it runs on; `cpu_baseline` times the FP64 oracle on a bounded sample of
 the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu] [--no-ring]
-                       [--no-heads] [--recompute-dq]
+                       [--no-heads] [--no-a2a] [--recompute-dq]
 """
 from __future__ import annotations
 
@@ -58,6 +58,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-ring", action="store_true", help="skip the key-window ring-step timing")
     ap.add_argument("--no-heads", action="store_true", help="skip the head-group (strided view) timing")
+    ap.add_argument("--no-a2a", action="store_true", help="skip the A2A swap-copy timing")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="dQ forms S, P and dP again instead of multiplying the stored dS")
     return ap.parse_args()
@@ -115,6 +116,54 @@ def layout_copy_rates(cp, torch, reps=10):
         out[name + "_ms"] = round(ms, 4)
     cp.check(err)
     out["bytes_per_call"] = 2 * x.numel() * 2
+    return out
+
+
+def a2a_copy_rates(cp, torch, reps=10):
+    """The A2A swap copies of one rank at CP4, B64/S8192/Hq32/Hkv8/D128 (the pages' CP4/A2A
+    coordinate): Q [131072, 32, 128] and K [131072, 8, 128] split into 4 head groups, the
+    4 received blocks scattered into whole sequences [524288, Hc, 128], and O gathered
+    and merged back.  GB/s counts the bytes read plus written."""
+    import workloads as W
+    B, S, Hq, Hkv, D, n = 64, 8192, 32, 8, 128, 4
+    lens = np.full(B, S, np.int32)
+    maps, rpr = W.a2a_rank_maps(lens, n)
+    lay = cp.make_a2a_layout(maps, (np.arange(B) * S).astype(np.int32), lens)
+    err = cp.new_dev_err()
+    q = torch.empty((rpr, Hq, D), dtype=torch.bfloat16, device="cuda").normal_()
+    k = torch.empty((rpr, Hkv, D), dtype=torch.bfloat16, device="cuda").normal_()
+    q_send = torch.empty((n, rpr, Hq // n, D), dtype=torch.bfloat16, device="cuda")
+    k_send = torch.empty((n, rpr, Hkv // n, D), dtype=torch.bfloat16, device="cuda")
+    q_full = torch.empty((B * S, Hq // n, D), dtype=torch.bfloat16, device="cuda")
+    k_full = torch.empty((B * S, Hkv // n, D), dtype=torch.bfloat16, device="cuda")
+    o_back = torch.empty_like(q)
+    ops = {
+        "split_heads_q": (lambda: cp.a2a_split_heads(q, n, dst=q_send), q.numel()),
+        "split_heads_kv": (lambda: cp.a2a_split_heads(k, n, dst=k_send), k.numel()),
+        "scatter_rows_q": (lambda: cp.a2a_scatter_rows(q_send, lay, B * S, full=q_full, dev_err=err), q.numel()),
+        "scatter_rows_kv": (lambda: cp.a2a_scatter_rows(k_send, lay, B * S, full=k_full, dev_err=err),
+                            k.numel()),
+        "gather_rows_o": (lambda: cp.a2a_gather_rows(q_full, lay, rpr, blocks=q_send, dev_err=err), q.numel()),
+        "merge_heads_o": (lambda: cp.a2a_merge_heads(q_send, dst=o_back), q.numel()),
+        "torch_split_heads_q": (lambda: q_send.copy_(q.view(rpr, n, Hq // n, D).transpose(0, 1)), q.numel()),
+    }
+    out = {"workload": "cp4_a2a_rank_share_b64_s8192_hq32_hkv8_d128"}
+    for name, (fn, elems) in ops.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "gbs": round(2 * elems * 2 / (ms * 1e-3) / 1e9, 1)}
+    cp.check(err)
+    # one forward's copies: Q, K, V in (split + scatter each), O out (gather + merge)
+    out["forward_swap_ms"] = round(sum(out[k]["ms"] for k in ("split_heads_q", "scatter_rows_q",
+                                                               "gather_rows_o", "merge_heads_o"))
+                                   + 2 * (out["split_heads_kv"]["ms"] + out["scatter_rows_kv"]["ms"]), 4)
     return out
 
 
@@ -338,6 +387,7 @@ def main():
     ms = wall * 1e3 / args.steps
 
     copy = layout_copy_rates(cp, torch)
+    a2a = None if args.no_a2a else a2a_copy_rates(cp, torch)
     ring = None if args.no_ring else ring_step_rates(
         cp, torch, w, q, k, v, do, bias, lay, visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq * 14 * w.head_dim)
 
@@ -397,6 +447,7 @@ def main():
         "dq_path": "stored dS" if use_ds else "recompute",
         "ds_bytes_per_step": ds_bytes if use_ds else 0,
         "layout_copy": copy,
+        "a2a_copy": a2a,
         "ring_step": ring,
         "head_groups": heads,
         "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),

@@ -32,6 +32,8 @@ EXPORTS = [
     "cpattn_validate", "cpattn_fwd", "cpattn_bwd", "cpattn_bwd_prepass", "cpattn_bwd_dkdv",
     "cpattn_bwd_dq", "cpattn_bwd_dbias", "cpattn_bwd_dkdv_ds", "cpattn_bwd_dq_ds", "cpattn_pack",
     "cpattn_unpack", "cpattn_fwd_window", "cpattn_merge", "cpattn_bwd_window",
+    "cpattn_a2a_split_heads", "cpattn_a2a_merge_heads", "cpattn_a2a_scatter_rows",
+    "cpattn_a2a_gather_rows",
 ]
 
 
@@ -56,6 +58,15 @@ class Problem(ctypes.Structure):
         ("max_kv_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
         ("bias_len", ctypes.c_int32), ("q_head_pitch", ctypes.c_int32),
         ("kv_head_pitch", ctypes.c_int32),
+    ]
+
+
+class A2aRows(ctypes.Structure):
+    """Sizes of an A2A row copy (cpattn_a2a_rows)."""
+    _fields_ = [
+        ("cp", ctypes.c_int32), ("chunks_per_rank", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("max_chunk_len", ctypes.c_int32), ("rows_per_rank", ctypes.c_int64), ("full_rows", ctypes.c_int64),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
     ]
 
 
@@ -100,6 +111,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                               _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, sz, _vp, _vp],
         "cpattn_pack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
         "cpattn_unpack": [_vp, _vp, i32, i32, i32, i32, i64, _vp, _vp, _vp, _vp],
+        "cpattn_a2a_split_heads": [_vp, _vp, i64, i32, i32, i32, _vp],
+        "cpattn_a2a_merge_heads": [_vp, _vp, i64, i32, i32, i32, _vp],
+        "cpattn_a2a_scatter_rows": [ctypes.POINTER(A2aRows), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+        "cpattn_a2a_gather_rows": [ctypes.POINTER(A2aRows), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -455,6 +470,104 @@ def unpack(thd, seq_offsets, seq_lens, B: int, S_pitch: int, bhsd=None, dev_err=
     _check(lib.cpattn_unpack(_ptr(thd), _ptr(bhsd), B, H, S_pitch, D, thd_rows, _ptr(seq_offsets),
                              _ptr(seq_lens), _ptr(dev_err), _stream(stream)))
     return bhsd, dev_err
+
+
+# ---------------------------------------------------------------- A2A swap copies
+
+def a2a_split_heads(src, cp: int, dst=None, stream=None):
+    """[rows, H, D] -> [cp, rows, H / cp, D]: block j holds heads [j H/cp, (j+1) H/cp)."""
+    torch = _torch()
+    _need(src, "src", torch.bfloat16)
+    rows, H, D = src.shape
+    if H % cp:
+        raise ValueError(f"H ({H}) is not a multiple of cp ({cp})")
+    if dst is None:
+        dst = torch.empty((cp, rows, H // cp, D), dtype=torch.bfloat16, device=src.device)
+    _need(dst, "dst", torch.bfloat16, (cp, rows, H // cp, D))
+    _check(load().cpattn_a2a_split_heads(_ptr(src), _ptr(dst), rows, H, D, cp, _stream(stream)))
+    return dst
+
+
+def a2a_merge_heads(src, dst=None, stream=None):
+    """[cp, rows, Hc, D] -> [rows, cp Hc, D]: the inverse of a2a_split_heads."""
+    torch = _torch()
+    _need(src, "src", torch.bfloat16)
+    cp, rows, Hc, D = src.shape
+    if dst is None:
+        dst = torch.empty((rows, cp * Hc, D), dtype=torch.bfloat16, device=src.device)
+    _need(dst, "dst", torch.bfloat16, (rows, cp * Hc, D))
+    _check(load().cpattn_a2a_merge_heads(_ptr(src), _ptr(dst), rows, cp * Hc, D, cp, _stream(stream)))
+    return dst
+
+
+@dataclasses.dataclass
+class A2aLayout:
+    """Rank maps and sequence descriptors of an A2A swap on the device, with host bounds."""
+    rank_maps: object     # int32 [cp, chunks_per_rank, 4] {seq, q_row, pos0, len}
+    seq_offsets: object   # int32 [B]: row of position 0 in the sequence-ordered tensor
+    seq_lens: object      # int32 [B]
+    cp: int
+    chunks_per_rank: int
+    num_seqs: int
+    max_chunk_len: int
+
+
+def make_a2a_layout(rank_maps, seq_offsets, seq_lens, device="cuda") -> A2aLayout:
+    """rank_maps: one [C_r, 4] array per rank; shorter maps are padded with len = 0."""
+    torch = _torch()
+    maps = [np.asarray(m, np.int32).reshape(-1, 4) for m in rank_maps]
+    C = max((len(m) for m in maps), default=0)
+    arr = np.zeros((len(maps), C, 4), np.int32)
+    for r, m in enumerate(maps):
+        arr[r, :len(m)] = m
+    mcl = int(arr[..., 3].max()) if arr.size else 0
+    so = np.ascontiguousarray(seq_offsets, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    return A2aLayout(torch.from_numpy(arr).to(device), torch.from_numpy(so).to(device),
+                     torch.from_numpy(sl).to(device), len(maps), C, len(so), max(mcl, 0))
+
+
+def _a2a_rows(lay: A2aLayout, rows_per_rank: int, full_rows: int, heads: int, D: int) -> A2aRows:
+    return A2aRows(lay.cp, lay.chunks_per_rank, lay.num_seqs, lay.max_chunk_len, rows_per_rank,
+                   full_rows, heads, D)
+
+
+def a2a_scatter_rows(blocks, lay: A2aLayout, full_rows: int, full=None, dev_err=None, stream=None):
+    """Blocks [cp, rows_per_rank, Hc, D] received from every rank -> the sequence-ordered
+    [full_rows, Hc, D] tensor; rows no chunk names keep their contents."""
+    torch = _torch()
+    _need(blocks, "blocks", torch.bfloat16)
+    cp, rpr, Hc, D = blocks.shape
+    if cp != lay.cp:
+        raise ValueError(f"blocks hold {cp} ranks, the layout {lay.cp}")
+    if full is None:
+        full = torch.empty((full_rows, Hc, D), dtype=torch.bfloat16, device=blocks.device)
+    _need(full, "full", torch.bfloat16, (full_rows, Hc, D))
+    if dev_err is None:
+        dev_err = new_dev_err(blocks.device)
+    p = _a2a_rows(lay, rpr, full_rows, Hc, D)
+    _check(load().cpattn_a2a_scatter_rows(ctypes.byref(p), _ptr(blocks), _ptr(full), _ptr(lay.rank_maps),
+                                          _ptr(lay.seq_offsets), _ptr(lay.seq_lens), _ptr(dev_err),
+                                          _stream(stream)))
+    return full, dev_err
+
+
+def a2a_gather_rows(full, lay: A2aLayout, rows_per_rank: int, blocks=None, dev_err=None, stream=None):
+    """The sequence-ordered [full_rows, Hc, D] tensor -> blocks [cp, rows_per_rank, Hc, D],
+    block s holding rank s's rows; rows no chunk names keep their contents."""
+    torch = _torch()
+    _need(full, "full", torch.bfloat16)
+    full_rows, Hc, D = full.shape
+    if blocks is None:
+        blocks = torch.empty((lay.cp, rows_per_rank, Hc, D), dtype=torch.bfloat16, device=full.device)
+    _need(blocks, "blocks", torch.bfloat16, (lay.cp, rows_per_rank, Hc, D))
+    if dev_err is None:
+        dev_err = new_dev_err(full.device)
+    p = _a2a_rows(lay, rows_per_rank, full_rows, Hc, D)
+    _check(load().cpattn_a2a_gather_rows(ctypes.byref(p), _ptr(full), _ptr(blocks), _ptr(lay.rank_maps),
+                                         _ptr(lay.seq_offsets), _ptr(lay.seq_lens), _ptr(dev_err),
+                                         _stream(stream)))
+    return blocks, dev_err
 
 
 # ---------------------------------------------------------------- host <-> device helpers

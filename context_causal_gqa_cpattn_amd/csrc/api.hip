@@ -832,4 +832,107 @@ int cpattn_unpack(const void* thd, void* bhsd, int32_t B, int32_t H, int32_t S_p
                      (hipStream_t)stream, 1);
 }
 
+// ---------------------------------------------------------------- A2A swap copies
+
+static int a2a_heads_call(const void* src, void* dst, int64_t rows, int32_t H, int32_t D, int32_t cp,
+                          hipStream_t s, int merge) {
+  g_last_error.clear();
+  if (rows < 0 || H <= 0 || D <= 0 || cp <= 0) return fail(CPATTN_EINVAL, "bad A2A head-copy sizes");
+  if (H % cp) return fail(CPATTN_EINVAL, "H (%d) is not a multiple of cp (%d)", H, cp);
+  if (D % 8) return fail(CPATTN_EUNSUPPORTED, "D must be a multiple of 8 for the A2A copies");
+  if (cp > 65535) return fail(CPATTN_EUNSUPPORTED, "cp above 65535");
+  if ((int64_t)H * D > (1 << 24)) return fail(CPATTN_EUNSUPPORTED, "rows above 2^24 elements");
+  const int64_t bytes = rows * H * (int64_t)D * 2;
+  int r;
+  if ((r = check_ptr(src, bytes, 16, "src")) || (r = check_ptr(dst, bytes, 16, "dst"))) return r;
+  std::vector<Range> rs = {rng("src", src, bytes, false), rng("dst", dst, bytes, true)};
+  if ((r = alias_audit(rs))) return r;
+  A2aHeadsArgs a{};
+  a.src = (const uint16_t*)src;
+  a.dst = (uint16_t*)dst;
+  a.rows = rows;
+  a.H = H;
+  a.D = D;
+  a.cp = cp;
+  a.merge = merge;
+  const int seg = H / cp * D / 8;  // 16-byte pieces of one row's head group
+  a.rows_per_wg = std::max(1, kThreads * 4 / seg);
+  if ((rows + a.rows_per_wg - 1) / a.rows_per_wg > kGridMax) return fail(CPATTN_EUNSUPPORTED, "too many rows");
+  return hip_check(launch_a2a_heads(a, s), "A2A head-copy launch");
+}
+
+int cpattn_a2a_split_heads(const void* src, void* dst, int64_t rows, int32_t H, int32_t D, int32_t cp,
+                           cpattn_stream_t stream) {
+  return a2a_heads_call(src, dst, rows, H, D, cp, (hipStream_t)stream, 0);
+}
+
+int cpattn_a2a_merge_heads(const void* src, void* dst, int64_t rows, int32_t H, int32_t D, int32_t cp,
+                           cpattn_stream_t stream) {
+  return a2a_heads_call(src, dst, rows, H, D, cp, (hipStream_t)stream, 1);
+}
+
+static int a2a_rows_call(const cpattn_a2a_rows* p, const void* src, void* dst, const int32_t* maps,
+                         const int32_t* so, const int32_t* sl, int32_t* dev_err, hipStream_t s,
+                         int gather) {
+  g_last_error.clear();
+  if (!p) return fail(CPATTN_EINVAL, "A2A row sizes are NULL");
+  if (p->cp <= 0 || p->chunks_per_rank < 0 || p->num_seqs < 0 || p->max_chunk_len < 0 ||
+      p->rows_per_rank < 0 || p->full_rows < 0 || p->heads <= 0 || p->head_dim <= 0)
+    return fail(CPATTN_EINVAL, "bad A2A row-copy sizes");
+  if (p->head_dim % 8) return fail(CPATTN_EUNSUPPORTED, "D must be a multiple of 8 for the A2A copies");
+  if ((int64_t)p->heads * p->head_dim > (1 << 24) || p->max_chunk_len > (1 << 30))
+    return fail(CPATTN_EUNSUPPORTED, "A2A row copy too large");
+  const int64_t row_bytes = (int64_t)p->heads * p->head_dim * 2;
+  const int64_t blk_bytes = (int64_t)p->cp * p->rows_per_rank * row_bytes;
+  const int64_t full_bytes = p->full_rows * row_bytes;
+  const int64_t n_chunks = (int64_t)p->cp * p->chunks_per_rank;
+  if (n_chunks > (1 << 24)) return fail(CPATTN_EUNSUPPORTED, "more than 2^24 chunks");
+  const int64_t seg = row_bytes / 16;
+  const int64_t wg_per_chunk = std::max<int64_t>(1, (p->max_chunk_len * seg + kThreads * 4 - 1) / (kThreads * 4));
+  if (wg_per_chunk * n_chunks > kGridMax) return fail(CPATTN_EUNSUPPORTED, "A2A row copy grid too large");
+  const int64_t src_bytes = gather ? full_bytes : blk_bytes, dst_bytes = gather ? blk_bytes : full_bytes;
+  int r;
+  if ((r = check_ptr(src, src_bytes, 16, "src")) || (r = check_ptr(dst, dst_bytes, 16, "dst")) ||
+      (r = check_ptr(maps, (uint64_t)n_chunks * 16, 16, "rank_maps")) ||
+      (r = check_ptr(so, (uint64_t)p->num_seqs * 4, 4, "seq_offsets")) ||
+      (r = check_ptr(sl, (uint64_t)p->num_seqs * 4, 4, "seq_lens")) || (r = check_ptr(dev_err, 4, 4, "dev_err")))
+    return r;
+  std::vector<Range> rs = {rng("src", src, src_bytes, false), rng("dst", dst, dst_bytes, true),
+                           rng("rank_maps", maps, (uint64_t)n_chunks * 16, false),
+                           rng("seq_offsets", so, (uint64_t)p->num_seqs * 4, false),
+                           rng("seq_lens", sl, (uint64_t)p->num_seqs * 4, false),
+                           rng("dev_err", dev_err, 4, true)};
+  if ((r = alias_audit(rs))) return r;
+  A2aRowsArgs a{};
+  a.src = (const uint16_t*)src;
+  a.dst = (uint16_t*)dst;
+  a.maps = maps;
+  a.seq_offsets = so;
+  a.seq_lens = sl;
+  a.dev_err = dev_err;
+  a.full_rows = p->full_rows;
+  a.rows_per_rank = p->rows_per_rank;
+  a.cp = p->cp;
+  a.chunks_per_rank = p->chunks_per_rank;
+  a.num_seqs = p->num_seqs;
+  a.max_chunk_len = p->max_chunk_len;
+  a.heads = p->heads;
+  a.D = p->head_dim;
+  a.gather = gather;
+  a.wg_per_chunk = (int)wg_per_chunk;
+  return hip_check(launch_a2a_rows(a, s), "A2A row-copy launch");
+}
+
+int cpattn_a2a_scatter_rows(const cpattn_a2a_rows* p, const void* blocks, void* full,
+                            const int32_t* rank_maps, const int32_t* seq_offsets,
+                            const int32_t* seq_lens, int32_t* dev_err, cpattn_stream_t stream) {
+  return a2a_rows_call(p, blocks, full, rank_maps, seq_offsets, seq_lens, dev_err, (hipStream_t)stream, 0);
+}
+
+int cpattn_a2a_gather_rows(const cpattn_a2a_rows* p, const void* full, void* blocks,
+                           const int32_t* rank_maps, const int32_t* seq_offsets,
+                           const int32_t* seq_lens, int32_t* dev_err, cpattn_stream_t stream) {
+  return a2a_rows_call(p, full, blocks, rank_maps, seq_offsets, seq_lens, dev_err, (hipStream_t)stream, 1);
+}
+
 }  // extern "C"

@@ -41,6 +41,33 @@ struct MergeArgs {
   int64_t q_pitch;      // heads per row in memory
   int hq, D, blocks_per_chunk;
 };
+// Head-group copies of the A2A swap: [rows, H, D] <-> [cp, rows, H / cp, D].
+struct A2aHeadsArgs {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t rows;
+  int H, D, cp;
+  int merge;        // 0: rows -> blocks (split), 1: blocks -> rows (merge)
+  int rows_per_wg;
+};
+
+// Row copies of the A2A swap between [cp, rows_per_rank, heads, D] blocks and the
+// sequence-ordered [full_rows, heads, D] tensor, driven by per-rank chunk maps.
+struct A2aRowsArgs {
+  const uint16_t* src;   // blocks (scatter) or the full tensor (gather)
+  uint16_t* dst;         // the full tensor (scatter) or blocks (gather)
+  const int32_t* maps;   // [cp][chunks_per_rank][4] {seq, q_row, pos0, len}
+  const int32_t* seq_offsets;
+  const int32_t* seq_lens;
+  int32_t* dev_err;
+  int64_t full_rows, rows_per_rank;
+  int cp, chunks_per_rank, num_seqs, max_chunk_len, heads, D;
+  int gather;            // 0: blocks -> full (scatter), 1: full -> blocks (gather)
+  int wg_per_chunk;
+};
+
+hipError_t launch_a2a_heads(const A2aHeadsArgs& a, hipStream_t s);
+hipError_t launch_a2a_rows(const A2aRowsArgs& a, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);

@@ -277,6 +277,56 @@ int cpattn_unpack(const void* thd, void* bhsd, int32_t B, int32_t H, int32_t S_p
                   int64_t thd_rows, const int32_t* seq_offsets, const int32_t* seq_lens,
                   int32_t* dev_err, cpattn_stream_t stream);
 
+/* Copies around the all-to-all (A2A) head <-> sequence swap of context parallelism
+ * (page "Optimize context parallel attention layouts and gradient accumulation",
+ * "Changes": BF16 A2A pack/unpack copies inside the swap; "Validation and
+ * performance": the CP4/A2A run they sped up).  Rank r of cp ranks holds the rows of
+ * its chunks of every sequence with all H heads; the swap gives every rank whole
+ * sequences of Hc = H / cp heads.  Before attention: split_heads, the exchange (block
+ * j to rank j), scatter_rows.  After attention: gather_rows, the exchange,
+ * merge_heads.  The exchange itself (an RCCL all-to-all) is not part of this library.
+ * All tensors are BF16 with the head dim innermost; D must be a multiple of 8 and
+ * every tensor pointer 16-byte aligned.  Source and destination must not overlap. */
+
+/* split_heads: dst[j, t, h, :] = src[t, j*Hc + h, :], src [rows, H, D] -> dst
+ * [cp, rows, Hc, D] (block j is contiguous: the send buffer for rank j).
+ * merge_heads is the inverse, src [cp, rows, Hc, D] -> dst [rows, H, D].  Every row is
+ * copied.  H must be a multiple of cp; cp <= 65535.  No device promise is involved. */
+int cpattn_a2a_split_heads(const void* src, void* dst, int64_t rows, int32_t H, int32_t D, int32_t cp,
+                           cpattn_stream_t stream);
+int cpattn_a2a_merge_heads(const void* src, void* dst, int64_t rows, int32_t H, int32_t D, int32_t cp,
+                           cpattn_stream_t stream);
+
+/* Sizes of a row copy between the exchange's blocks and the sequence-ordered tensor. */
+typedef struct {
+  int32_t cp;              /* ranks: blocks of the exchange                           */
+  int32_t chunks_per_rank; /* entries per rank map (unused entries: len = 0)         */
+  int32_t num_seqs;
+  int32_t max_chunk_len;   /* bound on every len (checked on the device)             */
+  int64_t rows_per_rank;   /* rows of each block                                     */
+  int64_t full_rows;       /* rows of the sequence-ordered tensor                    */
+  int32_t heads;           /* heads per row on both sides (Hc)                       */
+  int32_t head_dim;
+} cpattn_a2a_rows;
+
+/* scatter_rows: blocks [cp, rows_per_rank, heads, D] -> full [full_rows, heads, D].
+ * rank_maps is int32 [cp][chunks_per_rank][4] of {seq, q_row, pos0, len} in device
+ * memory: chunk {seq, q_row, pos0, len} of rank s moves rows [q_row, q_row + len) of
+ * block s to rows seq_offsets[seq] + pos0 + [0, len) of full.  gather_rows is the
+ * inverse (full -> blocks).  Rows no chunk names keep their contents.  Checked on the
+ * device (*dev_err overwritten; nothing copied on a violation): seq in range
+ * (CPATTN_DEV_ECHUNK_SEQ), 0 <= len <= max_chunk_len and [pos0, pos0 + len) inside
+ * [0, seq_lens[seq]) (CPATTN_DEV_ECHUNK_POS), [q_row, q_row + len) inside the block
+ * (CPATTN_DEV_ECHUNK_ROWS), seq_lens >= 0 (CPATTN_DEV_ESEQ_LEN) and every sequence
+ * inside [0, full_rows) (CPATTN_DEV_ESEQ_RANGE).  Chunks may come in any order; two
+ * chunks naming the same destination row leave that row with either one's data. */
+int cpattn_a2a_scatter_rows(const cpattn_a2a_rows* p, const void* blocks, void* full,
+                            const int32_t* rank_maps, const int32_t* seq_offsets,
+                            const int32_t* seq_lens, int32_t* dev_err, cpattn_stream_t stream);
+int cpattn_a2a_gather_rows(const cpattn_a2a_rows* p, const void* full, void* blocks,
+                           const int32_t* rank_maps, const int32_t* seq_offsets,
+                           const int32_t* seq_lens, int32_t* dev_err, cpattn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

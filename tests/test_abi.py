@@ -285,3 +285,28 @@ def test_alias_audit_is_exact_for_head_slices_of_one_tensor():
     assert last in msg, msg
     msg = _bwd_alias_msg(p, q, k, k + 2 * hd, A + (11 << 24), dk, dk + 1 * hd)
     assert "output dk overlaps output dv" in msg, msg
+
+
+def test_a2a_copy_host_checks():
+    lib = cp.load()
+    src, dst = A, A + (1 << 24)
+    assert lib.cpattn_a2a_split_heads(src, dst, 64, 6, 128, 4, None) == cp.EINVAL and "multiple" in _err()
+    assert lib.cpattn_a2a_split_heads(src, dst, 64, 8, 100, 4, None) == cp.EUNSUPPORTED
+    assert lib.cpattn_a2a_split_heads(src, src + 4096, 64, 8, 128, 4, None) == cp.EINVAL and "alias" in _err()
+    assert lib.cpattn_a2a_merge_heads(None, dst, 64, 8, 128, 4, None) == cp.EINVAL and "NULL" in _err()
+    assert lib.cpattn_a2a_merge_heads(src + 8, dst, 64, 8, 128, 4, None) == cp.EINVAL and "aligned" in _err()
+    assert lib.cpattn_a2a_split_heads(src, dst, -1, 8, 128, 4, None) == cp.EINVAL
+    p = cp.A2aRows(cp=4, chunks_per_rank=2, num_seqs=1, max_chunk_len=8, rows_per_rank=16, full_rows=64,
+                   heads=2, head_dim=128)
+    maps, so, sl, err = A + (2 << 24), A + (3 << 24), A + (3 << 24) + 256, A + (6 << 24)
+    f = lib.cpattn_a2a_scatter_rows
+    assert f(ctypes.byref(p), src, src + 4096, maps, so, sl, err, None) == cp.EINVAL and "alias" in _err()
+    assert f(ctypes.byref(p), src, dst, maps + 4, so, sl, err, None) == cp.EINVAL and "rank_maps" in _err()
+    assert f(ctypes.byref(p), src, dst, maps, so, sl, maps + 16, None) == cp.EINVAL and "alias" in _err()
+    assert f(ctypes.byref(p), src, dst, maps, so, sl, None, None) == cp.EINVAL
+    assert f(None, src, dst, maps, so, sl, err, None) == cp.EINVAL
+    bad = cp.A2aRows(cp=4, chunks_per_rank=2, num_seqs=1, max_chunk_len=8, rows_per_rank=16, full_rows=64,
+                     heads=2, head_dim=12)
+    assert f(ctypes.byref(bad), src, dst, maps, so, sl, err, None) == cp.EUNSUPPORTED
+    bad.head_dim, bad.rows_per_rank = 128, -1
+    assert lib.cpattn_a2a_gather_rows(ctypes.byref(bad), src, dst, maps, so, sl, err, None) == cp.EINVAL
