@@ -122,6 +122,24 @@ __device__ __forceinline__ void softmax_part(f32x16& s, f32x16& dp, int r0, cons
 
 }  // namespace
 
+// S and dP products in arch VGPRs.  At D = 256 the dK^T/dV^T accumulators fill all 256
+// accumulation registers, and the compiler places every MFMA result there, so S and dP
+// would displace one dK/dV block per step (96 register moves).  Inline assembly pins
+// their destinations to VGPRs.  A chain accumulates into the same registers (no wait
+// states needed between dependent products of one shape); sdp_fence covers the wait
+// states before VALU reads the results (at least 11 for an 8-pass product; 20 given).
+__device__ __forceinline__ f32x16 mfma32_v0(u32x4 a, u32x4 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma32_v(f32x16& c, u32x4 a, u32x4 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void sdp_fence(f32x16& s, f32x16& dp) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s), "+v"(dp));
+}
+
 template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   constexpr int NS = D / 16;       // 16-deep k-steps of S and dP
@@ -291,14 +309,25 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
           nq_ = tr_a(qtt, st + 1);
           nd_ = tr_a(dtt, st + 1);
         }
-        s = mfma32(fq, kf[st], s);
-        dp = mfma32(fd, vf[st], dp);
+        if (D == 256) {
+          if (st == 0) {
+            s = mfma32_v0(fq, kf[st]);
+            dp = mfma32_v0(fd, vf[st]);
+          } else {
+            mfma32_v(s, fq, kf[st]);
+            mfma32_v(dp, fd, vf[st]);
+          }
+        } else {
+          s = mfma32(fq, kf[st], s);
+          dp = mfma32(fd, vf[st], dp);
+        }
         fq = nq_;
         fd = nd_;
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
+    if (D == 256) sdp_fence(s, dp);
     // Softmax of this tile, between the dV/dK products of the previous one.
     const float* lse = lds_lse[buf];
     const float* dl = lds_dl[buf];
