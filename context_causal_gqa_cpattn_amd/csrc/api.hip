@@ -213,6 +213,8 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.off_dot = pl.off_qt + round256(tile_bytes);
   pl.off_partials = pl.off_dot + round256(tile_bytes);
   pl.ws_core = pl.off_partials;
+  // the pre-pass numbers its workgroups linearly (head fastest)
+  if (gx_pre * p->hq > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_prepass = dim3((unsigned)gx_pre, (unsigned)p->hq);
   // Stored dS: 2 KB per (tile slot, head, 32-key block), every slot sized for the longest
   // sequence.
