@@ -81,6 +81,18 @@ __device__ __forceinline__ float log2f_fast(float x) { return __builtin_amdgcn_l
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Max and sum over the two 32-lane halves of a wave (lanes l and l ^ 32), by one
+// v_permlane32_swap (a VALU lane swap; no LDS round trip): swapping the upper half of
+// one copy with the lower half of another leaves [lo, lo] and [hi, hi].
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define CPATTN_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 

@@ -29,7 +29,9 @@ constexpr int kBN = 64;  // keys per KV tile
 
 // Scores of one 64-key tile in base 2 (+ bias), masked when MASK (keys outside
 // [lo, hi), and past the query position when causal); returns the lane max (four
-// independent running maxima, so the chain is a quarter as long).
+// independent running maxima, so the chain is a quarter as long).  Without a bias the
+// scores stay unscaled (the positive scale is applied to the max and inside the
+// exponential's FMA); with one they are scaled and biased here.
 // Element r of block kb is key key0 + 32 kb + 8 (r/4) + 4 kg + r%4.
 template <bool BIAS, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float* bias_row, int key0,
@@ -52,8 +54,8 @@ __device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float*
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float x = s[kb][i * 4 + j] * c;
-        if (BIAS) x = fmaf(bv[j], kLog2e, x);
+        float x = s[kb][i * 4 + j];
+        if (BIAS) x = fmaf(bv[j], kLog2e, x * c);
         if (MASK) {
           const int key = kbi + j;
           x = ((key >= lo) && (key < hi) && (!CAUSAL || key <= qpos)) ? x : -INFINITY;
@@ -112,6 +114,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int st = 0; st < NST; ++st)
       qf[st] = (col < nrows) ? ld16(qp + st * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Without a bias the scale is folded in after the max (max(c s) = c max(s) for c > 0)
+  // and into the FMA before each exponential; a negative scale is applied as |c| with Q
+  // negated (exact in BF16), a zero one as a tiny positive one (every score 0 either way).
+  const float c_eff = BIAS ? a.scale_log2 : fmaxf(fabsf(a.scale_log2), 1e-30f);
+  if (!BIAS && a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) qf[st] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
   }
 
   f32x16 oacc[NDB];
@@ -215,7 +226,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
         scale_tile<BIAS, false, CAUSAL>(s, a.scale_log2, bias_row, key0, L, kv_lo, kv_hi, qpos, kg,
                                         a.bias_len, mx);
       }
-      mx = fmaxf(mx, xor32(mx));
+      mx = halves_max(mx);
+      if (!BIAS) mx *= c_eff;
       // Lazy rescale: move the reference max only when it grows by more than 8 (x256).
       if (__builtin_expect(__any(mx > m_run + 8.f), 0)) {
         // A real branch: the rescale must not be if-converted into every tile.
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f_fast(s[kb][r] - m_use);
+          const float p = BIAS ? exp2f_fast(s[kb][r] - m_use) : exp2f_fast(fmaf(s[kb][r], c_eff, -m_use));
           s[kb][r] = p;
           rs[r & 3] += p;
         }
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 
   if (col >= nrows) return;
   // A row with no visible key in the window: O = 0 and LSE = -inf (merges as nothing).
-  const float l = l_run + xor32(l_run);
+  const float l = halves_sum(l_run);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   uint16_t* op = a.o_out + ((int64_t)(ch.q_row + row0 + col) * a.q_pitch + h) * D + kg * 4;
 #pragma unroll

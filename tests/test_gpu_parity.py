@@ -75,6 +75,15 @@ def test_small_sweep_full(gpu_lib, idx, path):
     _run_and_compare(gpu_lib, w, label=f"sweep{idx} {path} ", bar="pages", store_ds=PATHS[path])
 
 
+@pytest.mark.parametrize("scale,D", [(-0.0625, 256), (-0.1, 128), (0.0, 256), (0.05, 128)])
+def test_scale_sign_and_zero(gpu_lib, scale, D):
+    """Any finite scale: the forward folds a positive scale in after the row max, takes a
+    negative one as |scale| with Q negated, and a zero one as uniform weights."""
+    w = W.make_custom(lens=[150, 97], hq=4, hkv=2, head_dim=D, causal=True, chunks=[(0, 0, 40), (0, 110, 40),
+                      (1, 0, 97)], seed=71, scale=scale, pad_kv_rows=3, pad_q_rows=2)
+    _run_and_compare(gpu_lib, w, label=f"scale {scale} D{D} ", bar="pages")
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 def test_bias_small_full(gpu_lib, D):
     lens = [70, 70, 70]
