@@ -120,6 +120,21 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return pid < per * 8 ? (pid & 7) * per + (pid >> 3) : pid;
 }
 
+// Logical work item (group * per_group + item) of physical block pid, for a launch of
+// n_groups groups of per_group items, where a group's items share their inputs through
+// L2 (the query blocks of one chunk and head group, the key tiles of one sequence and KV
+// head).  With n_groups a multiple of 8, XCD x takes groups x, x + 8, x + 16, ..., each
+// group's items consecutively: groups are numbered with the head fastest, so every XCD
+// gets its heads of every sequence and the same share of work however unequal the
+// sequences are.  Otherwise each XCD takes a contiguous range (xcd_remap).
+__device__ __forceinline__ int xcd_group_order(int pid, int n_groups, int per_group) {
+  if ((n_groups & 7) == 0) {
+    const int x = pid & 7, j = pid >> 3;
+    return (x + 8 * (j / per_group)) * per_group + j % per_group;
+  }
+  return xcd_remap(pid, n_groups * per_group);
+}
+
 // LDS tiles [rows][D] of BF16 are written by LDS DMA (1 KB contiguous per wave
 // instruction, so rows are unpadded) and read two ways: 16-byte row reads (A operands
 // whose contracted index runs along D) and transposing 8-byte reads (A operands whose
