@@ -123,12 +123,14 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
 // Logical work item (group * per_group + item) of physical block pid, for a launch of
 // n_groups groups of per_group items, where a group's items share their inputs through
 // L2 (the query blocks of one chunk and head group, the key tiles of one sequence and KV
-// head).  With n_groups a multiple of 8, XCD x takes groups x, x + 8, x + 16, ..., each
-// group's items consecutively: groups are numbered with the head fastest, so every XCD
-// gets its heads of every sequence and the same share of work however unequal the
-// sequences are.  Otherwise each XCD takes a contiguous range (xcd_remap).
-__device__ __forceinline__ int xcd_group_order(int pid, int n_groups, int per_group) {
-  if ((n_groups & 7) == 0) {
+// head).  Groups are numbered with the head index fastest, over n_heads heads.  With
+// n_heads a multiple of 8, XCD x takes the groups of heads x, x + 8, ... of every chunk or
+// sequence, each group's items consecutively, so every XCD gets the same share of work
+// however unequal the sequences are.  Otherwise (dealing by group index would then
+// follow the chunk order, e.g. put every short chunk on half the XCDs) each XCD takes a
+// contiguous range (xcd_remap).
+__device__ __forceinline__ int xcd_group_order(int pid, int n_groups, int per_group, int n_heads) {
+  if ((n_heads & 7) == 0) {
     const int x = pid & 7, j = pid >> 3;
     return (x + 8 * (j / per_group)) * per_group + j % per_group;
   }

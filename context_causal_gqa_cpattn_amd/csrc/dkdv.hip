@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, n = lane & 31;
-  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.kv_tiles, a.kv_tiles);
+  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.kv_tiles, a.kv_tiles, a.hkv);
   const int kt = logical % a.kv_tiles;
   const int rest = logical / a.kv_tiles;
   const int g = rest % a.hkv;

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, q = lane & 15;  // lane group, query within the wave
-  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk);
+  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk, a.hq / a.hpw);
   const int n_hg = a.hq / a.hpw;
   const int pb = logical % a.blocks_per_chunk;
   const int rest = logical / a.blocks_per_chunk;

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = wave / kSplit, part = wave % kSplit;
-  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk);
+  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk, a.hq / a.hpw);
   const int n_hg = a.hq / a.hpw;
   const int pb = logical % a.blocks_per_chunk;
   const int rest = logical / a.blocks_per_chunk;

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 5, col = lane & 31;
 
-  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk);
+  const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk, a.hq / a.hpw);
   const int n_hg = a.hq / a.hpw;
   const int pb = logical % a.blocks_per_chunk;
   const int rest = logical / a.blocks_per_chunk;
