@@ -312,7 +312,7 @@ def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optiona
     if store_ds is not False and ws is None:
         need = max(need, workspace_size(prob, OP_BWD_DS))
         if store_ds and need == workspace_size(prob, OP_BWD):
-            raise ValueError("the stored-dS backward needs head_dim >= 64")
+            raise ValueError("the stored-dS backward needs head_dim >= 32")
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if dev_err is None:

@@ -116,7 +116,7 @@ struct Plan {
   int64_t partial_bytes;
   // backward workspace: delta | Q^T tiles | dO^T tiles | dBias partials | dS blocks
   int64_t off_qt, off_dot, off_partials, ws_core;
-  bool ds_ok;            // the stored-dS backward applies (head_dim >= 64)
+  bool ds_ok;            // the stored-dS backward applies (every supported head_dim, 32 to 256)
   int64_t kb_max;        // 32-key blocks per (tile slot, head) in the dS store
   int64_t off_ds, ds_bytes;
   dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias, grid_dqds;
@@ -218,7 +218,7 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.grid_prepass = dim3((unsigned)gx_pre, (unsigned)p->hq);
   // Stored dS: 2 KB per (tile slot, head, 32-key block), every slot sized for the longest
   // sequence.
-  pl.ds_ok = D >= 64;
+  pl.ds_ok = D >= 32;
   pl.kb_max = cdiv(p->max_kv_len, kDsBlockKeys);
   pl.off_ds = pl.ws_core + pl.partial_bytes;
   pl.ds_bytes = pl.ds_ok ? round256(max_tiles * p->hq * pl.kb_max * kDsBlockKeys * kPrepassRows * 2) : 0;
@@ -720,7 +720,7 @@ int cpattn_bwd_dkdv_ds(const cpattn_problem* p, const void* q, const void* k, co
   int r;
   std::vector<Range> rs;
   if ((r = make_plan(p, pl))) return r;
-  if (!pl.ds_ok) return fail(CPATTN_EUNSUPPORTED, "the stored-dS backward needs head_dim >= 64");
+  if (!pl.ds_ok) return fail(CPATTN_EUNSUPPORTED, "the stored-dS backward needs head_dim >= 32");
   if ((r = step_checks(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws,
                        ws_bytes, pl.off_ds + pl.ds_bytes, dev_err, rs)))
     return r;
@@ -741,7 +741,7 @@ int cpattn_bwd_dq_ds(const cpattn_problem* p, const void* k, const int32_t* seq_
   Plan pl;
   int r;
   if ((r = make_plan(p, pl))) return r;
-  if (!pl.ds_ok) return fail(CPATTN_EUNSUPPORTED, "the stored-dS backward needs head_dim >= 64");
+  if (!pl.ds_ok) return fail(CPATTN_EUNSUPPORTED, "the stored-dS backward needs head_dim >= 32");
   if ((r = check_ptr(k, pl.kv_bytes, 16, "k")) || (r = check_ptr(dq, pl.q_bytes, 16, "dq"))) return r;
   if ((r = check_descriptors(p, seq_offsets, seq_lens, q_chunk_map, dev_err))) return r;
   const int64_t need = pl.off_ds + pl.ds_bytes;

@@ -17,7 +17,7 @@
 // Workgroup = (chunk, block of positions, hpw query heads that share one KV head) with
 // four slots of (head, two 32-query tiles).  For D >= 128 two waves share a slot, each
 // keeping half of dQ^T (D/2 x 64 queries, fp32) in registers, two waves per SIMD (one
-// wave's copies and LDS reads issue while the other's MFMAs run); for D = 64 one wave
+// wave's copies and LDS reads issue while the other's MFMAs run); for D <= 64 one wave
 // per slot.  Each 32-key step, the K tile (32 x D, kind-0 swizzle) and the slots' dS
 // blocks are copied into LDS three steps ahead (four stages: the dS stream comes from
 // HBM); the copy instructions are spread between the step's MFMAs rather than issued
@@ -38,7 +38,7 @@ constexpr int kBlkElems = 32 * 32;    // BF16 elements of a dS block
 constexpr int kSlots = 4;             // (head, two-tile) slots per workgroup
 
 // Waves per workgroup: each slot's D columns are split over kSplit waves, two waves per
-// SIMD for D >= 128 (128 accumulation registers each), one for D = 64.
+// SIMD for D >= 128 (128 accumulation registers each), one for D <= 64.
 template <int D>
 struct DsCfg {
   static constexpr int kSplit = D >= 128 ? 2 : 1;
@@ -74,9 +74,13 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   constexpr int kSplit = DsCfg<D>::kSplit;
   constexpr int kWaves = DsCfg<D>::kWaves;
   constexpr int NDB = D / 32 / kSplit;                 // 32-row blocks of dQ^T per wave
-  constexpr int KI = kBlk * D * 2 / 1024 / kWaves;     // K-tile copy instructions per wave
+  // K-tile copy instructions (1 KB each) per tile and per wave.  At D = 32 the 2 KB tile is
+  // two instructions for four waves: waves w and w + 2 copy the same kilobyte (identical
+  // bytes to the same place), so that every wave issues the same number of copies.
+  constexpr int KTI = kBlk * D * 2 / 1024;
+  constexpr int KI = KTI >= kWaves ? KTI / kWaves : 1;
   constexpr int PER = KI + 4 / kSplit;                 // copy instructions per wave per step
-  static_assert(KI >= 1 && (kBlk * D * 2 / 1024) % kWaves == 0, "K tile split evenly over the waves");
+  static_assert(KTI % kWaves == 0 || kWaves % KTI == 0, "K tile split evenly over the waves");
   static_assert(2 * PER < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k[kStages][kBlk * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_s[kStages][kSlots * 2 * kBlkElems];
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
     const int sb = kb_req % kStages;
     if (p < KI) {
       constexpr int G = D / 8, RPI = 64 / G;
-      const int i = wu + kWaves * p;    // instruction of the tile
+      const int i = KTI >= kWaves ? wu + kWaves * p : wu % KTI;  // instruction of the tile
       const int r = i * RPI + lane / G;  // tile row of this lane
       const int row = min(r, L - kb * kBlk - 1);
       const char* b = uniform_ptr(kbase + (int64_t)kb * kBlk * kv_stride);
@@ -240,6 +244,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
 hipError_t launch_dq_ds(const AttnArgs& a, int D, bool causal, dim3 grid, hipStream_t s) {
   if (causal) {
     switch (D) {
+      case 32: hipLaunchKernelGGL((dq_ds_kernel<32, true>), grid, dim3(DsCfg<32>::kThreads), 0, s, a); break;
       case 64: hipLaunchKernelGGL((dq_ds_kernel<64, true>), grid, dim3(DsCfg<64>::kThreads), 0, s, a); break;
       case 128: hipLaunchKernelGGL((dq_ds_kernel<128, true>), grid, dim3(DsCfg<128>::kThreads), 0, s, a); break;
       case 256: hipLaunchKernelGGL((dq_ds_kernel<256, true>), grid, dim3(DsCfg<256>::kThreads), 0, s, a); break;
@@ -247,6 +252,7 @@ hipError_t launch_dq_ds(const AttnArgs& a, int D, bool causal, dim3 grid, hipStr
     }
   } else {
     switch (D) {
+      case 32: hipLaunchKernelGGL((dq_ds_kernel<32, false>), grid, dim3(DsCfg<32>::kThreads), 0, s, a); break;
       case 64: hipLaunchKernelGGL((dq_ds_kernel<64, false>), grid, dim3(DsCfg<64>::kThreads), 0, s, a); break;
       case 128: hipLaunchKernelGGL((dq_ds_kernel<128, false>), grid, dim3(DsCfg<128>::kThreads), 0, s, a); break;
       case 256: hipLaunchKernelGGL((dq_ds_kernel<256, false>), grid, dim3(DsCfg<256>::kThreads), 0, s, a); break;

@@ -133,8 +133,8 @@ int cpattn_version(void);
  * head, 32-key block < ceil(max_kv_len / 32)): with it dK/dV stores dS and dQ is a
  * product with the stored dS instead of a second pass that forms S, P and dP
  * again.  It is 2 bytes per (query row slot, head, key position up to max_kv_len):
- * e.g. 36.5 GB for 128 chunks of 512 rows, 32 heads and max_kv_len 8192.  Head
- * dims 64, 128 and 256 only (0 for head_dim 32).
+ * e.g. 36.5 GB for 128 chunks of 512 rows, 32 heads and max_kv_len 8192.  Every
+ * supported head dim (32 to 256).
  * Returns 0 for an invalid problem (check it with the entry point for the reason). */
 size_t cpattn_workspace_size(const cpattn_problem* p, int op);
 
@@ -233,8 +233,7 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
  *      of ws (cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes): every block with a
  *      visible (key, query) pair, the others are left as they are.
  *  cpattn_bwd_dq_ds: dQ = scale dS K from the dS store that cpattn_bwd_dkdv_ds
- *      filled for the same problem and chunks (reads K and the dS store only).
- *  Both return CPATTN_EUNSUPPORTED for head_dim 32. */
+ *      filled for the same problem and chunks (reads K and the dS store only). */
 int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
                        const void* o, const void* dout, void* ws, size_t ws_bytes,
                        const int32_t* dev_err, cpattn_stream_t stream);

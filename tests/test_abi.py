@@ -181,8 +181,9 @@ def test_stored_ds_workspace_size():
                kv_rows=1 << 14, max_chunk_len=256, max_kv_len=256)
     assert lib.cpattn_workspace_size(ctypes.byref(pb), cp.OP_BWD_DS) == \
         lib.cpattn_workspace_size(ctypes.byref(pb), cp.OP_BWD) + _ds_bytes(4, 1 << 14, 64, 256)
-    # not for head_dim 32, nor for an invalid problem
-    assert lib.cpattn_workspace_size(ctypes.byref(_prob(head_dim=32)), cp.OP_BWD_DS) == 0
+    # head_dim 32 too (the pair-bias rows); not for an invalid problem
+    assert lib.cpattn_workspace_size(ctypes.byref(_prob(head_dim=32)), cp.OP_BWD_DS) == \
+        _ws_layout(8, 64, 2, 32) + _ds_bytes(8, 64, 2, 64)
     assert lib.cpattn_workspace_size(ctypes.byref(_prob(hq=3)), cp.OP_BWD_DS) == 0
 
 
@@ -207,10 +208,14 @@ def test_stored_ds_steps_check_workspace_and_aliases():
                                 None) == cp.EINVAL
     assert "alias" in _err()  # dQ over the dS it reads
     assert lib.cpattn_bwd_dq_ds(ctypes.byref(p), k, so, sl, cm, ws + 16, full, dq, err, None) == cp.EINVAL
+    # head_dim 32 has a dS store as well: its size is checked the same way
     p32 = _prob(head_dim=32)
+    full32 = lib.cpattn_workspace_size(ctypes.byref(p32), cp.OP_BWD_DS)
     args32 = [ctypes.byref(p32)] + args[1:]
-    assert lib.cpattn_bwd_dkdv_ds(*args32, ws, 1 << 30, dk, dv, 0, err, None) == cp.EUNSUPPORTED
-    assert lib.cpattn_bwd_dq_ds(ctypes.byref(p32), k, so, sl, cm, ws, 1 << 30, dq, err, None) == cp.EUNSUPPORTED
+    assert lib.cpattn_bwd_dkdv_ds(*args32, ws, full32 - 1, dk, dv, 0, err, None) == cp.EINVAL
+    assert "workspace" in _err()
+    assert lib.cpattn_bwd_dq_ds(ctypes.byref(p32), k, so, sl, cm, ws, full32 - 1, dq, err, None) == cp.EINVAL
+    assert "workspace" in _err()
 
 
 def test_window_and_merge_host_checks():
