@@ -96,18 +96,18 @@ __device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& i
 // Element r is query 8 (r / 4) + 4 hl + r % 4 of the tile; the lane's key is `key`.
 // With MASK the causal / length mask is applied (pipelined tiles always apply it: the
 // few VALU operations issue under the MFMAs).
+// bv: the bias of the lane's 16 elements (loaded a step ahead).
 template <int N, bool MASK, bool CAUSAL, bool BIAS>
 __device__ __forceinline__ void softmax_part(f32x16& s, f32x16& dp, int r0, const float* lse,
                                              const float* dl, int hl, float c, int key,
                                              bool key_ok, int nq, int tile_pos0,
-                                             const float* bias_h, int bias_len) {
+                                             const float (&bv)[16]) {
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int r = r0 + k, qi = 8 * (r >> 2) + 4 * hl + (r & 3);
     float x;
     if (BIAS)
-      x = fmaf(bias_h[(int64_t)min(tile_pos0 + qi, bias_len - 1) * bias_len + min(key, bias_len - 1)],
-               kLog2e, s[r] * c) - lse[qi];
+      x = fmaf(bv[r], kLog2e, s[r] * c) - lse[qi];
     else
       x = fmaf(s[r], c, -lse[qi]);
     if (MASK) {
@@ -213,6 +213,21 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   QTileIter cur;
   cur.c = chunk_lower_bound(a.chunks, a.num_chunks, b);
   bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0);
+  // With a bias: the lane's 16 bias values of a tile (element r is query 8 (r / 4) +
+  // 4 hl + r % 4 of the tile, key `key`), loaded one step ahead so that their latency
+  // is spent under the previous step's products; used only after the step's wait.
+  float bias_cur[16] = {}, bias_nxt[16] = {};
+  auto load_bias = [&](const QTileIter& it, float (&bv)[16]) {
+    const float* bh = a.bias + (int64_t)(g * a.group + it.hh) * a.bias_len * a.bias_len;
+    const int tp0 = it.ch.pos0 + it.qt * kTq;
+    const int kk = min(key, a.bias_len - 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 8 * (r >> 2) + 4 * hl + (r & 3);
+      bv[r] = bh[(int64_t)min(tp0 + qi, a.bias_len - 1) * a.bias_len + kk];
+    }
+  };
+  if (BIAS && have) load_bias(cur, bias_cur);
   float st_lse = 0.f, st_dl = 0.f;  // stats staged for the next tile (threads < kTq)
   if (have) {
     dma_tiles<D>(lds_t[0][0], lds_t[0][1], a, cur, g, wave, lane);
@@ -280,14 +295,13 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       dma16_at(cb[which] + i * 1024, (uint32_t)lane * 16u, cl[which] + i * 1024);
     };
     if (have_next && tid < kTq) load_stats(a, nxt, g, tid, st_lse, st_dl);
+    if (BIAS && have_next) load_bias(nxt, bias_nxt);
     if (!SPREAD && have_next) dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, g, wave, lane);
 
     // Every wave runs every tile of the loop: tiles that a wave's keys do not see (at the
     // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
     const int nq = min(kTq, cur.ch.len - cur.qt * kTq);
     const int tile_pos0 = cur.ch.pos0 + cur.qt * kTq;
-    const float* bias_h =
-        BIAS ? a.bias + (int64_t)(g * a.group + cur.hh) * a.bias_len * a.bias_len : nullptr;
 
     // S and dP of this tile; each A operand is read one k-step ahead.
     f32x16 s = {}, dp = {};
@@ -333,7 +347,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     const float* dl = lds_dl[buf];
     auto sm_block = [&](int blk) {
       softmax_part<EPB, true, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
-                                            nq, tile_pos0, bias_h, a.bias_len);
+                                            nq, tile_pos0, bias_cur);
     };
     if (PIPE && have_prev) {
       dvdk(pbuf, pp, pd, sm_block);
@@ -342,7 +356,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       for (int blk = 0; blk < NB; ++blk) sm_block(blk);
     } else {  // a tile every key of the wave sees: no mask
       softmax_part<16, false, CAUSAL, BIAS>(s, dp, 0, lse, dl, hl, a.scale_log2, key, key_ok, nq,
-                                            tile_pos0, bias_h, a.bias_len);
+                                            tile_pos0, bias_cur);
     }
     // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
     pp[0] = to_bf16x8(s, 0);
@@ -371,6 +385,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       __builtin_nontemporal_store(pd[1], reinterpret_cast<u32x4*>(dst + 16));
     }
     cur = nxt;
+    if (BIAS) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bias_cur[r] = bias_nxt[r];
+    }
     have = have_next;
     have_prev = true;
     pbuf = buf;

@@ -33,25 +33,36 @@ constexpr int kBN = 64;  // keys per KV tile
 // scores stay unscaled (the positive scale is applied to the max and inside the
 // exponential's FMA); with one they are scaled and biased here.
 // Element r of block kb is key key0 + 32 kb + 8 (r/4) + 4 kg + r%4.
+// The lane's bias values of the tile at key0 (element r of block kb: key
+// key0 + 32 kb + 8 (r/4) + 4 kg + r%4), as groups of four; keys past L read as 0.
+__device__ __forceinline__ void load_bias_tile(f32x4 (&bv)[8], const float* bias_row, int key0, int L,
+                                               int kg, int bias_len) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (kbi + 3 < L && (bias_len & 3) == 0)
+        v = *reinterpret_cast<const f32x4*>(bias_row + kbi);
+      else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (kbi + j < L) ? bias_row[kbi + j] : 0.f;
+      }
+      bv[kb * 4 + i] = v;
+    }
+}
+
 template <bool BIAS, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const float* bias_row, int key0,
-                                           int L, int lo, int hi, int qpos, int kg, int bias_len,
-                                           float& mx) {
+__device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const f32x4 (&btile)[8], int key0,
+                                           int lo, int hi, int qpos, int kg, float& mx) {
   float mj[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
-      f32x4 bv = {0.f, 0.f, 0.f, 0.f};
-      if (BIAS) {
-        if (kbi + 3 < L && (bias_len & 3) == 0)
-          bv = *reinterpret_cast<const f32x4*>(bias_row + kbi);
-        else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bv[j] = (kbi + j < L) ? bias_row[kbi + j] : 0.f;
-        }
-      }
+      const f32x4 bv = btile[kb * 4 + i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = s[kb][i * 4 + j];
@@ -131,8 +142,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   const TrOffsets<D> tro(lane);
   float m_run = -INFINITY, l_run = 0.f;
 
+  // With a bias, each tile's bias values are loaded one tile ahead (their latency is
+  // spent under the previous tile's products) and used after that tile's wait.
   const float* bias_row = nullptr;
-  if (BIAS) bias_row = a.bias + ((int64_t)h * a.bias_len + min(qpos, a.bias_len - 1)) * a.bias_len;
+  f32x4 bias_cur[8] = {}, bias_nxt[8] = {};
+  if (BIAS) {
+    bias_row = a.bias + ((int64_t)h * a.bias_len + min(qpos, a.bias_len - 1)) * a.bias_len;
+    if (n_tiles > t_first) load_bias_tile(bias_cur, bias_row, t_first * kBN, L, kg, a.bias_len);
+  }
 
   const int64_t kv_stride = a.kv_pitch * D;
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
@@ -186,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     const int key0 = t * kBN;
     const int buf = (t - t_first) & 1;
     const CopyStep cs = copy_step(t + 1, buf ^ 1);
+    if (BIAS && t + 1 < n_tiles) load_bias_tile(bias_nxt, bias_row, key0 + kBN, L, kg, a.bias_len);
 
     if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
       // scheduling hint: interleave the step's MFMAs with its LDS reads and VALU work
@@ -220,11 +238,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       float mx = -INFINITY;
       if (need_mask) {
         asm volatile("" ::: "memory");
-        scale_tile<BIAS, true, CAUSAL>(s, a.scale_log2, bias_row, key0, L, kv_lo, kv_hi, qpos, kg,
-                                       a.bias_len, mx);
+        scale_tile<BIAS, true, CAUSAL>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
       } else {
-        scale_tile<BIAS, false, CAUSAL>(s, a.scale_log2, bias_row, key0, L, kv_lo, kv_hi, qpos, kg,
-                                        a.bias_len, mx);
+        scale_tile<BIAS, false, CAUSAL>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
       }
       mx = halves_max(mx);
       if (!BIAS) mx *= c_eff;
@@ -273,6 +289,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     }
     wait_vm_all();
     __syncthreads();
+    if (BIAS) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bias_cur[i] = bias_nxt[i];
+    }
   }
 
   if (col >= nrows) return;
