@@ -316,7 +316,7 @@ def cpu_baseline(w, q, k, v, do, bias, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU sharding is designed, not built)"}))
         sys.exit(2)
     import torch

@@ -72,7 +72,7 @@ def assert_lse_close(name, got, ref, atol=LSE_ATOL):
     return e
 
 
-class GpuRun:
+class DeviceRun:
     """Device copies of a workload's inputs and the HIP path's outputs."""
 
     def __init__(self, cp, w: W.Workload, device="cuda", tensors=None):
@@ -144,7 +144,7 @@ def kv_rows_of(w: W.Workload, seqs=None):
     return m
 
 
-def compare(cp, run: GpuRun, seqs=None, kv_heads=None, chunks=None, check_bwd=True, label="",
+def compare(cp, run: DeviceRun, seqs=None, kv_heads=None, chunks=None, check_bwd=True, label="",
             bar: str = "configs"):
     """Run the oracle on a sampled sub-workload and compare the GPU rows that match it."""
     w = run.w

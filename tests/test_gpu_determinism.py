@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from harness import GpuRun, kv_rows_of, rows_of
+from harness import DeviceRun, kv_rows_of, rows_of
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def _spread(i):
 
 
 def _run(cp, w, store_ds):
-    run = GpuRun(cp, w)
+    run = DeviceRun(cp, w)
     run.forward()
     run.backward(store_ds=store_ds)
     return run
@@ -82,7 +82,7 @@ def test_repeated_calls_over_junk_workspace_give_the_same_bits(gpu_lib, idx):
     cp = gpu_lib
     w = _spread(idx)
     print(f"[case] repeat {idx} D={w.head_dim} bias={w.bias is not None}", flush=True)
-    run = GpuRun(cp, w)
+    run = DeviceRun(cp, w)
     run.forward()
     prob = cp.problem(run.layout, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal, w.scale,
                       w.bias_len)

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from harness import GpuRun, compare, kv_rows_of, rows_of
+from harness import DeviceRun, compare, kv_rows_of, rows_of
 
 pytestmark = pytest.mark.gpu
 
@@ -73,7 +73,7 @@ def test_head_group_views_match_the_call_over_all_heads(gpu_lib, idx):
     cp = gpu_lib
     w, groups = _workload(idx)
     print(f"[case] heads {idx} hq={w.hq} hkv={w.hkv} D={w.head_dim} groups={groups}", flush=True)
-    run = GpuRun(cp, w)
+    run = DeviceRun(cp, w)
     run.forward()
     run.backward()
     torch.cuda.synchronize()
@@ -109,7 +109,7 @@ def test_group_calls_write_only_their_heads(gpu_lib):
     import torch
     cp = gpu_lib
     w, _ = _workload(0)
-    run = GpuRun(cp, w)
+    run = DeviceRun(cp, w)
     run.forward()
     run.backward()
     G = w.hq // w.hkv

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from harness import (GpuRun, assert_close, compare, gather_rows_f64, host_f64, kv_rows_of,
+from harness import (DeviceRun, assert_close, compare, gather_rows_f64, host_f64, kv_rows_of,
                      run_oracle, rows_of)
 
 pytestmark = pytest.mark.gpu
@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 def _run_and_compare(gpu_lib, w, seqs=None, kv_heads=None, label="", bar="configs", store_ds=None):
     print(f"[case] {label or w.name} hq={w.hq} hkv={w.hkv} D={w.head_dim} C={w.num_chunks} "
           f"store_ds={store_ds}", flush=True)
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     run.forward()
     run.backward(store_ds=store_ds)
     info, ref, _ = compare(gpu_lib, run, seqs=seqs, kv_heads=kv_heads, label=label, bar=bar)
@@ -127,7 +127,7 @@ def test_config3_sampled(gpu_lib):
     import torch
     w = W.make_config(3, materialize=False)
     print("[case] cfg3 full size", flush=True)
-    run = GpuRun(gpu_lib, w, tensors=W.draw_on_device(w, 1003))
+    run = DeviceRun(gpu_lib, w, tensors=W.draw_on_device(w, 1003))
     run.forward()
     run.backward()
     compare(gpu_lib, run, seqs={0, 37, 63}, kv_heads={0, 7}, label="cfg3 ")
@@ -140,7 +140,7 @@ def test_config3_sampled(gpu_lib):
 def test_config5_sampled_and_dbias_positions(gpu_lib):
     w = W.make_config(5)
     print("[case] cfg5", flush=True)
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     run.forward()
     run.backward()
     compare(gpu_lib, run, seqs={0, 1023}, label="cfg5 ")
@@ -167,7 +167,7 @@ def _small_case(seed=1, **kw):
 def test_store_mode_ignores_nan_prefill_and_padding_untouched(gpu_lib):
     import torch
     w = _small_case()
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     sentinel_q = torch.full_like(run.q, float("nan"))
     o = sentinel_q.clone()
     lse = torch.full((w.hq, w.q_rows), -123.0, device="cuda")
@@ -188,7 +188,7 @@ def test_store_mode_ignores_nan_prefill_and_padding_untouched(gpu_lib):
 def test_first_contribution_store_then_add(gpu_lib):
     """STORE(second chunk of each sequence) then ADD(first chunk) matches the oracle's sum."""
     w = _small_case(chunks=[(0, 0, 40), (0, 110, 40), (1, 0, 30), (1, 60, 30)])
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     run.forward()
     first = w.chunks[0::2]
     second = w.chunks[1::2]
@@ -208,7 +208,7 @@ def test_first_contribution_store_then_add(gpu_lib):
 
 def test_sequence_without_chunks_gets_zero_dkdv(gpu_lib):
     w = _small_case(chunks=[(0, 0, 50)])
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     run.forward()
     run.backward()
     off, L = w.seq_offsets[1], w.seq_lens[1]
@@ -227,7 +227,7 @@ def test_stored_ds_steps_match_fused_entry_over_stale_workspace(gpu_lib):
     no dS block that dK/dV did not write is read."""
     import torch
     w = _small_case(seed=21, lens=[300, 77], chunks=[(0, 0, 40), (0, 230, 70), (1, 5, 33)])
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     run.forward()
     prob = gpu_lib.problem(run.layout, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal,
                            w.scale, 0)
@@ -258,7 +258,7 @@ def test_stored_ds_steps_match_fused_entry_over_stale_workspace(gpu_lib):
 def test_run_to_run_bitwise_identical(gpu_lib):
     import torch
     w = _small_case(seed=5)
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     run.forward()
     run.backward()
     qi = torch.from_numpy(np.flatnonzero(rows_of(w))).cuda()
@@ -276,7 +276,7 @@ def test_changed_inputs_in_reused_buffers(gpu_lib):
     import torch
     w1 = _small_case(seed=11)
     w2 = _small_case(seed=12)
-    run = GpuRun(gpu_lib, w1)
+    run = DeviceRun(gpu_lib, w1)
     run.forward()
     run.backward()
     # overwrite the same device buffers with the second workload's inputs
@@ -293,7 +293,7 @@ def test_changed_inputs_in_reused_buffers(gpu_lib):
 def test_device_promise_violation_fails_closed(gpu_lib, bad):
     import torch
     w = _small_case()
-    run = GpuRun(gpu_lib, w)
+    run = DeviceRun(gpu_lib, w)
     so, sl, ch = w.seq_offsets.copy(), w.seq_lens.copy(), w.chunks.copy()
     mcl, mkl = w.max_chunk_len, w.max_kv_len
     expect = {"chunk_past_length": 0x10, "overlapping_rows": 0x08, "seq_out_of_range": 0x04,
