@@ -365,7 +365,10 @@ def main():
             cp.bwd_dq(prob, lay, q, k, v, bias, lse, do, ws, dq, err)
         mark(5)
         if bias is not None:
-            cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, ws, dbias, err)
+            if use_ds:
+                cp.bwd_dbias_ds(prob, lay, ws, dbias, err)
+            else:
+                cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, ws, dbias, err)
             mark(6)
 
     for _ in range(args.warmup):

@@ -5,7 +5,7 @@ kernels behind include/cpattn.h.  PyTorch provides device memory and the current
 stream.  There is no fallback: if the library or a GPU is missing, calls raise.
 
 Names follow the C entry points: fwd, bwd, bwd_prepass, bwd_dkdv, bwd_dq,
-bwd_dbias, bwd_dkdv_ds, bwd_dq_ds, fwd_window, merge, bwd_window, validate, pack,
+bwd_dbias, bwd_dkdv_ds, bwd_dq_ds, bwd_dbias_ds, fwd_window, merge, bwd_window, validate, pack,
 unpack.
 """
 from __future__ import annotations
@@ -30,7 +30,8 @@ DEV_ERR_BITS = {
 EXPORTS = [
     "cpattn_status_str", "cpattn_last_error", "cpattn_version", "cpattn_workspace_size",
     "cpattn_validate", "cpattn_fwd", "cpattn_bwd", "cpattn_bwd_prepass", "cpattn_bwd_dkdv",
-    "cpattn_bwd_dq", "cpattn_bwd_dbias", "cpattn_bwd_dkdv_ds", "cpattn_bwd_dq_ds", "cpattn_pack",
+    "cpattn_bwd_dq", "cpattn_bwd_dbias", "cpattn_bwd_dkdv_ds", "cpattn_bwd_dq_ds",
+    "cpattn_bwd_dbias_ds", "cpattn_pack",
     "cpattn_unpack", "cpattn_fwd_window", "cpattn_merge", "cpattn_bwd_window",
     "cpattn_a2a_split_heads", "cpattn_a2a_merge_heads", "cpattn_a2a_scatter_rows",
     "cpattn_a2a_gather_rows",
@@ -105,6 +106,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "cpattn_bwd_dkdv_ds": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp,
                                ctypes.c_int, _vp, _vp],
         "cpattn_bwd_dq_ds": [P, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
+        "cpattn_bwd_dbias_ds": [P, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
         "cpattn_fwd_window": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, i32, i32, _vp, _vp, _vp, _vp],
         "cpattn_merge": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
         "cpattn_bwd_window": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, i32, i32, ctypes.c_int,
@@ -430,6 +432,14 @@ def bwd_dq_ds(prob: Problem, layout: Layout, k, ws, dq, dev_err, stream=None):
     _check(lib.cpattn_bwd_dq_ds(ctypes.byref(prob), _ptr(k), _ptr(layout.seq_offsets), _ptr(layout.seq_lens),
                                 _ptr(layout.chunks), _ptr(ws), ws.numel(), _ptr(dq), _ptr(dev_err),
                                 _stream(stream)))
+
+
+def bwd_dbias_ds(prob: Problem, layout: Layout, ws, dbias, dev_err, stream=None):
+    """dBias summed from the dS that bwd_dkdv_ds stored in `ws`."""
+    lib = load()
+    _check(lib.cpattn_bwd_dbias_ds(ctypes.byref(prob), _ptr(layout.seq_offsets), _ptr(layout.seq_lens),
+                                   _ptr(layout.chunks), _ptr(ws), ws.numel(), _ptr(dbias), _ptr(dev_err),
+                                   _stream(stream)))
 
 
 def bwd_dbias(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dbias, dev_err, stream=None):

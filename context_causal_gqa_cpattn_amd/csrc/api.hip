@@ -119,7 +119,7 @@ struct Plan {
   bool ds_ok;            // the stored-dS backward applies (every supported head_dim, 32 to 256)
   int64_t kb_max;        // 32-key blocks per (tile slot, head) in the dS store
   int64_t off_ds, ds_bytes;
-  dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias, grid_dqds;
+  dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias, grid_dbias_ds, grid_dqds;
   int bpc_fwd, bpc_prepass, bpc_dqds, kv_tiles;
 };
 
@@ -205,6 +205,11 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
     if (pl.parts > 1) pl.partial_bytes = round256((int64_t)pl.parts * pl.bias_bytes);
     pl.grid_dbias = dim3((unsigned)(cdiv(p->bias_len, kDbiasKeys) * pl.parts),
                          (unsigned)cdiv(p->bias_len, kDbiasPos), (unsigned)p->hq);
+    // from the stored dS: 32-key blocks x parts, 32-position tiles, heads (same units)
+    if (cdiv(p->bias_len, 32) > 65535 || cdiv(p->bias_len, 32) * pl.parts > kGridMax)
+      return fail(CPATTN_EUNSUPPORTED, "bias too large for one launch");
+    pl.grid_dbias_ds = dim3((unsigned)(cdiv(p->bias_len, 32) * pl.parts),
+                            (unsigned)cdiv(p->bias_len, 32), (unsigned)p->hq);
   }
   // Transposed 32-query tiles: at most ceil(q_rows/32) + C of them.
   const int64_t max_tiles = cdiv(p->q_rows, kPrepassRows) + p->num_chunks;
@@ -531,6 +536,21 @@ int enqueue_dbias(const cpattn_problem* p, const Plan& pl, AttnArgs a, float* db
                    "dBias reduce launch");
 }
 
+// dBias as a sum over the dS blocks that dK/dV stored (same units and order of the
+// partial sums as enqueue_dbias).
+int enqueue_dbias_ds(const cpattn_problem* p, const Plan& pl, AttnArgs a, float* dbias, const void* ws,
+                     hipStream_t s) {
+  if (!pl.bias || empty(pl.grid_dbias_ds)) return CPATTN_OK;
+  float* partial = pl.parts > 1 ? (float*)((char*)ws + pl.off_partials) : dbias;
+  a.dbias = partial;
+  a.ds = (const uint16_t*)((const char*)ws + pl.off_ds);
+  a.kb_max = pl.kb_max;
+  int r = hip_check(launch_dbias_ds(a, pl.grid_dbias_ds, s), "dBias (stored dS) launch");
+  if (r || pl.parts == 1) return r;
+  return hip_check(launch_dbias_reduce(partial, dbias, pl.bias_bytes / 4, pl.parts, a.dev_err, s),
+                   "dBias reduce launch");
+}
+
 }  // namespace
 
 int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void* v,
@@ -577,7 +597,7 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
     if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
     if ((r = enqueue_dq(p, pl, a, dq, s))) return r;
   }
-  if (dbias) return enqueue_dbias(p, pl, a, dbias, ws, s);
+  if (dbias) return use_ds ? enqueue_dbias_ds(p, pl, a, dbias, ws, s) : enqueue_dbias(p, pl, a, dbias, ws, s);
   return CPATTN_OK;
 }
 
@@ -781,6 +801,33 @@ int cpattn_bwd_dbias(const cpattn_problem* p, const void* q, const void* k, cons
   if ((r = alias_audit(rs))) return r;
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   return enqueue_dbias(p, pl, a, dbias, ws, (hipStream_t)stream);
+}
+
+int cpattn_bwd_dbias_ds(const cpattn_problem* p, const int32_t* seq_offsets, const int32_t* seq_lens,
+                        const int32_t* q_chunk_map, void* ws, size_t ws_bytes, float* dbias,
+                        const int32_t* dev_err, cpattn_stream_t stream) {
+  g_last_error.clear();
+  Plan pl;
+  int r;
+  if ((r = make_plan(p, pl))) return r;
+  if (!pl.bias) return fail(CPATTN_EINVAL, "dBias needs a bias (bias_len > 0)");
+  if (!pl.ds_ok) return fail(CPATTN_EUNSUPPORTED, "the stored-dS backward needs head_dim >= 32");
+  if ((r = check_descriptors(p, seq_offsets, seq_lens, q_chunk_map, dev_err))) return r;
+  if ((r = check_ptr(dbias, pl.bias_bytes, 16, "dbias"))) return r;
+  const int64_t need = pl.off_ds + pl.ds_bytes;
+  if ((int64_t)ws_bytes < need) return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)need);
+  if ((r = check_ptr(ws, need, 256, "ws"))) return r;
+  std::vector<Range> rs = {rng("ws (dS area)", (const char*)ws + pl.off_ds, pl.ds_bytes, false),
+                           rng("ws partials", (char*)ws + pl.off_partials, pl.partial_bytes, true),
+                           rng("dbias", dbias, pl.bias_bytes, true)};
+  add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, false);
+  if ((r = alias_audit(rs))) return r;
+  AttnArgs a = base_args(p, pl);
+  a.seq_offsets = seq_offsets;
+  a.seq_lens = seq_lens;
+  a.chunks = q_chunk_map;
+  a.dev_err = dev_err;
+  return enqueue_dbias_ds(p, pl, a, dbias, ws, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- layout copies

@@ -146,3 +146,108 @@ hipError_t launch_dbias_reduce(const float* partial, float* out, int64_t n, int 
 }
 
 }  // namespace cpattn
+
+namespace cpattn {
+
+// dBias from the stored dS: with the dS store filled by dK/dV (BF16 blocks of 32 keys x
+// 32 queries per (query tile slot, head, 32-key block)), dBias[h, p, k] is the sum over
+// every chunk row at position p of that row's dS[h, k]: a streaming reduction over the
+// blocks instead of forming S, P and dP again.
+//
+// Workgroup = (head h, 32 positions from P0, 32 keys from K0, unit of consecutive
+// chunks), 128 threads; thread t owns key row n = t / 4 and granule v = t % 4 of a
+// block, i.e. key K0 + n and the 8 queries 16 (v / 2) + 8 (i / 4) + 4 (v % 2) + i % 4
+// (i = 0..7) of a 32-query tile.  A chunk whose first position is a multiple of 32
+// covers the positions [P0, P0 + 32) with one of its tiles, and the thread adds its
+// 16 bytes of that tile's block; the chunks are read four at a time, added in chunk
+// order.  A unit with any other chunk is summed element by element (same order).  Only
+// blocks that dK/dV stored are read: a tile with rows and a key block below the
+// sequence length (the kernel runs without causal masking only).
+__global__ __launch_bounds__(128) void dbias_ds_kernel(const AttnArgs a) {
+  if (*a.dev_err) return;
+  const int t = threadIdx.x, n = t >> 2, v = t & 3;
+  const int BL = a.bias_len;
+  const int kblocks = (BL + 31) / 32;
+  const int kb = blockIdx.x % kblocks;
+  const int part = blockIdx.x / kblocks;
+  const int P0 = blockIdx.y * 32, K0 = kb * 32;
+  const int h = blockIdx.z;
+  const int per = (a.num_chunks + a.parts - 1) / a.parts;
+  const int c_begin = part * per, c_end = min(a.num_chunks, c_begin + per);
+  // the thread's 8 query slots within a tile
+  int qq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qq[i] = 16 * (v >> 1) + 8 * (i >> 2) + 4 * (v & 1) + (i & 3);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+  auto chunk_at = [&](int c) {
+    const int32_t* m = a.chunks + 4 * __builtin_amdgcn_readfirstlane(c);
+    return Chunk{m[0], m[1], m[2], m[3]};
+  };
+  auto block_ptr = [&](int c, const Chunk& ch, int tile) {
+    const int64_t blk = ((int64_t)tile_slot(c, ch.q_row, tile) * a.hq + h) * a.kb_max + kb;
+    return a.ds + blk * 1024;
+  };
+  // Does the unit hold a chunk whose tiles do not line up with 32-position tiles?
+  bool aligned = true;
+  for (int c = c_begin; c < c_end; ++c) aligned &= (chunk_at(c).pos0 & 31) == 0;
+
+  if (aligned) {
+    for (int c0 = c_begin; c0 < c_end; c0 += 4) {
+      u32x4 w[4];
+      bool use[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j;
+        use[j] = false;
+        w[j] = u32x4{0u, 0u, 0u, 0u};
+        if (c < c_end) {
+          const Chunk ch = chunk_at(c);
+          if (P0 >= ch.pos0 && P0 < ch.pos0 + ch.len && K0 < a.seq_lens[ch.seq]) {
+            use[j] = true;
+            w[j] = ld16(block_ptr(c, ch, (P0 - ch.pos0) >> 5) + n * 32 + v * 8);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (use[j]) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += bf16_lo(w[j][i]);
+            acc[2 * i + 1] += bf16_hi(w[j][i]);
+          }
+        }
+    }
+  } else {
+    for (int c = c_begin; c < c_end; ++c) {
+      const Chunk ch = chunk_at(c);
+      if (ch.pos0 >= P0 + 32 || ch.pos0 + ch.len <= P0 || K0 >= a.seq_lens[ch.seq]) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = P0 + qq[i] - ch.pos0;  // chunk row of this query slot
+        if (r < 0 || r >= ch.len) continue;
+        const int q = r & 31, e = q >> 4, wq = q & 15;
+        const int off = (2 * e + ((wq >> 2) & 1)) * 8 + 4 * (wq >> 3) + (wq & 3);
+        const uint16_t bits = block_ptr(c, ch, r >> 5)[n * 32 + off];
+        acc[i] += __uint_as_float((uint32_t)bits << 16);
+      }
+    }
+  }
+
+  const int k = K0 + n;
+  if (k >= BL) return;
+  float* dst = a.dbias + (int64_t)part * a.hq * BL * BL + (int64_t)h * BL * BL + k;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = P0 + qq[i];
+    if (p < BL) dst[(int64_t)p * BL] = acc[i];
+  }
+}
+
+hipError_t launch_dbias_ds(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL(dbias_ds_kernel, grid, dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -77,6 +77,8 @@ hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 gr
 hipError_t launch_dq(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
 hipError_t launch_dq_ds(const AttnArgs& a, int D, bool causal, dim3 grid, hipStream_t s);
 hipError_t launch_dbias(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
+// dBias summed from the stored dS (grid: 32-key blocks x parts, 32-position tiles, heads).
+hipError_t launch_dbias_ds(const AttnArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_dbias_reduce(const float* partial, float* out, int64_t n, int parts,
                                const int32_t* dev_err, hipStream_t s);
 

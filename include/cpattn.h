@@ -233,7 +233,16 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
  *      of ws (cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes): every block with a
  *      visible (key, query) pair, the others are left as they are.
  *  cpattn_bwd_dq_ds: dQ = scale dS K from the dS store that cpattn_bwd_dkdv_ds
- *      filled for the same problem and chunks (reads K and the dS store only). */
+ *      filled for the same problem and chunks (reads K and the dS store only).
+ *  cpattn_bwd_dbias_ds: dBias (fp32, with a bias) as the sum over chunk rows of the
+ *      dS that cpattn_bwd_dkdv_ds stored (page "Support and performance optimization
+ *      for Hopper (H200) architecture?": the pair bias is shared by every row, so its
+ *      gradient is a reduction over rows).  The rows are summed in the same fixed
+ *      partition units and order as cpattn_bwd_dbias; the result differs from it only
+ *      by the BF16 rounding of the stored dS.  ws must hold the dBias partial sums and
+ *      the dS store (cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes); reads the
+ *      descriptors and the dS store only.  cpattn_bwd computes dBias this way whenever
+ *      it uses the dS store. */
 int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
                        const void* o, const void* dout, void* ws, size_t ws_bytes,
                        const int32_t* dev_err, cpattn_stream_t stream);
@@ -260,6 +269,9 @@ int cpattn_bwd_dkdv_ds(const cpattn_problem* p, const void* q, const void* k, co
 int cpattn_bwd_dq_ds(const cpattn_problem* p, const void* k, const int32_t* seq_offsets,
                      const int32_t* seq_lens, const int32_t* q_chunk_map, const void* ws,
                      size_t ws_bytes, void* dq, const int32_t* dev_err, cpattn_stream_t stream);
+int cpattn_bwd_dbias_ds(const cpattn_problem* p, const int32_t* seq_offsets, const int32_t* seq_lens,
+                        const int32_t* q_chunk_map, void* ws, size_t ws_bytes, float* dbias,
+                        const int32_t* dev_err, cpattn_stream_t stream);
 
 /* Layout copies ("Changes": vectorised BF16 pack/unpack copies that keep
  * physical sequence origins).  BHSD is [B, H, S_pitch, D]; THD is

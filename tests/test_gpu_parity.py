@@ -255,6 +255,46 @@ def test_stored_ds_steps_match_fused_entry_over_stale_workspace(gpu_lib):
     compare(gpu_lib, run)
 
 
+def test_stored_ds_dbias_steps_match_fused_entry_over_stale_workspace(gpu_lib):
+    """With a bias, the step entry points (pre-pass, dK/dV storing dS, dQ and dBias from
+    the stored dS) give the fused entry point's results bit for bit over a workspace
+    prefilled with NaN bytes; chunks starting on and off 32-position boundaries (the
+    block-wise and the element-wise sums)."""
+    import torch
+    lens = [96, 70, 64]
+    chunks = [(0, 0, 96), (1, 5, 40), (2, 32, 32)]
+    w = W.make_custom(lens=lens, hq=4, hkv=2, head_dim=32, causal=False, bias=True, chunks=chunks, seed=33)
+    run = DeviceRun(gpu_lib, w)
+    run.forward()
+    prob = gpu_lib.problem(run.layout, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal,
+                           w.scale, w.bias_len)
+    need = gpu_lib.workspace_size(prob, gpu_lib.OP_BWD_DS)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    dq_f, dk_f, dv_f, dbias_f, err = gpu_lib.bwd(run.q, run.k, run.v, run.layout, run.o, run.lse, run.do,
+                                                 causal=False, scale=w.scale, bias=run.bias, ws=ws)
+    gpu_lib.check(err)
+    ws.fill_(0xFF)
+    err = gpu_lib.new_dev_err()
+    dq, dk, dv = torch.empty_like(run.q), torch.empty_like(run.k), torch.empty_like(run.v)
+    dbias = torch.full_like(run.bias, float("nan"))
+    gpu_lib.validate(prob, run.layout, err)
+    gpu_lib.bwd_prepass(prob, run.layout, run.q, run.o, run.do, ws, err)
+    gpu_lib.bwd_dkdv_ds(prob, run.layout, run.q, run.k, run.v, run.bias, run.lse, run.do, ws, dk, dv,
+                        False, err)
+    gpu_lib.bwd_dq_ds(prob, run.layout, run.k, ws, dq, err)
+    gpu_lib.bwd_dbias_ds(prob, run.layout, ws, dbias, err)
+    torch.cuda.synchronize()
+    gpu_lib.check(err)
+    qi = torch.from_numpy(np.flatnonzero(rows_of(w))).cuda()
+    ki = torch.from_numpy(np.flatnonzero(kv_rows_of(w))).cuda()
+    for x, y in ((dq_f[qi], dq[qi]), (dk_f[ki], dk[ki]), (dv_f[ki], dv[ki])):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(dbias_f.view(torch.int32), dbias.view(torch.int32))
+    run.dq, run.dk, run.dv, run.dbias = dq, dk, dv, dbias
+    info, ref, _ = compare(gpu_lib, run, bar="pages")
+    assert_close("dBias from stored dS", dbias.cpu().numpy(), ref["dbias"], bar="pages")
+
+
 def test_run_to_run_bitwise_identical(gpu_lib):
     import torch
     w = _small_case(seed=5)
