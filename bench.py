@@ -181,7 +181,12 @@ def ring_step_rates(cp, torch, w, q, k, v, do, bias, lay, flop, windows=8, reps=
     lse_w = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     prob = cp.problem(lay, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal, w.scale, w.bias_len)
-    ws = torch.empty(max(cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
+    # The dS store lets each window's dQ share multiply the dS its dK/dV pass stored;
+    # the smaller workspace forms dS again for dQ (timed as bwd_recompute).
+    ws_rc = torch.empty(max(cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
+    ws = ws_rc
+    if w.head_dim >= 32:
+        ws = torch.empty(max(cp.workspace_size(prob, cp.OP_BWD_DS), 256), dtype=torch.uint8, device="cuda")
     err = cp.new_dev_err()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -196,11 +201,11 @@ def ring_step_rates(cp, torch, w, q, k, v, do, bias, lay, flop, windows=8, reps=
                               lse=lse_w, dev_err=err)
                 cp.merge(prob, lay, o, lse, o_w, lse_w, dev_err=err)
 
-    def bwd():
+    def bwd(buf=None):
         for i in range(windows):
             cp.bwd_window(q, k, v, lay, o, lse, do, edges[i], edges[i + 1], causal=w.causal, scale=w.scale,
-                          bias=bias, prepass=(i == 0), dq=dq, dq_accumulate=(i > 0), dk=dk, dv=dv, ws=ws,
-                          dev_err=err)
+                          bias=bias, prepass=(i == 0), dq=dq, dq_accumulate=(i > 0), dk=dk, dv=dv,
+                          ws=ws if buf is None else buf, dev_err=err)
 
     def merges():
         for _ in range(windows - 1):
@@ -210,7 +215,10 @@ def ring_step_rates(cp, torch, w, q, k, v, do, bias, lay, flop, windows=8, reps=
     fwd()
     bwd()
     torch.cuda.synchronize()
-    for name, fn in (("fwd", fwd), ("bwd", bwd), ("merges", merges)):
+    runs = [("fwd", fwd), ("bwd", bwd), ("merges", merges)]
+    if ws is not ws_rc:
+        runs.append(("bwd_recompute", lambda: bwd(ws_rc)))
+    for name, fn in runs:
         e0, e1 = ev(), ev()
         e0.record()
         for _ in range(reps):

@@ -365,8 +365,12 @@ def merge(prob: Problem, layout: Layout, o_a, lse_a, o_b, lse_b, o=None, lse=Non
 def bwd_window(q, k, v, layout: Layout, o, lse, do, kv_lo: int, kv_hi: int, causal: bool = True,
                scale: Optional[float] = None, bias=None, prepass: bool = True, dq=None,
                dq_accumulate: bool = False, dk=None, dv=None, dkv_accumulate: bool = False, ws=None,
-               dev_err=None, stream=None):
-    """The key window [kv_lo, kv_hi)'s dQ share (store or add) and its keys' dK/dV."""
+               dev_err=None, stream=None, store_ds: Optional[bool] = None):
+    """The key window [kv_lo, kv_hi)'s dQ share (store or add) and its keys' dK/dV.
+
+    store_ds: size a new workspace for the stored-dS path (dK/dV store the window's dS,
+    the dQ share multiplies it); None = whenever the head dim allows it.  A given `ws`
+    decides by its size."""
     torch = _torch()
     lib = load()
     prob = _prob_for(q, k, v, layout, causal, scale, bias)
@@ -381,6 +385,8 @@ def bwd_window(q, k, v, layout: Layout, o, lse, do, kv_lo: int, kv_hi: int, caus
     if dv is None:
         dv = _like(v)
     need = workspace_size(prob, OP_BWD)
+    if store_ds is not False:
+        need = max(need, workspace_size(prob, OP_BWD_DS))
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if dev_err is None:

@@ -623,13 +623,17 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
     return fail(CPATTN_EINVAL, "prepass, dq_accumulate and dkv_accumulate must be 0 or 1");
   if ((int64_t)ws_bytes < pl.ws_core)
     return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)pl.ws_core);
-  if ((r = check_ptr(ws, pl.ws_core, 256, "ws"))) return r;
+  // With room for the dS store, dK/dV store the window's dS and the dQ share multiplies it.
+  const bool use_ds = pl.ds_ok && (int64_t)ws_bytes >= pl.off_ds + pl.ds_bytes;
+  const int64_t ws_used = use_ds ? pl.off_ds + pl.ds_bytes : pl.ws_core;
+  if ((r = check_ptr(ws, ws_used, 256, "ws"))) return r;
   std::vector<Range> rs = {rq(pl, "q", q, false),        rkv(pl, "k", k, false),
                            rkv(pl, "v", v, false),        rng("bias", bias, pl.bias_bytes, false),
                            rq(pl, "o", o, false),         rng("lse", lse, pl.stat_bytes, false),
                            rq(pl, "dout", dout, false),   rq(pl, "dq", dq, true),
                            rkv(pl, "dk", dk, true),       rkv(pl, "dv", dv, true),
                            rng("ws", ws, pl.ws_core, prepass != 0)};
+  if (use_ds) rs.push_back(rng("ws (dS area)", (char*)ws + pl.off_ds, pl.ds_bytes, true));
   add_descriptor_ranges(rs, p, seq_offsets, seq_lens, q_chunk_map, dev_err, prepass != 0);
   if ((r = alias_audit(rs))) return r;
 
@@ -642,6 +646,10 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
   a.kv_lo = kv_lo;
   a.kv_hi = kv_hi;
   a.dq_accumulate = dq_accumulate;
+  if (use_ds) {
+    if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s, (char*)ws + pl.off_ds))) return r;
+    return enqueue_dq_ds(p, pl, a, ws, dq, s);
+  }
   if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
   return enqueue_dq(p, pl, a, dq, s);
 }

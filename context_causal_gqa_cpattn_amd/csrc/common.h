@@ -384,7 +384,7 @@ struct AttnArgs {
   int64_t q_pitch;       // heads per row in memory: Q, O, dO, dQ
   int64_t kv_pitch;      // heads per row in memory: K, V, dK, dV
   int kv_lo, kv_hi;      // key window [kv_lo, kv_hi) in sequence positions (0, INT_MAX: all)
-  int dq_accumulate;     // dQ (recompute path): 0 store, 1 add to the existing values
+  int dq_accumulate;     // dQ: 0 store, 1 add to the existing values
   const int32_t* seq_offsets;
   const int32_t* seq_lens;
   const int32_t* chunks;

@@ -14,6 +14,10 @@
 // 32x32 accumulator lane holds its rows).  Block kb of (query tile slot, head h) is at
 // ((slot hq + h) kb_max + kb) 2 KB of the dS area.
 //
+// With a key window [kv_lo, kv_hi) only the window's key blocks are multiplied, and
+// with dq_accumulate the result is added to the existing BF16 dQ (one rounding): a ring
+// step's dQ share from the dS that its window's dK/dV stored.
+//
 // Workgroup = (chunk, block of positions, hpw query heads that share one KV head) with
 // four slots of (head, two 32-query tiles).  For D >= 128 two waves share a slot, each
 // keeping half of dQ^T (D/2 x 64 queries, fp32) in registers, two waves per SIMD (one
@@ -104,7 +108,11 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   const int L = a.seq_lens[ch.seq];
   const int64_t koff = a.seq_offsets[ch.seq];
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + wg_pos) - 1;
-  const int n_steps = (min(L, CAUSAL ? wg_last_pos + 1 : L) + kBlk - 1) / kBlk;
+  // Key blocks [kb_first, n_steps): those with a visible key, within the key window
+  // [kv_lo, kv_hi) (the whole sequence without one).
+  const int kv_end = min(min(L, CAUSAL ? wg_last_pos + 1 : L), a.kv_hi);
+  const int kb_first = a.kv_lo / kBlk;
+  const int n_steps = (kv_end + kBlk - 1) / kBlk;
 
   // The slot's two tiles: rows, key blocks with a visible pair, first dS block.
   int nq[2], nkb[2];
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
     const int r = row0 + 32 * i;
     nq[i] = max(0, min(32, ch.len - r));
     const int last = ch.pos0 + r + nq[i] - 1;
-    nkb[i] = nq[i] > 0 ? (min(L, CAUSAL ? last + 1 : L) + kBlk - 1) / kBlk : 0;
+    nkb[i] = nq[i] > 0 ? (min(min(L, CAUSAL ? last + 1 : L), a.kv_hi) + kBlk - 1) / kBlk : 0;
     dsrc[i] = a.ds;
     if (nq[i] > 0)
       dsrc[i] = a.ds + ((int64_t)tile_slot(c, ch.q_row, r / 32) * a.hq + h) * a.kb_max * kBlkElems;
@@ -181,14 +189,14 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   };
   const int dso = ds_tr_off(lane);
 
-  if (n_steps > 0) {
+  if (n_steps > kb_first) {
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
 #pragma unroll
-      for (int p = 0; p < PER; ++p) issue_one(s, p);
+      for (int p = 0; p < PER; ++p) issue_one(kb_first + s, p);
   }
 
-  for (int kb = 0; kb < n_steps; ++kb) {
+  for (int kb = kb_first; kb < n_steps; ++kb) {
     wait_vm<(kStages - 2) * PER>();  // stage kb has landed (later stages may be in flight)
     __syncthreads();                 // stage kb is in LDS for every wave; stage kb - 1 is free
 
@@ -233,8 +241,16 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
     for (int j = 0; j < NDB; ++j)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const u32x2 w{pack_bf16x2(acc[i][j][4 * i4] * a.scale, acc[i][j][4 * i4 + 1] * a.scale),
-                      pack_bf16x2(acc[i][j][4 * i4 + 2] * a.scale, acc[i][j][4 * i4 + 3] * a.scale)};
+        float r4[4] = {acc[i][j][4 * i4] * a.scale, acc[i][j][4 * i4 + 1] * a.scale,
+                       acc[i][j][4 * i4 + 2] * a.scale, acc[i][j][4 * i4 + 3] * a.scale};
+        if (a.dq_accumulate && ok) {  // add to the existing BF16 values, one rounding
+          const u32x2 old = ld8(op + j * 32 + i4 * 8);
+          r4[0] += bf16_lo(old[0]);
+          r4[1] += bf16_hi(old[0]);
+          r4[2] += bf16_lo(old[1]);
+          r4[3] += bf16_hi(old[1]);
+        }
+        const u32x2 w{pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
         if (ok) st8(op + j * 32 + i4 * 8, w);
         __builtin_amdgcn_sched_barrier(0);  // one block's registers at a time
       }

@@ -208,7 +208,9 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
  * every key is the full dQ.  prepass = 1 validates and runs the Delta pre-pass into
  * ws (cpattn_workspace_size(p, CPATTN_OP_BWD) bytes, without the dBias partials);
  * prepass = 0 reuses the pre-pass results an earlier call left in ws for the same O,
- * dO and chunks.  dS is formed again for dQ (no dS store), and no dBias is produced. */
+ * dO and chunks.  When ws holds cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes, dK/dV
+ * store the window's dS and the dQ share multiplies it (the dS store is reused by the
+ * next window); otherwise dS is formed again for dQ.  No dBias is produced. */
 int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, const void* v,
                       const int32_t* seq_offsets, const int32_t* seq_lens,
                       const int32_t* q_chunk_map, const float* bias, const void* o, const float* lse,

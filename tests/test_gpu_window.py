@@ -98,12 +98,13 @@ def test_window_forward_and_merge(gpu_lib, idx):
     _assert_lse("merged LSE", run_l.cpu().numpy()[:, rows], full["lse"][:, rows])
 
 
+@pytest.mark.parametrize("store_ds", [False, True], ids=["recompute", "stored_ds"])
 @pytest.mark.parametrize("idx", range(len(CASES)))
-def test_window_backward_shares_sum_to_full_gradients(gpu_lib, idx):
+def test_window_backward_shares_sum_to_full_gradients(gpu_lib, idx, store_ds):
     import torch
     cp = gpu_lib
     w, windows = _workload(idx)
-    print(f"[case] window bwd {idx} D={w.head_dim} windows={windows}", flush=True)
+    print(f"[case] window bwd {idx} D={w.head_dim} windows={windows} store_ds={store_ds}", flush=True)
     q, k, v, do, bias, lay = _inputs(cp, w)
     o, lse, err = cp.fwd(q, k, v, lay, causal=w.causal, scale=w.scale, bias=bias)
     dq = torch.empty_like(q)
@@ -113,7 +114,7 @@ def test_window_backward_shares_sum_to_full_gradients(gpu_lib, idx):
     for i, (lo, hi) in enumerate(windows):
         _, _, _, ws, err2 = cp.bwd_window(q, k, v, lay, o, lse, do, lo, hi, causal=w.causal, scale=w.scale,
                                           bias=bias, prepass=(i == 0), dq=dq, dq_accumulate=(i > 0),
-                                          dk=dk, dv=dv, ws=ws, dev_err=err)
+                                          dk=dk, dv=dv, ws=ws, dev_err=err, store_ds=store_ds)
     torch.cuda.synchronize()
     cp.check(err)
     qf, kf, vf, dof, bf = _f64(w)
@@ -127,10 +128,12 @@ def test_window_backward_shares_sum_to_full_gradients(gpu_lib, idx):
     assert np.isnan(host_f64(cp, dk)[~kr]).all() and np.isnan(host_f64(cp, dv)[~kr]).all()
 
 
-def test_window_backward_matches_window_oracle_shares(gpu_lib):
+@pytest.mark.parametrize("store_ds", [False, True], ids=["recompute", "stored_ds"])
+def test_window_backward_matches_window_oracle_shares(gpu_lib, store_ds):
     """One window's dK/dV and dQ share against the window oracle directly."""
     import torch
     cp = gpu_lib
+    print(f"[case] window bwd share store_ds={store_ds}", flush=True)
     w, _ = _workload(0)
     lo, hi = 64, 200
     q, k, v, do, bias, lay = _inputs(cp, w)
@@ -138,7 +141,7 @@ def test_window_backward_matches_window_oracle_shares(gpu_lib):
     dk = torch.full_like(k, float("nan"))
     dv = torch.full_like(v, float("nan"))
     dq, _, _, _, err = cp.bwd_window(q, k, v, lay, o, lse, do, lo, hi, causal=True, scale=w.scale,
-                                     dk=dk, dv=dv, dev_err=err)
+                                     dk=dk, dv=dv, dev_err=err, store_ds=store_ds)
     torch.cuda.synchronize()
     cp.check(err)
     qf, kf, vf, dof, _ = _f64(w)
