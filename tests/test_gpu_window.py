@@ -10,7 +10,7 @@ import pytest
 import oracle
 import oracle.window as OW
 import workloads as W
-from harness import assert_close, host_f64
+from harness import DeviceRun, assert_close, compare, host_f64, rows_of
 
 pytestmark = pytest.mark.gpu
 
@@ -154,3 +154,47 @@ def test_window_backward_matches_window_oracle_shares(gpu_lib, store_ds):
     assert_close("dK share", host_f64(cp, dk)[m], ref["dk"][m], bar="pages")
     assert_close("dV share", host_f64(cp, dv)[m], ref["dv"][m], bar="pages")
     assert np.isnan(host_f64(cp, dk)[~m]).all()
+
+
+@pytest.mark.slow
+def test_config3_ring_of_eight_windows_sampled(gpu_lib):
+    """The full-size rank share run as a ring of eight equal key windows: window forwards
+    merged on the GPU, window backwards with the dS store and dQ added over the windows,
+    checked on sampled sequences and KV heads against the full-attention oracle."""
+    import torch
+    cp = gpu_lib
+    w = W.make_config(3, materialize=False)
+    print("[case] cfg3 ring of 8 key windows", flush=True)
+    run = DeviceRun(cp, w, tensors=W.draw_on_device(w, 1013))
+    lay = run.layout
+    n = 8
+    Lmax = int(max(w.seq_lens))
+    edges = [Lmax * i // n for i in range(n)] + [BIGW]
+    prob = cp.problem(lay, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal, w.scale, w.bias_len)
+    o = torch.empty_like(run.q)
+    lse = torch.empty((w.hq, w.q_rows), dtype=torch.float32, device="cuda")
+    o_w, lse_w = torch.empty_like(o), torch.empty_like(lse)
+    err = cp.new_dev_err()
+    for i in range(n):
+        first = i == 0
+        cp.fwd_window(run.q, run.k, run.v, lay, edges[i], edges[i + 1], causal=True, scale=w.scale,
+                      o=o if first else o_w, lse=lse if first else lse_w, dev_err=err)
+        if not first:
+            cp.merge(prob, lay, o, lse, o_w, lse_w, dev_err=err)
+    dq, dk, dv = torch.empty_like(run.q), torch.empty_like(run.k), torch.empty_like(run.v)
+    ws = None
+    for i in range(n):
+        _, _, _, ws, _ = cp.bwd_window(run.q, run.k, run.v, lay, o, lse, run.do, edges[i], edges[i + 1],
+                                       causal=True, scale=w.scale, prepass=(i == 0), dq=dq,
+                                       dq_accumulate=(i > 0), dk=dk, dv=dv, ws=ws, dev_err=err,
+                                       store_ds=True)
+    torch.cuda.synchronize()
+    cp.check(err)
+    assert ws.numel() >= cp.workspace_size(prob, cp.OP_BWD_DS)
+    del ws
+    run.o, run.lse, run.dq, run.dk, run.dv = o, lse, dq, dk, dv
+    compare(cp, run, seqs={0, 63}, kv_heads={0, 7}, label="cfg3 ring ", bar="pages")
+    qi = torch.from_numpy(np.flatnonzero(rows_of(w))).cuda()
+    for t in (o, dq):
+        assert bool(torch.isfinite(t.index_select(0, qi)).all())
+    assert bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dv).all())
