@@ -187,6 +187,15 @@ __device__ __forceinline__ void dma16_at(const char* base, uint32_t off, uint32_
                : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint, for data read once (a stream that should not
+// push reused tiles out of L2).
+__device__ __forceinline__ void dma16_nt_at(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
 // 32-bit LDS address of a shared-memory pointer that is the same in every lane.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)CPATTN_LDS(const void, p));

@@ -24,7 +24,8 @@
 // wave's copies and LDS reads issue while the other's MFMAs run); for D <= 64 one wave
 // per slot.  Each 32-key step, the K tile (32 x D, kind-0 swizzle) and the slots' dS
 // blocks are copied into LDS three steps ahead (four stages: the dS stream comes from
-// HBM); the copy instructions are spread between the step's MFMAs rather than issued
+// HBM, read once, with the non-temporal hint so that the K tiles stay in L2); the copy
+// instructions are spread between the step's MFMAs rather than issued
 // together after the barrier, where all waves would queue on the address unit at once.
 // With 32x32x16 MFMAs:
 //   dQ^T += K^T dS^T    A = K^T by transposing reads of the K tile (as V^T in the forward),
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
       const int ti = kSplit == 2 ? part : (q >> 1);
       const int half = q & 1;
       const uint16_t* src = kb < nkb[ti] ? dsrc[ti] + (int64_t)kb * kBlkElems : a.ds;
-      dma16_at(uniform_ptr(src) + half * 1024, (uint32_t)lane * 16u,
+      dma16_nt_at(uniform_ptr(src) + half * 1024, (uint32_t)lane * 16u,
                lds_addr(lds_s[sb] + (slot * 2 + ti) * kBlkElems) + half * 1024);
     }
   };
