@@ -12,8 +12,17 @@ HBM.  `roofline` reports the dominant kernel, timed with HIP events on the
 stream it runs on; `cpu_baseline` times the FP64 oracle on a bounded sample of
 the same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu] [--no-ring]
-                       [--no-heads] [--no-a2a] [--recompute-dq]
+Timing follows the pages' protocol (page "Optimize context parallel attention
+layouts and gradient accumulation", "Current public integration": five warmups,
+then 50 timed iterations, eager, default allocator, no graphs and no profiler):
+`value` comes from the median of the per-step HIP-event times; the mean wall time
+of the K steps (bracketed by synchronizations) is reported beside it.  The other
+named workloads (full causal 8 x 2048 at D 128, the unequal padded rank share,
+the pair-biased rows) follow as extra result blocks with the same protocol, each
+with its own roofline and CPU baseline; they are not part of `value`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--extra 2,4,5]
+                       [--no-cpu] [--no-ring] [--no-heads] [--no-a2a] [--recompute-dq]
 """
 from __future__ import annotations
 
@@ -51,9 +60,13 @@ def visible_pairs(seq_lens, chunks, causal) -> int:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--extra", default="2,4,5",
+                    help="other named workloads timed after the headline one ('' for none)")
+    ap.add_argument("--extra-cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock/power samples")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-ring", action="store_true", help="skip the key-window ring-step timing")
@@ -297,6 +310,7 @@ def cpu_baseline(w, q, k, v, do, bias, budget_s):
     rng = np.random.default_rng(0)
     rng.shuffle(order)
     done_flop, t_used, samples = 0, 0.0, []
+    bs = None if bias is None else bias.cpu().numpy().astype(np.float64)
     for b, g in order:
         sub, qi, ki = W.subset(w, seqs={b})
         tq = torch.from_numpy(qi).cuda()
@@ -304,7 +318,6 @@ def cpu_baseline(w, q, k, v, do, bias, budget_s):
         f64 = lambda t, idx: t.index_select(0, idx).float().cpu().numpy().astype(np.float64)
         qs, dos = f64(q, tq), f64(do, tq)
         ks, vs = f64(k, tk), f64(v, tk)
-        bs = None if bias is None else bias.cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
         oracle.attention(qs, ks, vs, sub.seq_offsets, sub.seq_lens, sub.chunks, w.causal, w.scale,
                          bias=bs, do=dos, select=(None, {g}))
@@ -313,27 +326,140 @@ def cpu_baseline(w, q, k, v, do, bias, budget_s):
         samples.append((b, g))
         if t_used >= budget_s:
             break
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
     return {
         "value": done_flop / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
+        "blas_threads": int(threads), "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
         "sample": f"FP64 NumPy oracle fwd+bwd on {len(samples)} (sequence, KV-head group) pairs "
                   f"{samples[:4]}{'...' if len(samples) > 4 else ''}: {done_flop:.3e} FLOP in {t_used:.1f} s",
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
-                                   "(multi-GPU sharding is designed, not built)"}))
-        sys.exit(2)
-    import torch
-    import context_causal_gqa_cpattn_amd as cp
-    import workloads as W
+# ---------------------------------------------------------------- clock / power samples
 
-    cp.load()
-    w = W.make_config(args.config, materialize=False)
-    q, k, v, do, bias = W.draw_on_device(w, 2000 + args.config)
+_SAMPLER = r"""
+import json, select, subprocess, sys, time
+out = []
+if sys.stdin.readline().strip() == "start":
+    while True:
+        t = time.time()
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"],
+                               capture_output=True, text=True, timeout=20)
+            out.append({"t": t, "rc": r.returncode, "out": r.stdout[-20000:], "err": r.stderr[-500:]})
+        except Exception as e:
+            out.append({"t": t, "error": repr(e)})
+        if select.select([sys.stdin], [], [], max(0.0, 0.25 - (time.time() - t)))[0]:
+            break
+print(json.dumps(out))
+"""
+
+
+class ClockSampler:
+    """amd-smi clock and power readings taken while the timed steps run.  The sampler
+    is a child process started before this process touches the GPU; it runs
+    `amd-smi metric` between the "start" and "stop" lines it reads."""
+
+    def __init__(self, enabled=True):
+        import subprocess
+        self.p = None
+        if enabled:
+            try:
+                self.p = subprocess.Popen([sys.executable, "-c", _SAMPLER], stdin=subprocess.PIPE,
+                                          stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+            except Exception:
+                self.p = None
+
+    def start(self):
+        if self.p:
+            self.p.stdin.write("start\n")
+            self.p.stdin.flush()
+
+    def stop(self):
+        if not self.p:
+            return None
+        try:
+            out, _ = self.p.communicate("stop\n", timeout=60)
+            samples = json.loads(out.strip().splitlines()[-1])
+        except Exception as e:
+            try:
+                self.p.kill()
+            except Exception:
+                pass
+            return {"error": repr(e)}
+        return summarize_smi(samples)
+
+
+def summarize_smi(samples):
+    """Min / max of every clock (MHz) and power (W) value found in the amd-smi JSON."""
+    vals = {}
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            if "value" in x and isinstance(x["value"], (int, float)) and len(path) > 0:
+                vals.setdefault("/".join(path), []).append(float(x["value"]))
+                return
+            for k2, v2 in x.items():
+                walk(v2, path + [str(k2)])
+        elif isinstance(x, list):
+            for i2, v2 in enumerate(x):
+                walk(v2, path + ([str(i2)] if len(x) > 1 else []))
+        elif isinstance(x, (int, float)) and not isinstance(x, bool):
+            vals.setdefault("/".join(path), []).append(float(x))
+
+    n_ok = 0
+    for smp in samples:
+        try:
+            walk(json.loads(smp["out"]), [])
+            n_ok += 1
+        except Exception:
+            continue
+    keep = {k: [min(v), max(v)] for k, v in vals.items()
+            if any(t in k.lower() for t in ("gfx", "clk", "power")) and "min" not in k.lower().split("/")[-1]
+            and "max" not in k.lower().split("/")[-1] and "locked" not in k.lower()}
+    return {"samples": len(samples), "parsed": n_ok, "source": "amd-smi metric -g 0 -c -p", "min_max": keep}
+
+
+# ---------------------------------------------------------------- one workload
+
+def kernel_rooflines(w, per_kernel, pairs):
+    """Achieved rate of each attention kernel against its bound: MFMA kernels against
+    the dense BF16 peak (algorithmic FLOP: 4D forward, 8D dK/dV, 2D dQ per visible pair
+    per head), and the dS-stream dQ against HBM as well."""
+    D = w.head_dim
+    algo = {"fwd": 4 * D, "dkdv": 8 * D, "dq": 2 * D}
+    out = {}
+    for n, f in algo.items():
+        if n in per_kernel and per_kernel[n] > 0:
+            t = pairs * f / (per_kernel[n] * 1e-3) / 1e12
+            out[n] = {"tflops": round(t, 2), "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
+def ds_store_bytes(w):
+    """Stored dS: one 2 KB block per (32-query tile, head, 32-key block with a visible pair)."""
+    n = 0
+    for b, r0, pos0, cnt in w.chunks:
+        L = int(w.seq_lens[b])
+        for t in range(-(-int(cnt) // 32)):
+            last = int(pos0) + min(32 * (t + 1), int(cnt)) - 1
+            n += -(-min(L, last + 1 if w.causal else L) // 32)
+    return n * w.hq * 2048
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_workload(cp, torch, W, cfg, args, seed, headline):
+    """Warmups, then `steps` timed steps of the whole hot path on one workload."""
+    w = W.make_config(cfg, materialize=False)
+    progress(f"config {cfg} ({w.name}): drawing inputs")
+    q, k, v, do, bias = W.draw_on_device(w, seed)
     lay = cp.make_layout(w.seq_offsets, w.seq_lens, w.chunks, "cuda",
                          max_chunk_len=w.max_chunk_len, max_kv_len=w.max_kv_len)
     prob = cp.problem(lay, w.q_rows, w.kv_rows, w.hq, w.hkv, w.head_dim, w.causal, w.scale,
@@ -344,10 +470,11 @@ def main():
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     dbias = torch.empty_like(bias) if bias is not None else None
-    # With room for it (head_dim >= 64), dK/dV stores dS and dQ multiplies the stored dS.
+    # With room for it, dK/dV stores dS and dQ multiplies the stored dS.
     ws_ds = 0 if args.recompute_dq else cp.workspace_size(prob, cp.OP_BWD_DS)
     use_ds = ws_ds > 0
-    ws = torch.empty(max(ws_ds, cp.workspace_size(prob, cp.OP_BWD), 256), dtype=torch.uint8, device="cuda")
+    ws_bytes = max(ws_ds, cp.workspace_size(prob, cp.OP_BWD), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     err = cp.new_dev_err()
 
     names = ["fwd", "validate", "prepass", "dkdv", "dq"] + (["dbias"] if bias is not None else [])
@@ -373,37 +500,33 @@ def main():
             cp.bwd_dq(prob, lay, q, k, v, bias, lse, do, ws, dq, err)
         mark(5)
         if bias is not None:
-            if use_ds:
-                cp.bwd_dbias_ds(prob, lay, ws, dbias, err)
-            else:
-                cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, ws, dbias, err)
+            # dBias forms dS again in fp32 (as the fused backward does)
+            cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, ws, dbias, err)
             mark(6)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     cp.check(err)
+    progress(f"config {cfg}: {args.warmup} warmup steps done; timing {args.steps}")
 
     n_ev = len(names) + 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    sampler = headline.get("sampler")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
+    if sampler is not None:
+        sampler.start()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clocks = sampler.stop() if sampler is not None else None
     cp.check(err)
-    per_kernel = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
-                                     for i in range(args.steps)])) for j, n in enumerate(names)}
-    ms = wall * 1e3 / args.steps
-
-    copy = layout_copy_rates(cp, torch)
-    a2a = None if args.no_a2a else a2a_copy_rates(cp, torch)
-    ring = None if args.no_ring else ring_step_rates(
-        cp, torch, w, q, k, v, do, bias, lay, visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq * 14 * w.head_dim)
-
-    heads = None if args.no_heads else head_group_rates(
-        cp, torch, w, q, k, v, do, bias, lay, visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq * 14 * w.head_dim)
+    step_ms = [events[i][0].elapsed_time(events[i][-1]) for i in range(args.steps)]
+    per_kernel = {n: float(np.median([events[i][j].elapsed_time(events[i][j + 1])
+                                       for i in range(args.steps)])) for j, n in enumerate(names)}
+    ms = float(np.median(step_ms))
 
     pairs = visible_pairs(w.seq_lens, w.chunks, w.causal) * w.hq
     D = w.head_dim
@@ -412,64 +535,101 @@ def main():
     fwd_tflops = pairs * 4 * D / (per_kernel["fwd"] * 1e-3) / 1e12
     bwd_ms = sum(per_kernel[n] for n in names[1:])
     bwd_tflops = pairs * 10 * D / (bwd_ms * 1e-3) / 1e12
-    # dominant kernel: the longest one; its algorithmic FLOP per launch
+    # dominant kernel: the longest attention kernel; its algorithmic FLOP per launch
     algo = {"fwd": 4 * D, "dkdv": 8 * D, "dq": 2 * D}
     dom = max((n for n in per_kernel if n in algo), key=lambda n: per_kernel[n])
     dom_flop = pairs * algo[dom]
     achieved = dom_flop / (per_kernel[dom] * 1e-3) / 1e12
-    # pre-pass: reads Q, O, dO; writes Delta and the Q^T / dO^T tiles (32 queries, zero
-    # padded)
+    # pre-pass: reads Q, O, dO; writes Delta and the Q^T / dO^T tiles (32 queries, zero padded)
     n_tiles = int(sum(-(-int(n) // 32) for n in w.chunks[:, 3]))
-    pre_bytes = (3 * w.q_valid_rows().sum() * w.hq * D * 2 + 4 * w.q_valid_rows().sum() * w.hq
-                 + 2 * n_tiles * w.hq * 32 * D * 2)
-
-    # stored dS: one 2 KB block per (32-query tile, head, 32-key block with a visible pair),
-    # written by dK/dV and read by dQ
-    ds_bytes = 0
-    for b, r0, pos0, n in w.chunks:
-        L = int(w.seq_lens[b])
-        for t in range(-(-int(n) // 32)):
-            last = int(pos0) + min(32 * (t + 1), int(n)) - 1
-            ds_bytes += -(-min(L, last + 1 if w.causal else L) // 32)
-    ds_bytes *= w.hq * 2048
-
-    line = {
-        "metric": METRIC,
+    valid_q = int(sum(int(n) for n in w.chunks[:, 3]))
+    pre_bytes = 3 * valid_q * w.hq * D * 2 + 4 * valid_q * w.hq + 2 * n_tiles * w.hq * 32 * D * 2
+    ds_bytes = ds_store_bytes(w) if use_ds else 0
+    res = {
         "value": round(tflops, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic N(0,1) BF16 drawn on the device, seeded",
+        "ms_per_step_wall_mean": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "seq_len": int(w.seq_lens.max()),
                    "q_rows": w.q_rows, "kv_rows": w.kv_rows, "hq": w.hq, "hkv": w.hkv,
                    "head_dim": D, "causal": bool(w.causal), "chunks": w.num_chunks,
+                   "bias": bias is not None, "visible_pairs_x_heads": pairs,
                    "flop_per_step": flop, "parallelism": "none (one GPU: one rank's share)"},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_tflops, 2),
         "bwd_tflops": round(bwd_tflops, 2),
-        "kernel_ms": {n: round(x, 4) for n, x in per_kernel.items()},
+        "kernel_ms_median": {n: round(x, 4) for n, x in per_kernel.items()},
+        "kernel_rooflines": kernel_rooflines(w, per_kernel, pairs),
         "prepass_gbs": round(pre_bytes / (per_kernel["prepass"] * 1e-3) / 1e9, 1),
         "dq_path": "stored dS" if use_ds else "recompute",
-        "ds_bytes_per_step": ds_bytes if use_ds else 0,
-        "layout_copy": copy,
-        "a2a_copy": a2a,
-        "ring_step": ring,
-        "head_groups": heads,
-        "peak_mem_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
+        "ds_bytes_per_step": ds_bytes,
+        "bwd_workspace_bytes": ws_bytes,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(w.name, dom),
                      "algorithmic_flop_per_launch": dom_flop},
     }
+    if use_ds:
+        dq_gb = (ds_bytes + 2 * valid_q * w.hq * D) / (per_kernel["dq"] * 1e-3) / 1e9
+        res["dq_ds_gbs_algorithmic"] = round(dq_gb, 1)
+    if clocks is not None:
+        res["clock_power_during_timed_steps"] = clocks
+    progress(f"config {cfg}: {ms:.3f} ms per step (median), {tflops:.1f} TFLOP/s")
+    if headline.get("full"):
+        fl = pairs * 14 * D
+        res["layout_copy"] = layout_copy_rates(cp, torch)
+        res["a2a_copy"] = None if args.no_a2a else a2a_copy_rates(cp, torch)
+        res["ring_step"] = None if args.no_ring else ring_step_rates(cp, torch, w, q, k, v, do, bias, lay, fl)
+        res["head_groups"] = None if args.no_heads else head_group_rates(cp, torch, w, q, k, v, do, bias, lay, fl)
+    res["peak_mem_gib"] = round(torch.cuda.max_memory_allocated() / 2 ** 30, 2)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, do, bias, args.cpu_seconds)
+        progress(f"config {cfg}: CPU baseline (oracle)")
+        budget = args.cpu_seconds if headline.get("full") else args.extra_cpu_seconds
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, do, bias, budget)
+    del q, k, v, do, bias, o, lse, dq, dk, dv, dbias, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is designed, not built)"}))
+        sys.exit(2)
+    # started before anything here touches the GPU
+    sampler = ClockSampler(enabled=not args.no_clock)
+    import torch
+    import context_causal_gqa_cpattn_amd as cp
+    import workloads as W
+
+    cp.load()
+    main_res = time_workload(cp, torch, W, args.config, args, 2000 + args.config,
+                             {"full": True, "sampler": sampler})
+    extra = {}
+    for c in [int(x) for x in args.extra.split(",") if x.strip()]:
+        if c != args.config:
+            extra[f"config{c}"] = time_workload(cp, torch, W, c, args, 2000 + c, {})
+    line = {
+        "metric": METRIC,
+        "value": main_res.pop("value"),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) BF16 drawn on the device, seeded",
+        "timing": "median of per-step HIP-event times over the timed steps",
+    }
+    line.update(main_res)
+    line["other_workloads"] = extra
     print(json.dumps(line), flush=True)
 
 

@@ -597,7 +597,9 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
     if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s))) return r;
     if ((r = enqueue_dq(p, pl, a, dq, s))) return r;
   }
-  if (dbias) return use_ds ? enqueue_dbias_ds(p, pl, a, dbias, ws, s) : enqueue_dbias(p, pl, a, dbias, ws, s);
+  // dBias from dS formed in fp32 on either path (the stored dS is BF16, and a sum of
+  // many rows of it drifts by their rounding errors)
+  if (dbias) return enqueue_dbias(p, pl, a, dbias, ws, s);
   return CPATTN_OK;
 }
 

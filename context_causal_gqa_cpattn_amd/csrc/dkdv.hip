@@ -27,6 +27,14 @@
 // between the dV/dK products of tile i-1, so that VALU work issues while the matrix
 // cores are busy.  dK = scale dK^T and dV are rounded to BF16 once (STORE), or added to
 // the existing BF16 values and rounded once (ADD).
+//
+// Rounding P and dS to BF16 for the dV/dK products costs up to 2^-9 of each term.  Where
+// single probabilities are large (queries with few visible keys: the first positions of a
+// sequence, or a peaked row), those few terms dominate the largest dV/dK elements, and
+// their rounding comes on top of the final BF16 rounding of the output.  So where any P
+// of a wave's tile reaches 2^-5, the wave repeats that tile's dV/dK products with the
+// rounding residues P - bf16(P) and dS - bf16(dS) as B operands (exact to about 2^-17);
+// smaller probabilities add at most about 1e-3 in total.
 #include "common.h"
 #include "launch.h"
 
@@ -120,6 +128,27 @@ __device__ __forceinline__ void softmax_part(f32x16& s, f32x16& dp, int r0, cons
   }
 }
 
+// Probability from which a tile's dV/dK products are repeated with the BF16 residues.
+constexpr float kResidueP = 0.03125f;
+
+// The BF16 residues x - bf16(x) of accumulator elements [base, base + 8), given their
+// packed BF16 values hi (the difference is exact in fp32).
+__device__ __forceinline__ u32x4 residue_bf16x8(const f32x16& v, const u32x4& hi, int base) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_bf16x2(v[base + 2 * i] - bf16_lo(hi[i]), v[base + 2 * i + 1] - bf16_hi(hi[i]));
+  return r;
+}
+
+// Whether any probability of the wave's tile (P in the accumulator) reaches kResidueP.
+__device__ __forceinline__ uint32_t wave_has_large_p(const f32x16& p) {
+  float m = fmaxf(p[0], p[1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) m = fmaxf(m, p[r]);
+  return __builtin_amdgcn_ballot_w64(m >= kResidueP) != 0 ? 1u : 0u;
+}
+
 }  // namespace
 
 // S and dP products in arch VGPRs.  At D = 256 the dK^T/dV^T accumulators fill all 256
@@ -138,6 +167,209 @@ __device__ __forceinline__ void mfma32_v(f32x16& c, u32x4 a, u32x4 b) {
 }
 __device__ __forceinline__ void sdp_fence(f32x16& s, f32x16& dp) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s), "+v"(dp));
+}
+
+// The residue products of one tile, dV^T += dO^T rp and dK^T += Q^T rd for every 32-row
+// block, only when flag (wave-uniform) is non-zero.  The branch and the products are one
+// assembly block: the compiler then sees no control flow around the accumulators (at
+// D = 256 they take all 256 accumulation registers, and with a branch around compiler
+// products it shuffled them through the arch registers and spilled), and the common case
+// costs one taken branch per step.  The block reads its A operands itself (16-byte reads
+// of the transposed tiles at the lane addresses a0 / a1 of k-steps 0 / 1; the dO^T tile
+// is TB bytes after the Q^T tile, block b 2048 bytes after block 0), two blocks' reads in
+// flight, and runs before the tile's ordinary products, so that the last writer of every
+// accumulator is a product the compiler placed (and whose hazards it tracks); consecutive
+// products accumulating into exactly the same registers need no wait states.  The
+// s_waitcnt at entry drains the compiler's outstanding LDS / scalar loads, so the counts
+// inside refer to this block's reads only.
+template <int NB, int TB>
+__device__ __forceinline__ void residue_products(f32x16 (&dvt)[NB], f32x16 (&dkt)[NB], uint32_t a0,
+                                                 uint32_t a1, const u32x4 (&rp)[2], const u32x4 (&rd)[2],
+                                                 uint32_t flag_in) {
+  static_assert(TB + (NB - 1) * 2048 < 65536, "ds_read offsets are 16 bits");
+  const uint32_t flag = __builtin_amdgcn_readfirstlane(flag_in);
+  u32x4 t[4], u[4];
+  (void)u;
+  if constexpr (NB == 1) {
+    asm volatile(
+        "s_cmp_eq_u32 %[flag], 0\n\t"
+        "s_cbranch_scc1 9f\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 1\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq0]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq0]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t0], %[rp0], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t1], %[rp1], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t2], %[rd0], %[dk0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t3], %[rd1], %[dk0]\n\t"
+        "9:"
+        : [dv0] "+a"(dvt[0]), [dk0] "+a"(dkt[0]), [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3])
+        : [a0] "v"(a0), [a1] "v"(a1), [rp0] "v"(rp[0]), [rp1] "v"(rp[1]), [rd0] "v"(rd[0]), [rd1] "v"(rd[1]), [flag] "s"(flag), [od0] "i"(TB + 0 * 2048), [oq0] "i"(0 * 2048)
+        : "scc");
+  }
+  if constexpr (NB == 2) {
+    asm volatile(
+        "s_cmp_eq_u32 %[flag], 0\n\t"
+        "s_cbranch_scc1 9f\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 1\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq0]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq0]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[od1]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[od1]\n\t"
+        "ds_read_b128 %[u2], %[a0] offset:%c[oq1]\n\t"
+        "ds_read_b128 %[u3], %[a1] offset:%c[oq1]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t0], %[rp0], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t1], %[rp1], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t2], %[rd0], %[dk0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t3], %[rd1], %[dk0]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv1], %[u0], %[rp0], %[dv1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv1], %[u1], %[rp1], %[dv1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk1], %[u2], %[rd0], %[dk1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk1], %[u3], %[rd1], %[dk1]\n\t"
+        "9:"
+        : [dv0] "+a"(dvt[0]), [dk0] "+a"(dkt[0]), [dv1] "+a"(dvt[1]), [dk1] "+a"(dkt[1]), [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [u0] "=&v"(u[0]), [u1] "=&v"(u[1]), [u2] "=&v"(u[2]), [u3] "=&v"(u[3])
+        : [a0] "v"(a0), [a1] "v"(a1), [rp0] "v"(rp[0]), [rp1] "v"(rp[1]), [rd0] "v"(rd[0]), [rd1] "v"(rd[1]), [flag] "s"(flag), [od0] "i"(TB + 0 * 2048), [oq0] "i"(0 * 2048), [od1] "i"(TB + 1 * 2048), [oq1] "i"(1 * 2048)
+        : "scc");
+  }
+  if constexpr (NB == 4) {
+    asm volatile(
+        "s_cmp_eq_u32 %[flag], 0\n\t"
+        "s_cbranch_scc1 9f\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 1\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq0]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq0]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[od1]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[od1]\n\t"
+        "ds_read_b128 %[u2], %[a0] offset:%c[oq1]\n\t"
+        "ds_read_b128 %[u3], %[a1] offset:%c[oq1]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t0], %[rp0], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t1], %[rp1], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t2], %[rd0], %[dk0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t3], %[rd1], %[dk0]\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od2]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od2]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq2]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq2]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv1], %[u0], %[rp0], %[dv1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv1], %[u1], %[rp1], %[dv1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk1], %[u2], %[rd0], %[dk1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk1], %[u3], %[rd1], %[dk1]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[od3]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[od3]\n\t"
+        "ds_read_b128 %[u2], %[a0] offset:%c[oq3]\n\t"
+        "ds_read_b128 %[u3], %[a1] offset:%c[oq3]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv2], %[t0], %[rp0], %[dv2]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv2], %[t1], %[rp1], %[dv2]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk2], %[t2], %[rd0], %[dk2]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk2], %[t3], %[rd1], %[dk2]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv3], %[u0], %[rp0], %[dv3]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv3], %[u1], %[rp1], %[dv3]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk3], %[u2], %[rd0], %[dk3]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk3], %[u3], %[rd1], %[dk3]\n\t"
+        "9:"
+        : [dv0] "+a"(dvt[0]), [dk0] "+a"(dkt[0]), [dv1] "+a"(dvt[1]), [dk1] "+a"(dkt[1]), [dv2] "+a"(dvt[2]), [dk2] "+a"(dkt[2]), [dv3] "+a"(dvt[3]), [dk3] "+a"(dkt[3]), [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [u0] "=&v"(u[0]), [u1] "=&v"(u[1]), [u2] "=&v"(u[2]), [u3] "=&v"(u[3])
+        : [a0] "v"(a0), [a1] "v"(a1), [rp0] "v"(rp[0]), [rp1] "v"(rp[1]), [rd0] "v"(rd[0]), [rd1] "v"(rd[1]), [flag] "s"(flag), [od0] "i"(TB + 0 * 2048), [oq0] "i"(0 * 2048), [od1] "i"(TB + 1 * 2048), [oq1] "i"(1 * 2048), [od2] "i"(TB + 2 * 2048), [oq2] "i"(2 * 2048), [od3] "i"(TB + 3 * 2048), [oq3] "i"(3 * 2048)
+        : "scc");
+  }
+  if constexpr (NB == 8) {
+    asm volatile(
+        "s_cmp_eq_u32 %[flag], 0\n\t"
+        "s_cbranch_scc1 9f\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 1\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od0]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq0]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq0]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[od1]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[od1]\n\t"
+        "ds_read_b128 %[u2], %[a0] offset:%c[oq1]\n\t"
+        "ds_read_b128 %[u3], %[a1] offset:%c[oq1]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t0], %[rp0], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv0], %[t1], %[rp1], %[dv0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t2], %[rd0], %[dk0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk0], %[t3], %[rd1], %[dk0]\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od2]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od2]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq2]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq2]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv1], %[u0], %[rp0], %[dv1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv1], %[u1], %[rp1], %[dv1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk1], %[u2], %[rd0], %[dk1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk1], %[u3], %[rd1], %[dk1]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[od3]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[od3]\n\t"
+        "ds_read_b128 %[u2], %[a0] offset:%c[oq3]\n\t"
+        "ds_read_b128 %[u3], %[a1] offset:%c[oq3]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv2], %[t0], %[rp0], %[dv2]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv2], %[t1], %[rp1], %[dv2]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk2], %[t2], %[rd0], %[dk2]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk2], %[t3], %[rd1], %[dk2]\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od4]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od4]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq4]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq4]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv3], %[u0], %[rp0], %[dv3]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv3], %[u1], %[rp1], %[dv3]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk3], %[u2], %[rd0], %[dk3]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk3], %[u3], %[rd1], %[dk3]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[od5]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[od5]\n\t"
+        "ds_read_b128 %[u2], %[a0] offset:%c[oq5]\n\t"
+        "ds_read_b128 %[u3], %[a1] offset:%c[oq5]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv4], %[t0], %[rp0], %[dv4]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv4], %[t1], %[rp1], %[dv4]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk4], %[t2], %[rd0], %[dk4]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk4], %[t3], %[rd1], %[dk4]\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[od6]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[od6]\n\t"
+        "ds_read_b128 %[t2], %[a0] offset:%c[oq6]\n\t"
+        "ds_read_b128 %[t3], %[a1] offset:%c[oq6]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv5], %[u0], %[rp0], %[dv5]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv5], %[u1], %[rp1], %[dv5]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk5], %[u2], %[rd0], %[dk5]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk5], %[u3], %[rd1], %[dk5]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[od7]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[od7]\n\t"
+        "ds_read_b128 %[u2], %[a0] offset:%c[oq7]\n\t"
+        "ds_read_b128 %[u3], %[a1] offset:%c[oq7]\n\t"
+        "s_waitcnt lgkmcnt(4)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv6], %[t0], %[rp0], %[dv6]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv6], %[t1], %[rp1], %[dv6]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk6], %[t2], %[rd0], %[dk6]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk6], %[t3], %[rd1], %[dk6]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv7], %[u0], %[rp0], %[dv7]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dv7], %[u1], %[rp1], %[dv7]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk7], %[u2], %[rd0], %[dk7]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[dk7], %[u3], %[rd1], %[dk7]\n\t"
+        "9:"
+        : [dv0] "+a"(dvt[0]), [dk0] "+a"(dkt[0]), [dv1] "+a"(dvt[1]), [dk1] "+a"(dkt[1]), [dv2] "+a"(dvt[2]), [dk2] "+a"(dkt[2]), [dv3] "+a"(dvt[3]), [dk3] "+a"(dkt[3]), [dv4] "+a"(dvt[4]), [dk4] "+a"(dkt[4]), [dv5] "+a"(dvt[5]), [dk5] "+a"(dkt[5]), [dv6] "+a"(dvt[6]), [dk6] "+a"(dkt[6]), [dv7] "+a"(dvt[7]), [dk7] "+a"(dkt[7]), [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]), [u0] "=&v"(u[0]), [u1] "=&v"(u[1]), [u2] "=&v"(u[2]), [u3] "=&v"(u[3])
+        : [a0] "v"(a0), [a1] "v"(a1), [rp0] "v"(rp[0]), [rp1] "v"(rp[1]), [rd0] "v"(rd[0]), [rd1] "v"(rd[1]), [flag] "s"(flag), [od0] "i"(TB + 0 * 2048), [oq0] "i"(0 * 2048), [od1] "i"(TB + 1 * 2048), [oq1] "i"(1 * 2048), [od2] "i"(TB + 2 * 2048), [oq2] "i"(2 * 2048), [od3] "i"(TB + 3 * 2048), [oq3] "i"(3 * 2048), [od4] "i"(TB + 4 * 2048), [oq4] "i"(4 * 2048), [od5] "i"(TB + 5 * 2048), [oq5] "i"(5 * 2048), [od6] "i"(TB + 6 * 2048), [oq6] "i"(6 * 2048), [od7] "i"(TB + 7 * 2048), [oq7] "i"(7 * 2048)
+        : "scc");
+  }
+
 }
 
 template <int D, bool CAUSAL, bool BIAS>
@@ -268,8 +500,18 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   };
 
   u32x4 pp[2] = {}, pd[2] = {};  // packed P and dS of the previous tile
+  u32x4 rp[2] = {}, rd[2] = {};  // their BF16 residues, when res_prev
   int buf = 0, pbuf = 0;
   bool have_prev = false;
+  uint32_t res_prev = 0;
+  auto nop = [](int) {};
+  // Residue products of the tile in buffer pb (lane addresses of its k-step 0 / 1 operands).
+  const uint32_t res_a0 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off0;
+  const uint32_t res_a1 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off1;
+  auto residue = [&](int pb, const u32x4 (&rp)[2], const u32x4 (&rd)[2], uint32_t flag) {
+    const uint32_t boff = (uint32_t)pb * (2u * TE * 2u);
+    residue_products<NB, TE * 2>(dvt, dkt, res_a0 + boff, res_a1 + boff, rp, rd, flag);
+  };
   while (have) {
     QTileIter nxt = cur;
     const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
@@ -350,6 +592,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
                                             nq, tile_pos0, bias_cur);
     };
     if (PIPE && have_prev) {
+      residue(pbuf, rp, rd, res_prev);
       dvdk(pbuf, pp, pd, sm_block);
     } else if (PIPE || (nk < 32) || !wave_in_window || (nq < kTq) || (CAUSAL && tile_pos0 < wkey0 + 31)) {
 #pragma unroll
@@ -363,7 +606,27 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     pp[1] = to_bf16x8(s, 8);
     pd[0] = to_bf16x8(dp, 0);
     pd[1] = to_bf16x8(dp, 8);
-    if (!PIPE) dvdk(buf, pp, pd, [](int) {});
+    const uint32_t res_cur = wave_has_large_p(s);
+    if (PIPE) {
+      if (res_cur) {  // kept for the next step, with pp / pd
+        rp[0] = residue_bf16x8(s, pp[0], 0);
+        rp[1] = residue_bf16x8(s, pp[1], 8);
+        rd[0] = residue_bf16x8(dp, pd[0], 0);
+        rd[1] = residue_bf16x8(dp, pd[1], 8);
+      }
+    } else {
+      // the residues live only within this step (at D = 256 every register is taken
+      // during the S/dP products)
+      u32x4 sp[2] = {}, sd[2] = {};
+      if (res_cur) {
+        sp[0] = residue_bf16x8(s, pp[0], 0);
+        sp[1] = residue_bf16x8(s, pp[1], 8);
+        sd[0] = residue_bf16x8(dp, pd[0], 0);
+        sd[1] = residue_bf16x8(dp, pd[1], 8);
+      }
+      residue(buf, sp, sd, res_cur);
+      dvdk(buf, pp, pd, nop);
+    }
 
     wait_vm_all();
     if (have_next && tid < kTq) {
@@ -391,10 +654,14 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     }
     have = have_next;
     have_prev = true;
+    res_prev = res_cur;
     pbuf = buf;
     buf = nbuf;
   }
-  if (PIPE && have_prev) dvdk(pbuf, pp, pd, [](int) {});
+  if (PIPE && have_prev) {
+    residue(pbuf, rp, rd, res_prev);
+    dvdk(pbuf, pp, pd, nop);
+  }
 
   if (!key_ok) return;
   // element r of block blk is dimension 32 blk + 8 (r / 4) + 4 hl + r % 4

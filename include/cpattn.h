@@ -186,7 +186,9 @@ int cpattn_merge(const cpattn_problem* p, const int32_t* q_chunk_map, const void
  *  dkv_accumulate = 1 (second addition): the existing BF16 dK/dV values are
  *  read, this call's contribution is added in fp32 and the sum is rounded once.
  *  dbias (fp32, with a bias only, may be NULL to skip it) is STORED: the sum of
- *  dS over every chunk row, unscaled.  O and LSE are the forward's outputs.
+ *  dS over every chunk row, unscaled, with dS formed in fp32 (cpattn_bwd_dbias,
+ *  whichever dQ path is taken: a sum over many rows of BF16-rounded dS drifts by
+ *  the rows' rounding errors).  O and LSE are the forward's outputs.
  *  ws must hold cpattn_workspace_size(p, CPATTN_OP_BWD) bytes.  When it holds
  *  cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes (nonzero), dK/dV stores dS in
  *  it and dQ multiplies the stored dS (cpattn_bwd_dkdv_ds, cpattn_bwd_dq_ds);
@@ -241,10 +243,11 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
  *      for Hopper (H200) architecture?": the pair bias is shared by every row, so its
  *      gradient is a reduction over rows).  The rows are summed in the same fixed
  *      partition units and order as cpattn_bwd_dbias; the result differs from it only
- *      by the BF16 rounding of the stored dS.  ws must hold the dBias partial sums and
- *      the dS store (cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes); reads the
- *      descriptors and the dS store only.  cpattn_bwd computes dBias this way whenever
- *      it uses the dS store. */
+ *      by the BF16 rounding of the stored dS (about 2^-9 |dS| per row, adding up over
+ *      the rows like a random walk), in exchange for reading 2 bytes per pair instead
+ *      of forming S and dP again.  ws must hold the dBias partial sums and the dS
+ *      store (cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes); reads the
+ *      descriptors and the dS store only. */
 int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
                        const void* o, const void* dout, void* ws, size_t ws_bytes,
                        const int32_t* dev_err, cpattn_stream_t stream);

@@ -2,14 +2,15 @@
 
 Tolerances (BF16 outputs O, dQ, dK, dV and fp32 dBias, against the FP64 oracle):
   * relative L2 error of the whole compared tensor <= 1e-2;
-  * per element |got - ref| <= max(2e-2, ulp_bf16(ref)): the max-abs bar of
-    2e-2 wherever BF16's spacing at |ref| is finer than it (|ref| < 4), and one
-    BF16 ulp where the format itself is coarser (|ref| >= 4: spacing 2^-5 and
-    up, so rounding even the exact value to BF16 costs up to 0.0156 and one
-    rounded BF16 operand in a contraction adds a few 1e-3 on top);
+  * per element |got - ref| <= 2e-2 wherever |ref| < 8;
+  * per element |got - ref| <= one BF16 ulp of ref where |ref| >= 8: there the
+    format's spacing is 2^-4 or more, so rounding even the exact value to BF16
+    can cost 2^-5 = 0.031 > 2e-2 (below 8 the rounding costs at most 0.0156,
+    inside the bar, so no relaxation is taken there);
   * LSE (fp32): max-abs <= 1e-3.
-The plain max-abs and the pages' own form |err| <= 0.025 + 0.025 |ref| are
-reported alongside.
+Every comparison prints one line (name, element count, max-abs, max-abs over
+|ref| < 8, count of |ref| >= 8, rel-L2, count over the pages' own form
+|err| <= 0.025 + 0.025 |ref|) so that the run's log carries the margins.
 
 That bar is stated for the five named workloads.  Shapes outside them (the
 sweeps over group sizes, head dims and chunk maps) use the full-tensor bar the
@@ -26,7 +27,10 @@ import workloads as W
 ATOL = 2e-2
 REL_L2 = 1e-2
 LSE_ATOL = 1e-3
-BIG = 4.0
+BIG = 8.0
+
+# Every margin line of this process, for the end-of-run summary (tests/conftest.py).
+MARGINS: list = []
 
 
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
@@ -53,6 +57,11 @@ def assert_close(name: str, got: np.ndarray, ref: np.ndarray, atol=ATOL, rel_l2=
             "n_big": int((~small).sum()),
             "big_over_ulp": big_bad, "rel_l2": rl2,
             "pages_form_fail": int(np.count_nonzero(err > 0.025 + 0.025 * np.abs(ref)))}
+    line = (f"{name} bar={bar} n={info['n']} max_abs={info['max_abs']:.5f} "
+            f"max_abs_small={max_small:.5f} n_big={info['n_big']} big_over_ulp={big_bad} "
+            f"rel_l2={rl2:.5f} pages_form_fail={info['pages_form_fail']}")
+    MARGINS.append((name, bar, max_small, rl2, line))
+    print("[margin] " + line, flush=True)
     if bar == "pages":
         assert info["pages_form_fail"] == 0, f"{name}: elements over 0.025+0.025|ref| ({info})"
         assert rl2 < 0.02, f"{name}: relative RMS {rl2} >= 0.02 ({info})"
@@ -68,6 +77,9 @@ def assert_lse_close(name, got, ref, atol=LSE_ATOL):
     ref = np.asarray(ref, np.float64).ravel()
     assert np.isfinite(got).all(), f"{name}: non-finite LSE"
     e = float(np.abs(got - ref).max()) if got.size else 0.0
+    line = f"{name} n={got.size} lse_max_abs={e:.2e}"
+    MARGINS.append((name, "lse", e, 0.0, line))
+    print("[margin] " + line, flush=True)
     assert e <= atol, f"{name}: LSE max abs err {e} > {atol}"
     return e
 

@@ -144,14 +144,19 @@ def test_config5_sampled_and_dbias_positions(gpu_lib):
     run.forward()
     run.backward()
     compare(gpu_lib, run, seqs={0, 1023}, label="cfg5 ")
-    # dBias at a few positions, summed over all 1024 rows: single-row chunks of every row
-    positions = [0, 511, 1023]
-    chunks = [(i, 1024 * i + p, p, 1) for i in range(1024) for p in positions]
+    # dBias at 80 query positions, summed over all 1024 rows: four runs of positions per
+    # row ([0, 24), [360, 376), [600, 616), [1000, 1024)), which cover both ends, every
+    # residue mod 32 (the dBias tile height) at least twice, and four of its 32 tiles
+    runs = [(0, 24), (360, 16), (600, 16), (1000, 24)]
+    positions = [p for p0, n in runs for p in range(p0, p0 + n)]
+    assert len({p % 32 for p in positions}) == 32
+    chunks = [(i, 1024 * i + p0, p0, n) for i in range(1024) for p0, n in runs]
     import workloads
     sub, _, _ = workloads.subset(w, chunks=chunks)
     ref_b = run_oracle(sub)
     got = run.dbias.cpu().numpy()
     assert_close("cfg5 dBias", got[:, positions, :], ref_b["dbias"][:, positions, :])
+
     assert np.isfinite(got).all()
 
 
@@ -256,10 +261,11 @@ def test_stored_ds_steps_match_fused_entry_over_stale_workspace(gpu_lib):
 
 
 def test_stored_ds_dbias_steps_match_fused_entry_over_stale_workspace(gpu_lib):
-    """With a bias, the step entry points (pre-pass, dK/dV storing dS, dQ and dBias from
-    the stored dS) give the fused entry point's results bit for bit over a workspace
-    prefilled with NaN bytes; chunks starting on and off 32-position boundaries (the
-    block-wise and the element-wise sums)."""
+    """With a bias, the step entry points (pre-pass, dK/dV storing dS, dQ from the stored
+    dS, dBias forming dS again in fp32) give the fused entry point's results bit for bit
+    over a workspace prefilled with NaN bytes; dBias summed from the stored dS (chunks
+    starting on and off 32-position boundaries: the block-wise and the element-wise
+    sums) matches the oracle."""
     import torch
     lens = [96, 70, 64]
     chunks = [(0, 0, 96), (1, 5, 40), (2, 32, 32)]
@@ -282,7 +288,9 @@ def test_stored_ds_dbias_steps_match_fused_entry_over_stale_workspace(gpu_lib):
     gpu_lib.bwd_dkdv_ds(prob, run.layout, run.q, run.k, run.v, run.bias, run.lse, run.do, ws, dk, dv,
                         False, err)
     gpu_lib.bwd_dq_ds(prob, run.layout, run.k, ws, dq, err)
-    gpu_lib.bwd_dbias_ds(prob, run.layout, ws, dbias, err)
+    dbias_ds = torch.full_like(run.bias, float("nan"))
+    gpu_lib.bwd_dbias_ds(prob, run.layout, ws, dbias_ds, err)
+    gpu_lib.bwd_dbias(prob, run.layout, run.q, run.k, run.v, run.bias, run.lse, run.do, ws, dbias, err)
     torch.cuda.synchronize()
     gpu_lib.check(err)
     qi = torch.from_numpy(np.flatnonzero(rows_of(w))).cuda()
@@ -291,8 +299,9 @@ def test_stored_ds_dbias_steps_match_fused_entry_over_stale_workspace(gpu_lib):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
     assert torch.equal(dbias_f.view(torch.int32), dbias.view(torch.int32))
     run.dq, run.dk, run.dv, run.dbias = dq, dk, dv, dbias
-    info, ref, _ = compare(gpu_lib, run, bar="pages")
-    assert_close("dBias from stored dS", dbias.cpu().numpy(), ref["dbias"], bar="pages")
+    info, ref, _ = compare(gpu_lib, run)
+    assert_close("dBias", dbias.cpu().numpy(), ref["dbias"])
+    assert_close("dBias from stored dS", dbias_ds.cpu().numpy(), ref["dbias"], bar="pages")
 
 
 def test_run_to_run_bitwise_identical(gpu_lib):
