@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libcpattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 OP_FWD, OP_BWD, OP_BWD_DS = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CPATTN_NOALLOC_SCRATCH_BYTES
 DEV_ERR_BITS = {
     0x01: "ESEQ_LEN", 0x02: "ESEQ_RANGE", 0x04: "ECHUNK_SEQ", 0x08: "ECHUNK_ROWS",
     0x10: "ECHUNK_POS", 0x20: "EBIAS", 0x40: "ELAYOUT",
@@ -34,7 +35,7 @@ EXPORTS = [
     "cpattn_bwd_dbias_ds", "cpattn_pack",
     "cpattn_unpack", "cpattn_fwd_window", "cpattn_merge", "cpattn_bwd_window",
     "cpattn_a2a_split_heads", "cpattn_a2a_merge_heads", "cpattn_a2a_scatter_rows",
-    "cpattn_a2a_gather_rows",
+    "cpattn_a2a_gather_rows", "cpattn_bwd_noalloc",
 ]
 
 
@@ -98,6 +99,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "cpattn_fwd": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
         "cpattn_bwd": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                        ctypes.c_int, _vp, sz, _vp, _vp],
+        "cpattn_bwd_noalloc": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               ctypes.c_int, _vp, _vp],
         "cpattn_bwd_prepass": [P, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
         "cpattn_bwd_dkdv": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp,
                             ctypes.c_int, _vp, _vp],
@@ -324,6 +327,29 @@ def bwd(q, k, v, layout: Layout, o, lse, do, causal: bool = True, scale: Optiona
                           _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
                           1 if dkv_accumulate else 0, _ptr(ws), ws.numel(), _ptr(dev_err),
                           _stream(stream)))
+    return dq, dk, dv, dbias, dev_err
+
+
+def bwd_noalloc(q, k, v, layout: Layout, o, lse, do, dq, dk, dv, causal: bool = True,
+                scale: Optional[float] = None, bias=None, dbias=None, dkv_accumulate: bool = False,
+                dev_err=None, stream=None):
+    """cpattn_bwd_noalloc: the backward with the library's static scratch as workspace.
+    The caller passes every output (nothing is allocated here either)."""
+    torch = _torch()
+    lib = load()
+    prob = _prob_for(q, k, v, layout, causal, scale, bias)
+    _need(o, "o", torch.bfloat16, q.shape, prob.q_head_pitch)
+    _need(do, "do", torch.bfloat16, q.shape, prob.q_head_pitch)
+    _need(lse, "lse", torch.float32, (prob.hq, prob.q_rows))
+    for n, t, ref, pt in (("dq", dq, q, prob.q_head_pitch), ("dk", dk, k, prob.kv_head_pitch),
+                          ("dv", dv, v, prob.kv_head_pitch)):
+        _need(t, n, torch.bfloat16, ref.shape, pt)
+    if dev_err is None:
+        raise ValueError("bwd_noalloc needs a caller-provided dev_err")
+    _check(lib.cpattn_bwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(layout.seq_offsets),
+                                  _ptr(layout.seq_lens), _ptr(layout.chunks), _ptr(bias), _ptr(o), _ptr(lse),
+                                  _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
+                                  1 if dkv_accumulate else 0, _ptr(dev_err), _stream(stream)))
     return dq, dk, dv, dbias, dev_err
 
 

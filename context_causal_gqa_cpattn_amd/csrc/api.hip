@@ -311,6 +311,10 @@ const char* cpattn_status_str(int status) {
 
 const char* cpattn_last_error(void) { return g_last_error.c_str(); }
 
+__attribute__((visibility("hidden"))) int cpattn_internal_fail(int status, const char* msg) {
+  return fail(status, "%s", msg);
+}
+
 int cpattn_version(void) { return 10000; }
 
 size_t cpattn_workspace_size(const cpattn_problem* p, int op) {

@@ -17,7 +17,9 @@
  * Conventions shared by every entry point
  * ----------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *    allocates no memory and keeps no state between calls.
+ *    allocates no memory and keeps no state between calls, except the static
+ *    scratch array of cpattn_bwd_noalloc (part of its code object, one per GPU)
+ *    and that array's device address, looked up once per GPU.
  *  - BF16 tensors are passed as raw 16-bit patterns, contiguous, head dim
  *    innermost, 16-byte aligned:
  *        Q, O, dO, dQ : [q_rows,  hq,  head_dim]
@@ -277,6 +279,29 @@ int cpattn_bwd_dq_ds(const cpattn_problem* p, const void* k, const int32_t* seq_
 int cpattn_bwd_dbias_ds(const cpattn_problem* p, const int32_t* seq_offsets, const int32_t* seq_lens,
                         const int32_t* q_chunk_map, void* ws, size_t ws_bytes, float* dbias,
                         const int32_t* dev_err, cpattn_stream_t stream);
+
+/* Bytes of the static scratch array behind cpattn_bwd_noalloc (64 MiB per GPU). */
+#define CPATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* cpattn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, outputs, checks and kernels as cpattn_bwd; the
+ * workspace is a static device array of CPATTN_NOALLOC_SCRATCH_BYTES held by each GPU
+ * the library runs on until the process ends.  It takes the stored-dS backward when
+ * cpattn_workspace_size(p, CPATTN_OP_BWD_DS) fits in the array, else the backward that
+ * forms dS again for dQ when cpattn_workspace_size(p, CPATTN_OP_BWD) fits (results
+ * bit-identical to cpattn_bwd with a workspace of that size), else returns
+ * CPATTN_EUNSUPPORTED with nothing enqueued.  Calls no allocating routine; the first
+ * call on a device looks up the array's device address (hipGetSymbolAddress) with the
+ * current device, which must be the stream's.  Nothing in the array needs clearing
+ * between calls.  Calls that overlap in time on one GPU share the array and race:
+ * serialize them (one stream, or the caller's own ordering). */
+int cpattn_bwd_noalloc(const cpattn_problem* p, const void* q, const void* k, const void* v,
+                       const int32_t* seq_offsets, const int32_t* seq_lens,
+                       const int32_t* q_chunk_map, const float* bias, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       float* dbias, int dkv_accumulate, int32_t* dev_err,
+                       cpattn_stream_t stream);
 
 /* Layout copies ("Changes": vectorised BF16 pack/unpack copies that keep
  * physical sequence origins).  BHSD is [B, H, S_pitch, D]; THD is
