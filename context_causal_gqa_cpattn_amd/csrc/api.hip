@@ -119,8 +119,8 @@ struct Plan {
   bool ds_ok;            // the stored-dS backward applies (every supported head_dim, 32 to 256)
   int64_t kb_max;        // 32-key blocks per (tile slot, head) in the dS store
   int64_t off_ds, ds_bytes;
-  dim3 grid_fwd, grid_fwd1d, grid_prepass, grid_dkdv, grid_dbias, grid_dbias_ds, grid_dqds;
-  int bpc_fwd, bpc_prepass, bpc_dqds, kv_tiles;
+  dim3 grid_fwd, grid_fwd1d, grid_fwdk, grid_prepass, grid_dkdv, grid_dbias, grid_dbias_ds, grid_dqds;
+  int bpc_fwd, bpc_fwdk, bpc_prepass, bpc_dqds, kv_tiles;
 };
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -175,8 +175,10 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.bias_bytes = pl.bias ? (int64_t)p->hq * p->bias_len * p->bias_len * 4 : 0;
   pl.delta_bytes = round256(pl.stat_bytes);
 
+  // dQ (forming dS again): four waves of 32 rows; the forward: fwd_waves(D) waves
   const int64_t pos_per_wg = 32 * (4 / pl.hpw);
   pl.bpc_fwd = (int)cdiv(p->max_chunk_len, pos_per_wg);
+  pl.bpc_fwdk = (int)cdiv(p->max_chunk_len, (int64_t)32 * (fwd_waves(D) / pl.hpw));
   pl.bpc_prepass = (int)cdiv(p->max_chunk_len, kPrepassRows);
   pl.kv_tiles = (int)cdiv(p->max_kv_len, kDkdvKeys);
   const int64_t gx_fwd = (int64_t)p->num_chunks * pl.bpc_fwd;
@@ -188,6 +190,7 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.grid_fwd = dim3((unsigned)gx_fwd, (unsigned)(p->hq / pl.hpw));
   if (gx_fwd * (p->hq / pl.hpw) > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_fwd1d = dim3((unsigned)(gx_fwd * (p->hq / pl.hpw)));
+  pl.grid_fwdk = dim3((unsigned)((int64_t)p->num_chunks * pl.bpc_fwdk * (p->hq / pl.hpw)));
   if (gx_kv * p->hkv > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_dkdv = dim3((unsigned)(gx_kv * p->hkv));
 
@@ -364,7 +367,7 @@ int fwd_impl(const cpattn_problem* p, const void* q, const void* k, const void* 
 
   hipStream_t s = (hipStream_t)stream;
   if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
-  if (empty(pl.grid_fwd1d)) return CPATTN_OK;
+  if (empty(pl.grid_fwdk)) return CPATTN_OK;
   AttnArgs a = base_args(p, pl);
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -376,10 +379,10 @@ int fwd_impl(const cpattn_problem* p, const void* q, const void* k, const void* 
   a.seq_lens = seq_lens;
   a.chunks = q_chunk_map;
   a.dev_err = dev_err;
-  a.blocks_per_chunk = pl.bpc_fwd;
+  a.blocks_per_chunk = pl.bpc_fwdk;
   a.kv_lo = kv_lo;
   a.kv_hi = kv_hi;
-  return hip_check(launch_fwd(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwd1d, s), "forward launch");
+  return hip_check(launch_fwd(a, pl.D, p->causal != 0, pl.bias, pl.grid_fwdk, s), "forward launch");
 }
 }  // namespace
 

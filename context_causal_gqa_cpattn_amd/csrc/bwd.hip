@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(const AttnArgs a) {
   const int h = lin % a.hq;
   const int c = (lin / a.hq) / a.blocks_per_chunk;
   const int qt = (lin / a.hq) % a.blocks_per_chunk;
-  const Chunk ch = load_chunk(a.chunks, c);
+  const Chunk ch = load_chunk_uniform(a.chunks, c);
   const int r0 = qt * kTileQ;
   if (r0 >= ch.len) return;  // the whole workgroup
   const int nq = min(kTileQ, ch.len - r0);

@@ -279,34 +279,39 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t* t, int kr0, int db, int
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
-// Lane parts of the tr_frag addresses, computed once per kernel.  The fragment for
-// rows [16 st, +16) and columns [32 db, +32) of a tile sits at element
-// 16 st D + 128 (db / 4) + lo[db % 4] (and hi[...] for its second read): the swizzle
-// depends on the row mod 16 only and touches granule bits 0-3, so both st and db / 4
-// enter as constants.
+// Lane parts of the tr_frag addresses, computed once per kernel (three registers).  The
+// fragment for rows [16 st, +16) and columns [32 db, +32) of a tile sits at element
+// 16 st D + 128 (db / 4) + lo(db % 4), its second read hi_delta further on:
+//  - the swizzle depends on the row mod 16 only and touches granule bits 0-3, so st and
+//    db / 4 enter as constants;
+//  - granule 4 m + gsub of row rr (rr < 8) is stored at (4 m + gsub) ^ swz(rr), which
+//    splits into bits 2-3, m ^ t with t = swz(rr) >> 2, and bits 0-1 from the lane alone:
+//    lo(m) = base + 32 (m ^ t) elements;
+//  - the second read's rows are the first's + 8, whose swizzle is the first's with bit 1
+//    set (rows below 8 have it clear), and bit 1 of the granule index comes from the lane
+//    alone, so the two reads differ by one lane constant: 8 D + 16 elements when that bit
+//    is clear, 8 D - 16 when set.
 template <int D>
 struct TrOffsets {
   static constexpr int NM = (D / 32) < 4 ? (D / 32) : 4;
-  int lo[NM], hi[NM];
+  int base, t, hi_delta;
   __device__ __forceinline__ explicit TrOffsets(int lane) {
     const int rr = (lane >> 5) * 4 + ((lane & 15) >> 2);
     const int gsub = ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1);
     const int off = (lane & 1) * 4;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int gl = 4 * m + gsub;
-      lo[m] = rr * D + ((gl ^ swz<D>(rr)) << 3) + off;
-      hi[m] = (rr + 8) * D + ((gl ^ swz<D>(rr + 8)) << 3) + off;
-    }
+    base = rr * D + ((gsub ^ (swz<D>(rr) & 3)) << 3) + off;
+    t = swz<D>(rr) >> 2;
+    hi_delta = 8 * D + ((gsub & 2) ? -16 : 16);
   }
+  __device__ __forceinline__ int lo(int m) const { return base + ((m ^ t) << 5); }
 };
 
 // tr_frag(t, 16 st, db, lane) with the lane parts precomputed.
 template <int D>
 __device__ __forceinline__ u32x4 tr_frag_at(const uint16_t* t, const TrOffsets<D>& o, int st, int db) {
-  const uint16_t* b = t + st * 16 * D + (db >> 2) * 128;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + o.lo[db & 3]));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + o.hi[db & 3]));
+  const uint16_t* b = t + st * 16 * D + (db >> 2) * 128 + o.lo(db & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + o.hi_delta));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
@@ -345,12 +350,21 @@ __device__ __forceinline__ Chunk load_chunk(const int32_t* map, int c) {
   return Chunk{v.x, v.y, v.z, v.w};
 }
 
+// The same for a chunk index that is the same in every lane (from the block index or a
+// workgroup-uniform loop): the fields go to scalar registers, so that loops and tests on
+// them compile to scalar branches instead of exec-masked vector code, and take no VGPRs.
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ Chunk load_chunk_uniform(const int32_t* map, int c) {
+  const Chunk ch = load_chunk(map, c);
+  return Chunk{rfl(ch.seq), rfl(ch.q_row), rfl(ch.pos0), rfl(ch.len)};
+}
+
 // First chunk index whose seq is >= b (chunks are listed with non-decreasing seq).
 __device__ __forceinline__ int chunk_lower_bound(const int32_t* map, int num_chunks, int b) {
   int lo = 0, hi = num_chunks;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (map[4 * mid] < b) lo = mid + 1; else hi = mid;
+    if (rfl(map[4 * mid]) < b) lo = mid + 1; else hi = mid;
   }
   return lo;
 }

@@ -57,7 +57,7 @@ struct QTileIter {
 template <bool CAUSAL>
 __device__ __forceinline__ bool seek_chunk(const AttnArgs& a, QTileIter& it, int c_end, int key0) {
   for (; it.c < c_end; ++it.c) {
-    it.ch = load_chunk(a.chunks, it.c);
+    it.ch = load_chunk_uniform(a.chunks, it.c);
     const int first_row = CAUSAL ? max(0, key0 - it.ch.pos0) : 0;
     if (first_row < it.ch.len) {
       it.qt_first = first_row / kTq;
@@ -393,11 +393,11 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   const int rest = logical / a.kv_tiles;
   const int g = rest % a.hkv;
   const int b = rest / a.hkv;
-  const int L = a.seq_lens[b];
+  const int L = rfl(a.seq_lens[b]);
   const int wg_key0 = kt * kDkdvKeys;
   // no key of the tile in the sequence or in the key window [kv_lo, kv_hi)
   if (wg_key0 >= L || wg_key0 >= a.kv_hi || wg_key0 + kDkdvKeys <= a.kv_lo) return;
-  const int64_t koff = a.seq_offsets[b];
+  const int64_t koff = rfl(a.seq_offsets[b]);
   const int wkey0 = wg_key0 + wave * 32;
   const int nk = max(0, min(32, L - wkey0));
   const int key = wkey0 + n;  // this lane's key (column of S, dP, dK^T, dV^T)

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   const int rest = logical / a.blocks_per_chunk;
   const int hg = rest % n_hg;
   const int c = rest / n_hg;
-  const Chunk ch = load_chunk(a.chunks, c);
+  const Chunk ch = load_chunk_uniform(a.chunks, c);
   const int wg_pos = kRows * (kWavesQ / a.hpw);  // positions per workgroup
   const int wg_row0 = pb * wg_pos;
   if (wg_row0 >= ch.len) return;  // uniform over the workgroup, before any barrier
@@ -114,8 +114,8 @@ __global__ __launch_bounds__(kThreadsQ) void dq_kernel(const AttnArgs a) {
   const int kvh = h / a.group;
   const int row0 = wg_row0 + (wave / a.hpw) * kRows;  // first chunk row of this wave
   const int nrows = max(0, min(kRows, ch.len - row0));
-  const int L = a.seq_lens[ch.seq];
-  const int64_t koff = a.seq_offsets[ch.seq];
+  const int L = rfl(a.seq_lens[ch.seq]);
+  const int64_t koff = rfl(a.seq_offsets[ch.seq]);
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + wg_pos) - 1;
   // Keys [kv_lo, kv_end): the key window (the whole sequence without one), cut at the
   // workgroup's last position when causal.

@@ -99,15 +99,15 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   const int rest = logical / a.blocks_per_chunk;
   const int hg = rest % n_hg;
   const int c = rest / n_hg;
-  const Chunk ch = load_chunk(a.chunks, c);
+  const Chunk ch = load_chunk_uniform(a.chunks, c);
   const int wg_pos = 64 * (kSlots / a.hpw);  // positions per workgroup
   const int wg_row0 = pb * wg_pos;
   if (wg_row0 >= ch.len) return;  // uniform over the workgroup, before any barrier
   const int h = hg * a.hpw + (slot % a.hpw);
   const int kvh = h / a.group;
   const int row0 = wg_row0 + (slot / a.hpw) * 64;  // first chunk row of this slot (a tile start)
-  const int L = a.seq_lens[ch.seq];
-  const int64_t koff = a.seq_offsets[ch.seq];
+  const int L = rfl(a.seq_lens[ch.seq]);
+  const int64_t koff = rfl(a.seq_offsets[ch.seq]);
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + wg_pos) - 1;
   // Key blocks [kb_first, n_steps): those with a visible key, within the key window
   // [kv_lo, kv_hi) (the whole sequence without one).
@@ -170,15 +170,8 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
       const int db = part * NDB + j;
-      int lo = tro.lo[0], hi = tro.hi[0];
-#pragma unroll
-      for (int m = 1; m < TrOffsets<D>::NM; ++m)
-        if ((db & 3) == m) {
-          lo = tro.lo[m];
-          hi = tro.hi[m];
-        }
-      klo[j] = lo + (db >> 2) * 128;
-      khi[j] = hi + (db >> 2) * 128;
+      klo[j] = tro.lo(db & 3) + (db >> 2) * 128;
+      khi[j] = klo[j] + tro.hi_delta;
     }
   }
   auto kfrag = [&](const uint16_t* kt, int st, int j) {

@@ -25,7 +25,15 @@
 
 namespace cpattn {
 
-constexpr int kBN = 64;  // keys per KV tile
+// Keys per K/V tile and waves per workgroup.  D <= 128: 64-key tiles, four waves (the
+// tiles leave room for a second workgroup per CU).  D = 256: 32-key tiles and eight
+// waves, two per SIMD: a 64-key tile pair (128 KB of LDS) would leave one wave per SIMD,
+// and a tile now serves 256 query rows instead of 128, half the copied bytes per FLOP.
+template <int D>
+struct FwdShape {
+  static constexpr int BN = D == 256 ? 32 : 64;
+  static constexpr int NW = D == 256 ? 8 : 4;
+};
 
 // Scores of one 64-key tile in base 2 (+ bias), masked when MASK (keys outside
 // [lo, hi), and past the query position when causal); returns the lane max (four
@@ -38,7 +46,7 @@ constexpr int kBN = 64;  // keys per KV tile
 __device__ __forceinline__ void load_bias_tile(f32x4 (&bv)[8], const float* bias_row, int key0, int L,
                                                int kg, int bias_len) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb)  // bias only with 64-key tiles (D <= 128)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
@@ -53,12 +61,12 @@ __device__ __forceinline__ void load_bias_tile(f32x4 (&bv)[8], const float* bias
     }
 }
 
-template <bool BIAS, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const f32x4 (&btile)[8], int key0,
+template <bool BIAS, bool MASK, bool CAUSAL, int NKB>
+__device__ __forceinline__ void scale_tile(f32x16 (&s)[NKB], float c, const f32x4 (&btile)[8], int key0,
                                            int lo, int hi, int qpos, int kg, float& mx) {
   float mj[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kbi = key0 + kb * 32 + i * 8 + kg * 4;
@@ -79,9 +87,13 @@ __device__ __forceinline__ void scale_tile(f32x16 (&s)[2], float c, const f32x4 
 }
 
 template <int D, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int kBN = FwdShape<D>::BN;  // keys per K/V tile
+  constexpr int NW = FwdShape<D>::NW;   // waves per workgroup
+  constexpr int NKB = kBN / 32;         // 32-key blocks of S^T
   constexpr int NST = D / 16;  // 16-wide k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  static_assert(!BIAS || kBN == 64, "bias tiles are 64 keys");
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][kBN * D];
 
@@ -95,16 +107,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
   const int rest = logical / a.blocks_per_chunk;
   const int hg = rest % n_hg;
   const int c = rest / n_hg;
-  const Chunk ch = load_chunk(a.chunks, c);
-  const int segs = 4 / a.hpw;
+  const Chunk ch = load_chunk_uniform(a.chunks, c);
+  const int segs = NW / a.hpw;
   const int wg_row0 = pb * 32 * segs;
   if (wg_row0 >= ch.len) return;
   const int h = hg * a.hpw + (wave % a.hpw);
   const int g = h / a.group;
   const int row0 = wg_row0 + (wave / a.hpw) * 32;  // first chunk row of this wave
   const int nrows = max(0, min(32, ch.len - row0));
-  const int L = a.seq_lens[ch.seq];
-  const int64_t koff = a.seq_offsets[ch.seq];
+  const int L = rfl(a.seq_lens[ch.seq]);
+  const int64_t koff = rfl(a.seq_offsets[ch.seq]);
 
   const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + 32 * segs) - 1;
   // Keys [kv_lo, kv_end) are visible to some row of the workgroup: the key window
@@ -157,24 +169,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 
   if (n_tiles > t_first) {
     const int64_t first = (int64_t)t_first * kBN * kv_stride;
-    dma_rows<D, kBN>(lds_k[0], kbase + first, kv_stride, L - t_first * kBN, wave, lane);
-    dma_rows<D, kBN>(lds_v[0], vbase + first, kv_stride, L - t_first * kBN, wave, lane);
+    dma_rows<D, kBN, NW>(lds_k[0], kbase + first, kv_stride, L - t_first * kBN, wave, lane);
+    dma_rows<D, kBN, NW>(lds_v[0], vbase + first, kv_stride, L - t_first * kBN, wave, lane);
   }
   wait_vm_all();
   __syncthreads();
 
-  // Copies of the next tile, one instruction at a time between the S^T products: NST per
-  // wave (K then V, NST / 2 each).  Copy p of a tensor is tile instruction i = w + 4 p,
-  // rows i RPI + lane / G (clamped to the valid rows), swizzled granule of the row.
-  // The last tile re-copies itself into the free buffer so that the loop has no branch.
+  // Copies of the next tile, one instruction at a time between the S^T products: CPW per
+  // wave (K then V, CPW / 2 each), one every NST / CPW k-steps.  Copy p of a tensor is
+  // tile instruction i = w + NW p, rows i RPI + lane / G (clamped to the valid rows),
+  // swizzled granule of the row.  The last tile re-copies itself into the free buffer so
+  // that the loop has no branch.
   constexpr int G = D / 8, RPI = 64 / G;
-  static_assert(2 * (kBN * G / 64 / 4) == NST, "one copy per S^T k-step");
+  constexpr int CPW = 2 * (kBN * G / 64 / NW);
+  static_assert(CPW >= 2 && NST % CPW == 0, "copies spread evenly over the S^T k-steps");
+  constexpr int CEVERY = NST / CPW;
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const int lane_row = lane / G;
   const uint32_t rs_bytes = (uint32_t)(kv_stride * 2);
   uint32_t gran[2];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) gran[e] = (uint32_t)(((lane % G) ^ swz<D>((wu + 4 * e) * RPI + lane_row)) * 16);
+  for (int e = 0; e < 2; ++e) gran[e] = (uint32_t)(((lane % G) ^ swz<D>((wu + NW * e) * RPI + lane_row)) * 16);
   struct CopyStep {
     const char* bk;
     const char* bv;
@@ -192,9 +207,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
     return c;
   };
   auto copy_one = [&](const CopyStep& c, int p) {
-    const bool is_v = p >= NST / 2;
-    const int pp = is_v ? p - NST / 2 : p;
-    const int i = wu + 4 * pp;
+    const bool is_v = p >= CPW / 2;
+    const int pp = is_v ? p - CPW / 2 : p;
+    const int i = wu + NW * pp;
     const int row = min(i * RPI + lane_row, c.last_row);
     dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
   };
@@ -209,26 +224,31 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       // scheduling hint: interleave the step's MFMAs with its LDS reads and VALU work
       // (on the 64x8192 D256 rank share: 10% faster than no hint; strategy 1 another
       // 0.7% over strategy 0)
-      __builtin_amdgcn_iglp_opt(1);
+      if (D != 256) __builtin_amdgcn_iglp_opt(1);
       const uint16_t* kt = lds_k[buf];
       const uint16_t* vt = lds_v[buf];
-      // S^T for two 32-key blocks, as two interleaved accumulator chains; the LDS
+      // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
       // fragments for step st+1 are requested before the MFMAs of step st.
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
       {
-        u32x4 ka = lds_row16<D>(kt, col, kg), kb_ = lds_row16<D>(kt, 32 + col, kg);
+        u32x4 kf[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) kf[kb] = lds_row16<D>(kt, 32 * kb + col, kg);
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
-          u32x4 na = ka, nb = kb_;
-          if (st + 1 < NST) {
-            na = lds_row16<D>(kt, col, (st + 1) * 2 + kg);
-            nb = lds_row16<D>(kt, 32 + col, (st + 1) * 2 + kg);
+          u32x4 nf[NKB];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            nf[kb] = kf[kb];
+            if (st + 1 < NST) nf[kb] = lds_row16<D>(kt, 32 * kb + col, (st + 1) * 2 + kg);
           }
-          copy_one(cs, st);
-          s[0] = mfma32(ka, qf[st], s[0]);
-          s[1] = mfma32(kb_, qf[st], s[1]);
-          ka = na;
-          kb_ = nb;
+          if (st % CEVERY == 0) copy_one(cs, st / CEVERY);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kf[kb], qf[st], s[kb]);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) kf[kb] = nf[kb];
         }
       }
 
@@ -239,9 +259,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
       float mx = -INFINITY;
       if (need_mask) {
         asm volatile("" ::: "memory");
-        scale_tile<BIAS, true, CAUSAL>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
+        scale_tile<BIAS, true, CAUSAL, NKB>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
       } else {
-        scale_tile<BIAS, false, CAUSAL>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
+        scale_tile<BIAS, false, CAUSAL, NKB>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
       }
       mx = halves_max(mx);
       if (!BIAS) mx *= c_eff;
@@ -257,36 +277,37 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
         m_run = m_new;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      float rs[2] = {0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = BIAS ? exp2f_fast(s[kb][r] - m_use) : exp2f_fast(fmaf(s[kb][r], c_eff, -m_use));
           s[kb][r] = p;
-          rs[r & 3] += p;
+          rs[r & 1] += p;
         }
-      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      l_run += rs[0] + rs[1];
 
-      // O^T += V^T P^T over four 16-key steps; the V^T fragment of the next MFMA is
+      // O^T += V^T P^T over the tile's 16-key steps; the V^T fragment of the next MFMA is
       // requested before the current one issues.
       {
-        u32x4 pf[4];
+        constexpr int NPS = kBN / 16;
+        u32x4 pf[NPS];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) pf[st] = to_bf16x8(s[st >> 1], (st & 1) * 8);
+        for (int st = 0; st < NPS; ++st) pf[st] = to_bf16x8(s[st >> 1], (st & 1) * 8);
         u32x4 va = tr_frag_at<D>(vt, tro, 0, 0);
 #pragma unroll
-        for (int it = 0; it < 4 * NDB; ++it) {
+        for (int it = 0; it < NPS * NDB; ++it) {
           const int st = it / NDB, db = it % NDB;
           u32x4 nv = va;
-          if (it + 1 < 4 * NDB) nv = tr_frag_at<D>(vt, tro, (it + 1) / NDB, (it + 1) % NDB);
+          if (it + 1 < NPS * NDB) nv = tr_frag_at<D>(vt, tro, (it + 1) / NDB, (it + 1) % NDB);
           oacc[db] = mfma32(va, pf[st], oacc[db]);
           va = nv;
         }
       }
     } else {
 #pragma unroll
-      for (int p = 0; p < NST; ++p) copy_one(cs, p);
+      for (int p = 0; p < CPW; ++p) copy_one(cs, p);
     }
     wait_vm_all();
     __syncthreads();
@@ -316,8 +337,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const AttnArgs a) {
 
 template <int D, bool CAUSAL, bool BIAS>
 static void launch_fwd_t(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, BIAS>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, BIAS>), grid, dim3(FwdShape<D>::NW * 64), 0, s, a);
 }
+
+int fwd_waves(int D) { return D == 256 ? FwdShape<256>::NW : FwdShape<128>::NW; }
 
 hipError_t launch_fwd(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s) {
   if (bias) {

@@ -72,6 +72,8 @@ hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
+// Waves per forward workgroup at head dim D (each wave: 32 query rows of one head).
+int fwd_waves(int D);
 hipError_t launch_prepass(const AttnArgs& a, int D, dim3 grid, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int D, bool causal, bool bias, dim3 grid, hipStream_t s);

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
   const int pairs_per_wg = kThreads / per_pair;
   const int c = blockIdx.x / a.blocks_per_chunk;
   const int blk = blockIdx.x % a.blocks_per_chunk;
-  const Chunk ch = load_chunk(a.chunks, c);
+  const Chunk ch = load_chunk_uniform(a.chunks, c);
   const int pair = blk * pairs_per_wg + threadIdx.x / per_pair;
   if (pair >= ch.len * a.hq) return;  // no barriers in this kernel
   const int r = pair / a.hq, h = pair % a.hq;
