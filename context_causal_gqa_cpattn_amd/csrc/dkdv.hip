@@ -90,13 +90,14 @@ __device__ __forceinline__ void dma_tiles(uint16_t* lqt, uint16_t* ldot, const A
 
 // LSE and Delta of tile row r (clamped to the valid rows), as loaded: the values are
 // first used after the step's wait for all loads, so the loads never make a wave wait
-// for the tile DMA issued after them.
+// for the tile DMA issued after them.  Rows past the chunk end get LSE = +inf, so that
+// their probabilities come out 0 without a mask.
 __device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& it, int g, int r,
                                            float& lse, float& dl) {
   const int h = g * a.group + it.hh;
   const int nq = min(kTq, it.ch.len - it.qt * kTq);
   const int64_t idx = (int64_t)h * a.q_rows + it.ch.q_row + it.qt * kTq + min(r, nq - 1);
-  lse = a.lse[idx];
+  lse = r < nq ? a.lse[idx] : INFINITY;
   dl = a.delta[idx];
 }
 
@@ -155,7 +156,7 @@ __device__ __forceinline__ uint32_t wave_has_large_p(const f32x16& p) {
 // accumulation registers, and the compiler places every MFMA result there, so S and dP
 // would displace one dK/dV block per step (96 register moves).  Inline assembly pins
 // their destinations to VGPRs.  A chain accumulates into the same registers (no wait
-// states needed between dependent products of one shape); sdp_fence covers the wait
+// states needed between dependent products of one shape); xdl_fence covers the wait
 // states before VALU reads the results (at least 11 for an 8-pass product; 20 given).
 __device__ __forceinline__ f32x16 mfma32_v0(u32x4 a, u32x4 b) {
   f32x16 d;
@@ -165,8 +166,8 @@ __device__ __forceinline__ f32x16 mfma32_v0(u32x4 a, u32x4 b) {
 __device__ __forceinline__ void mfma32_v(f32x16& c, u32x4 a, u32x4 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void sdp_fence(f32x16& s, f32x16& dp) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s), "+v"(dp));
+__device__ __forceinline__ void xdl_fence(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x));
 }
 
 // The residue products of one tile, dV^T += dO^T rp and dK^T += Q^T rd for every 32-row
@@ -372,15 +373,82 @@ __device__ __forceinline__ void residue_products(f32x16 (&dvt)[NB], f32x16 (&dkt
 
 }
 
+// One side of the residue products, for the step order that runs all dV^T products
+// before all dK^T products: acc += X^T r for every 32-row block, X^T the tile OFF bytes
+// after the lane addresses a0 / a1 (k-steps 0 / 1), only when flag (wave-uniform) is
+// non-zero.  The same conventions as residue_products.
+template <int NB, int OFF>
+__device__ __forceinline__ void residue_half(f32x16 (&acc)[NB], uint32_t a0, uint32_t a1,
+                                             const u32x4 (&r)[2], uint32_t flag_in) {
+  static_assert(NB == 8 && OFF + (NB - 1) * 2048 < 65536, "ds_read offsets are 16 bits");
+  const uint32_t flag = __builtin_amdgcn_readfirstlane(flag_in);
+  u32x4 t[2], u[2];
+  if constexpr (NB == 8) {
+    asm volatile(
+        "s_cmp_eq_u32 %[flag], 0\n\t"
+        "s_cbranch_scc1 9f\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 1\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[o0]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[o0]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[o1]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[o1]\n\t"
+        "s_waitcnt lgkmcnt(2)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c0], %[t0], %[r0], %[c0]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c0], %[t1], %[r1], %[c0]\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[o2]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[o2]\n\t"
+        "s_waitcnt lgkmcnt(2)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c1], %[u0], %[r0], %[c1]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c1], %[u1], %[r1], %[c1]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[o3]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[o3]\n\t"
+        "s_waitcnt lgkmcnt(2)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c2], %[t0], %[r0], %[c2]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c2], %[t1], %[r1], %[c2]\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[o4]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[o4]\n\t"
+        "s_waitcnt lgkmcnt(2)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c3], %[u0], %[r0], %[c3]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c3], %[u1], %[r1], %[c3]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[o5]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[o5]\n\t"
+        "s_waitcnt lgkmcnt(2)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c4], %[t0], %[r0], %[c4]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c4], %[t1], %[r1], %[c4]\n\t"
+        "ds_read_b128 %[t0], %[a0] offset:%c[o6]\n\t"
+        "ds_read_b128 %[t1], %[a1] offset:%c[o6]\n\t"
+        "s_waitcnt lgkmcnt(2)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c5], %[u0], %[r0], %[c5]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c5], %[u1], %[r1], %[c5]\n\t"
+        "ds_read_b128 %[u0], %[a0] offset:%c[o7]\n\t"
+        "ds_read_b128 %[u1], %[a1] offset:%c[o7]\n\t"
+        "s_waitcnt lgkmcnt(2)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c6], %[t0], %[r0], %[c6]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c6], %[t1], %[r1], %[c6]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c7], %[u0], %[r0], %[c7]\n\t"
+        "v_mfma_f32_32x32x16_bf16 %[c7], %[u1], %[r1], %[c7]\n\t"
+        "9:"
+        : [c0] "+a"(acc[0]), [c1] "+a"(acc[1]), [c2] "+a"(acc[2]), [c3] "+a"(acc[3]), [c4] "+a"(acc[4]), [c5] "+a"(acc[5]), [c6] "+a"(acc[6]), [c7] "+a"(acc[7]), [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [u0] "=&v"(u[0]), [u1] "=&v"(u[1])
+        : [a0] "v"(a0), [a1] "v"(a1), [r0] "v"(r[0]), [r1] "v"(r[1]), [flag] "s"(flag), [o0] "i"(OFF + 0 * 2048), [o1] "i"(OFF + 1 * 2048), [o2] "i"(OFF + 2 * 2048), [o3] "i"(OFF + 3 * 2048), [o4] "i"(OFF + 4 * 2048), [o5] "i"(OFF + 5 * 2048), [o6] "i"(OFF + 6 * 2048), [o7] "i"(OFF + 7 * 2048)
+        : "scc");
+  }
+
+}
+
 template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   constexpr int NS = D / 16;       // 16-deep k-steps of S and dP
   constexpr int NB = D / 32;       // 32-row blocks of dK^T and dV^T
   constexpr int TE = D * kTq;      // elements of one transposed tile
   constexpr int EPB = 16 / NB;     // softmax elements per dV/dK block
-  // Software pipelining needs registers for two tiles' P/dS; with D = 256 the
-  // accumulators fill the accumulation registers and the steps run in order instead.
-  constexpr bool PIPE = D <= 128;
+  // Up to D = 128 the steps are software pipelined: a tile's softmax runs under the
+  // previous tile's dV/dK products.  At D = 256 the accumulators fill the accumulation
+  // registers and two tiles' P / dS do not fit; a step then orders its own products so
+  // that its softmax runs under its dP and dV products (SPLIT).
+  constexpr bool SPLIT = D == 256;
+  constexpr bool PIPE = !SPLIT;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_t[kBufs][2][TE];  // [buf][Q^T, dO^T]
   __shared__ __attribute__((aligned(16))) float lds_lse[kBufs][kTq];
   __shared__ __attribute__((aligned(16))) float lds_dl[kBufs][kTq];
@@ -544,88 +612,186 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
     const int nq = min(kTq, cur.ch.len - cur.qt * kTq);
     const int tile_pos0 = cur.ch.pos0 + cur.qt * kTq;
+    uint32_t res_cur = 0;
 
-    // S and dP of this tile; each A operand is read one k-step ahead.
-    f32x16 s = {}, dp = {};
-    {
+    // A operand of the S / dP products, k-step st, from the transposed tile t.
+    auto tr_a = [&](const uint16_t* t, int st) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[0]));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[1]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+    if constexpr (SPLIT) {
+      // One tile as a stream of 64 products in four phases, so that the softmax runs on
+      // the vector ALU while the matrix core works: (1) S, (2) dP, with P = exp2(S c - LSE)
+      // formed element by element under it, (3) dV^T += dO^T P, with dS = P (dP - Delta)
+      // formed under it, (4) dK^T += Q^T dS.  The A operands of the stream are read from
+      // LDS three products ahead.
+      static_assert(!BIAS, "no bias term at this head dimension");
       const uint16_t* qtt = lds_t[buf][0];
       const uint16_t* dtt = lds_t[buf][1];
-      auto tr_a = [&](const uint16_t* t, int st) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[0]));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[1]));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        return u32x4{l2[0], l2[1], h2[0], h2[1]};
-      };
-      u32x4 fq = tr_a(qtt, 0), fd = tr_a(dtt, 0);
+      // Elements that a mask may hide this step: the causal diagonal, and keys past the
+      // sequence end or outside the key window (queries past the chunk end have LSE =
+      // +inf, so their P is 0 already).  Element r is visible iff c(r) >= thr, with
+      // c(r) = 8 (r / 4) + r % 4 its query less 4 hl.
+      const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
+      const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
+      // the lane's 16 LSE / Delta values (element r: query 8 (r / 4) + 4 hl + r % 4)
+      auto row16 = [&](const float* x, float (&out)[16]) {
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        if (SPREAD && (st & 1) == 0) copy_one(st >> 1);
-        u32x4 nq_ = fq, nd_ = fd;
-        if (st + 1 < NS) {
-          nq_ = tr_a(qtt, st + 1);
-          nd_ = tr_a(dtt, st + 1);
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(x + 8 * i + 4 * hl);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) out[4 * i + j] = v[j];
         }
-        if (D == 256) {
-          if (st == 0) {
-            s = mfma32_v0(fq, kf[st]);
-            dp = mfma32_v0(fd, vf[st]);
-          } else {
-            mfma32_v(s, fq, kf[st]);
-            mfma32_v(dp, fd, vf[st]);
-          }
-        } else {
-          s = mfma32(fq, kf[st], s);
-          dp = mfma32(fd, vf[st], dp);
-        }
-        fq = nq_;
-        fd = nd_;
+      };
+      auto opnd = [&](int i) -> u32x4 {
+        if (i < NS) return tr_a(qtt, i);
+        if (i < 2 * NS) return tr_a(dtt, i - NS);
+        const int j = i & 15;  // (3) dO^T, (4) Q^T: block j / 2, k-step j % 2
+        return ld16((i < 48 ? dtt : qtt) + (j >> 1) * 32 * kTq + ((j & 1) ? tr_off1 : tr_off0));
+      };
+      static_assert(2 * NS == 32 && 4 * NB == 32, "64 products per step");
+      f32x16 s, dp;
+      float lv[16], dlv[16];
+      u32x4 sp[2], sd[2];  // BF16 residues of P and dS (set when flag)
+      uint32_t flag = 0;
+      const uint32_t boff = (uint32_t)buf * (2u * TE * 2u);
+      u32x4 ring[4];
+      ring[0] = opnd(0);
+      ring[1] = opnd(1);
+      ring[2] = opnd(2);
+      // product i of the stream: its A operand, with the read of product i + 3 issued
+      auto next_a = [&](int i) {
+        if (i + 3 < 64) ring[(i + 3) & 3] = opnd(i + 3);
+        return ring[i & 3];
+      };
+      // (1) S; the next tile's copies every other k-step
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const u32x4 A = next_a(i);
+        if ((i & 1) == 0) copy_one(i >> 1);
+        if (i == 0)
+          s = mfma32_v0(A, kf[0]);
+        else
+          mfma32_v(s, A, kf[i]);
+        if (i == 12) row16(lds_lse[buf], lv);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-
-    if (D == 256) sdp_fence(s, dp);
-    // Softmax of this tile, between the dV/dK products of the previous one.
-    const float* lse = lds_lse[buf];
-    const float* dl = lds_dl[buf];
-    auto sm_block = [&](int blk) {
-      softmax_part<EPB, true, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
-                                            nq, tile_pos0, bias_cur);
-    };
-    if (PIPE && have_prev) {
-      residue(pbuf, rp, rd, res_prev);
-      dvdk(pbuf, pp, pd, sm_block);
-    } else if (PIPE || (nk < 32) || !wave_in_window || (nq < kTq) || (CAUSAL && tile_pos0 < wkey0 + 31)) {
+      // (2) dP; P two elements per product, then the mask, the packing, the residue decision
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) sm_block(blk);
-    } else {  // a tile every key of the wave sees: no mask
-      softmax_part<16, false, CAUSAL, BIAS>(s, dp, 0, lse, dl, hl, a.scale_log2, key, key_ok, nq,
-                                            tile_pos0, bias_cur);
-    }
-    // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
-    pp[0] = to_bf16x8(s, 0);
-    pp[1] = to_bf16x8(s, 8);
-    pd[0] = to_bf16x8(dp, 0);
-    pd[1] = to_bf16x8(dp, 8);
-    const uint32_t res_cur = wave_has_large_p(s);
-    if (PIPE) {
+      for (int st = 0; st < 16; ++st) {
+        const u32x4 A = next_a(16 + st);
+        if (st == 0) {
+          dp = mfma32_v0(A, vf[0]);
+          xdl_fence(s);
+        } else {
+          mfma32_v(dp, A, vf[st]);
+        }
+        if (st >= 1 && st <= 8) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * (st - 1) + e;
+            s[r] = exp2f_fast(fmaf(s[r], a.scale_log2, -lv[r]));
+          }
+        }
+        if (st == 9 && fix) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) >= thr) ? s[r] : 0.f;
+        }
+        if (st == 10) {
+          pp[0] = to_bf16x8(s, 0);
+          pp[1] = to_bf16x8(s, 8);
+        }
+        if (st == 11) flag = wave_has_large_p(s);
+        if (st == 12) row16(lds_dl[buf], dlv);
+        if (st == 13 && flag) {
+          sp[0] = residue_bf16x8(s, pp[0], 0);
+          sp[1] = residue_bf16x8(s, pp[1], 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // (3) dV^T += dO^T P; dS two elements per product, its packing and residues
+      residue_half<NB, TE * 2>(dvt, res_a0 + boff, res_a1 + boff, sp, flag);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const u32x4 A = next_a(32 + j);
+        dvt[j >> 1] = mfma32(A, pp[j & 1], dvt[j >> 1]);
+        if (j == 0) xdl_fence(dp);
+        if (j >= 1 && j <= 8) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * (j - 1) + e;
+            dp[r] = s[r] * (dp[r] - dlv[r]);
+          }
+        }
+        if (j == 9) {
+          pd[0] = to_bf16x8(dp, 0);
+          pd[1] = to_bf16x8(dp, 8);
+        }
+        if (j == 10 && flag) {
+          sd[0] = residue_bf16x8(dp, pd[0], 0);
+          sd[1] = residue_bf16x8(dp, pd[1], 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // (4) dK^T += Q^T dS
+      residue_half<NB, 0>(dkt, res_a0 + boff, res_a1 + boff, sd, flag);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const u32x4 A = next_a(48 + j);
+        dkt[j >> 1] = mfma32(A, pd[j & 1], dkt[j >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // S and dP of this tile; each A operand is read one k-step ahead.
+      f32x16 s = {}, dp = {};
+      {
+        const uint16_t* qtt = lds_t[buf][0];
+        const uint16_t* dtt = lds_t[buf][1];
+        u32x4 fq = tr_a(qtt, 0), fd = tr_a(dtt, 0);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          if (SPREAD && (st & 1) == 0) copy_one(st >> 1);
+          u32x4 nq_ = fq, nd_ = fd;
+          if (st + 1 < NS) {
+            nq_ = tr_a(qtt, st + 1);
+            nd_ = tr_a(dtt, st + 1);
+          }
+          s = mfma32(fq, kf[st], s);
+          dp = mfma32(fd, vf[st], dp);
+          fq = nq_;
+          fd = nd_;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // Softmax of this tile, between the dV/dK products of the previous one.
+      const float* lse = lds_lse[buf];
+      const float* dl = lds_dl[buf];
+      auto sm_block = [&](int blk) {
+        softmax_part<EPB, true, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
+                                              nq, tile_pos0, bias_cur);
+      };
+      if (have_prev) {
+        residue(pbuf, rp, rd, res_prev);
+        dvdk(pbuf, pp, pd, sm_block);
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) sm_block(blk);
+      }
+      // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
+      pp[0] = to_bf16x8(s, 0);
+      pp[1] = to_bf16x8(s, 8);
+      pd[0] = to_bf16x8(dp, 0);
+      pd[1] = to_bf16x8(dp, 8);
+      res_cur = wave_has_large_p(s);
       if (res_cur) {  // kept for the next step, with pp / pd
         rp[0] = residue_bf16x8(s, pp[0], 0);
         rp[1] = residue_bf16x8(s, pp[1], 8);
         rd[0] = residue_bf16x8(dp, pd[0], 0);
         rd[1] = residue_bf16x8(dp, pd[1], 8);
       }
-    } else {
-      // the residues live only within this step (at D = 256 every register is taken
-      // during the S/dP products)
-      u32x4 sp[2] = {}, sd[2] = {};
-      if (res_cur) {
-        sp[0] = residue_bf16x8(s, pp[0], 0);
-        sp[1] = residue_bf16x8(s, pp[1], 8);
-        sd[0] = residue_bf16x8(dp, pd[0], 0);
-        sd[1] = residue_bf16x8(dp, pd[1], 8);
-      }
-      residue(buf, sp, sd, res_cur);
-      dvdk(buf, pp, pd, nop);
     }
 
     wait_vm_all();
