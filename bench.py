@@ -488,7 +488,7 @@ def time_workload(cp, torch, W, cfg, args, seed, headline):
         mark(1)
         cp.validate(prob, lay, err)
         mark(2)
-        cp.bwd_prepass(prob, lay, q, o, do, ws, err)
+        cp.bwd_prepass(prob, lay, q, o, do, lse, ws, err)
         mark(3)
         if use_ds:
             cp.bwd_dkdv_ds(prob, lay, q, k, v, bias, lse, do, ws, dk, dv, False, err)

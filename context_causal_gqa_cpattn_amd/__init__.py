@@ -59,7 +59,7 @@ class Problem(ctypes.Structure):
         ("num_chunks", ctypes.c_int32), ("max_chunk_len", ctypes.c_int32),
         ("max_kv_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
         ("bias_len", ctypes.c_int32), ("q_head_pitch", ctypes.c_int32),
-        ("kv_head_pitch", ctypes.c_int32),
+        ("kv_head_pitch", ctypes.c_int32), ("ds_blocks", ctypes.c_int64),
     ]
 
 
@@ -101,7 +101,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                        ctypes.c_int, _vp, sz, _vp, _vp],
         "cpattn_bwd_noalloc": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                ctypes.c_int, _vp, _vp],
-        "cpattn_bwd_prepass": [P, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
+        "cpattn_bwd_prepass": [P, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp],
         "cpattn_bwd_dkdv": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp,
                             ctypes.c_int, _vp, _vp],
         "cpattn_bwd_dq": [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp, _vp, _vp],
@@ -197,6 +197,19 @@ class Layout:
     num_chunks: int
     max_chunk_len: int
     max_kv_len: int
+    host_chunks: Optional[np.ndarray] = None  # int32 [C, 4], the same descriptors on the host
+    host_seq_lens: Optional[np.ndarray] = None
+
+
+def ds_blocks(chunks, seq_lens, causal: bool) -> int:
+    """The dS store bound of cpattn_problem.ds_blocks: sum over chunks of ceil(len / 32)
+    times the 32-key blocks its last row sees (causal: pos0 + len keys; else L)."""
+    ch = np.asarray(chunks, dtype=np.int64).reshape(-1, 4)
+    if len(ch) == 0:
+        return 0
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    keys = ch[:, 2] + ch[:, 3] if causal else sl[ch[:, 0]]
+    return int((((ch[:, 3] + 31) // 32) * ((keys + 31) // 32)).sum())
 
 
 def make_layout(seq_offsets: Sequence[int], seq_lens: Sequence[int], chunks, device="cuda",
@@ -208,16 +221,20 @@ def make_layout(seq_offsets: Sequence[int], seq_lens: Sequence[int], chunks, dev
     mcl = int(ch[:, 3].max()) if len(ch) and max_chunk_len is None else (max_chunk_len or 0)
     mkl = int(sl.max()) if len(sl) and max_kv_len is None else (max_kv_len or 0)
     return Layout(torch.from_numpy(so).to(device), torch.from_numpy(sl).to(device),
-                  torch.from_numpy(ch).to(device), len(so), len(ch), max(mcl, 0), max(mkl, 0))
+                  torch.from_numpy(ch).to(device), len(so), len(ch), max(mcl, 0), max(mkl, 0),
+                  ch, sl)
 
 
 def problem(layout: Layout, q_rows: int, kv_rows: int, hq: int, hkv: int, head_dim: int,
             causal: bool = True, scale: Optional[float] = None, bias_len: int = 0,
             q_head_pitch: int = 0, kv_head_pitch: int = 0) -> Problem:
+    dsb = 0
+    if layout.host_chunks is not None and layout.host_seq_lens is not None:
+        dsb = ds_blocks(layout.host_chunks, layout.host_seq_lens, causal)
     return Problem(layout.num_seqs, hq, hkv, head_dim, q_rows, kv_rows, layout.num_chunks,
                    layout.max_chunk_len, layout.max_kv_len, 1 if causal else 0,
                    (1.0 / math.sqrt(head_dim)) if scale is None else float(scale), bias_len,
-                   q_head_pitch, kv_head_pitch)
+                   q_head_pitch, kv_head_pitch, dsb)
 
 
 def new_dev_err(device="cuda"):
@@ -425,11 +442,12 @@ def bwd_window(q, k, v, layout: Layout, o, lse, do, kv_lo: int, kv_hi: int, caus
     return dq, dk, dv, ws, dev_err
 
 
-def bwd_prepass(prob: Problem, layout: Layout, q, o, do, ws, dev_err, stream=None):
-    """Delta and the transposed Q/dO tiles into the backward workspace `ws` (uint8)."""
+def bwd_prepass(prob: Problem, layout: Layout, q, o, do, lse, ws, dev_err, stream=None):
+    """Delta, the transposed Q/dO tiles and their row statistics into the backward
+    workspace `ws` (uint8)."""
     lib = load()
     _check(lib.cpattn_bwd_prepass(ctypes.byref(prob), _ptr(q), _ptr(layout.chunks), _ptr(o), _ptr(do),
-                                  _ptr(ws), ws.numel(), _ptr(dev_err), _stream(stream)))
+                                  _ptr(lse), _ptr(ws), ws.numel(), _ptr(dev_err), _stream(stream)))
 
 
 def bwd_dkdv(prob: Problem, layout: Layout, q, k, v, bias, lse, do, ws, dk, dv,

@@ -114,11 +114,12 @@ struct Plan {
   int64_t delta_bytes;  // rounded to 256
   int parts;            // dBias partitions
   int64_t partial_bytes;
-  // backward workspace: delta | Q^T tiles | dO^T tiles | dBias partials | dS blocks
-  int64_t off_qt, off_dot, off_partials, ws_core;
+  // backward workspace: delta | Q^T tiles | dO^T tiles | tile statistics | dBias partials |
+  // dS store (per-chunk offsets, then the blocks)
+  int64_t off_qt, off_dot, off_stats, off_partials, ws_core;
   bool ds_ok;            // the stored-dS backward applies (every supported head_dim, 32 to 256)
-  int64_t kb_max;        // 32-key blocks per (tile slot, head) in the dS store
-  int64_t off_ds, ds_bytes;
+  int64_t ds_head_blocks;  // dS blocks per query head
+  int64_t off_ds, off_ds_blocks, ds_bytes;  // ds_bytes: offsets and blocks
   dim3 grid_fwd, grid_fwd1d, grid_fwdk, grid_prepass, grid_dkdv, grid_dbias, grid_dbias_ds, grid_dqds;
   int bpc_fwd, bpc_fwdk, bpc_prepass, bpc_dqds, kv_tiles;
 };
@@ -219,17 +220,26 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   const int64_t tile_bytes = max_tiles * p->hq * (int64_t)D * kPrepassRows * 2;
   pl.off_qt = pl.delta_bytes;
   pl.off_dot = pl.off_qt + round256(tile_bytes);
-  pl.off_partials = pl.off_dot + round256(tile_bytes);
+  // per tile and head: log2(e) LSE of its 32 rows, then their Delta (fp32)
+  pl.off_stats = pl.off_dot + round256(tile_bytes);
+  pl.off_partials = pl.off_stats + round256(max_tiles * p->hq * 64 * 4);
   pl.ws_core = pl.off_partials;
   // the pre-pass numbers its workgroups linearly (head fastest)
   if (gx_pre * p->hq > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
   pl.grid_prepass = dim3((unsigned)gx_pre, (unsigned)p->hq);
-  // Stored dS: 2 KB per (tile slot, head, 32-key block), every slot sized for the longest
-  // sequence.
+  // Stored dS: 2 KB per (chunk tile, head, 32-key block the chunk sees), the chunks'
+  // block count promised in ds_blocks (checked on the device); without a promise every
+  // tile slot is sized for the longest sequence.
+  if (p->ds_blocks < 0) return fail(CPATTN_EINVAL, "ds_blocks is negative");
   pl.ds_ok = D >= 32;
-  pl.kb_max = cdiv(p->max_kv_len, kDsBlockKeys);
+  pl.ds_head_blocks = p->ds_blocks > 0 ? p->ds_blocks : max_tiles * cdiv(p->max_kv_len, kDsBlockKeys);
+  if (pl.ds_head_blocks > (int64_t(1) << 40) / std::max(1, p->hq))
+    return fail(CPATTN_EUNSUPPORTED, "dS store too large");
   pl.off_ds = pl.ws_core + pl.partial_bytes;
-  pl.ds_bytes = pl.ds_ok ? round256(max_tiles * p->hq * pl.kb_max * kDsBlockKeys * kPrepassRows * 2) : 0;
+  pl.off_ds_blocks = pl.off_ds + round256((int64_t)p->num_chunks * 8);
+  pl.ds_bytes = pl.ds_ok ? (pl.off_ds_blocks - pl.off_ds) +
+                               round256(pl.ds_head_blocks * p->hq * kDsBlockKeys * kPrepassRows * 2)
+                         : 0;
   pl.bpc_dqds = (int)cdiv(p->max_chunk_len, (int64_t)kDqDsRows * (4 / pl.hpw));
   const int64_t gx_dqds = (int64_t)p->num_chunks * pl.bpc_dqds * (p->hq / pl.hpw);
   if (gx_dqds > kGridMax) return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
@@ -293,6 +303,8 @@ int run_validate(const cpattn_problem* p, const int32_t* so, const int32_t* sl, 
   v.max_kv_len = p->max_kv_len;
   v.bias_len = p->bias_len;
   v.s_pitch = 0;
+  v.causal = p->causal;
+  v.ds_blocks = p->ds_blocks;
   return hip_check(launch_validate(v, s), "validate launch");
 }
 
@@ -318,7 +330,7 @@ __attribute__((visibility("hidden"))) int cpattn_internal_fail(int status, const
   return fail(status, "%s", msg);
 }
 
-int cpattn_version(void) { return 10000; }
+int cpattn_version(void) { return 10100; }
 
 size_t cpattn_workspace_size(const cpattn_problem* p, int op) {
   Plan pl;
@@ -480,6 +492,7 @@ AttnArgs bwd_args(const cpattn_problem* p, const Plan& pl, const void* q, const 
   a.lse = lse;
   a.dout = (const uint16_t*)dout;
   a.delta = delta;
+  a.stats = (const float*)(w + pl.off_stats);
   a.seq_offsets = so;
   a.seq_lens = sl;
   a.chunks = cm;
@@ -488,7 +501,8 @@ AttnArgs bwd_args(const cpattn_problem* p, const Plan& pl, const void* q, const 
 }
 
 int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, const void* q,
-                    const void* o, const void* dout, void* ws, const int32_t* dev_err, hipStream_t s) {
+                    const void* o, const void* dout, const float* lse, void* ws, const int32_t* dev_err,
+                    hipStream_t s) {
   AttnArgs a = base_args(p, pl);
   char* w = (char*)ws;
   a.q = (const uint16_t*)q;
@@ -497,6 +511,8 @@ int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, 
   a.delta_out = (float*)w;
   a.qt_out = (uint16_t*)(w + pl.off_qt);
   a.dot_out = (uint16_t*)(w + pl.off_dot);
+  a.stats_out = (float*)(w + pl.off_stats);
+  a.lse = lse;
   a.chunks = cm;
   a.dev_err = dev_err;
   a.blocks_per_chunk = pl.bpc_prepass;
@@ -504,14 +520,26 @@ int enqueue_prepass(const cpattn_problem* p, const Plan& pl, const int32_t* cm, 
   return hip_check(launch_prepass(a, pl.D, pl.grid_prepass, s), "pre-pass launch");
 }
 
+// ds_area: the dS part of the workspace (offsets, then blocks), or null to store no dS.
 int enqueue_dkdv(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dk, void* dv, int acc,
-                 hipStream_t s, void* ds_out = nullptr) {
+                 hipStream_t s, void* ds_area = nullptr) {
   if (empty(pl.grid_dkdv)) return CPATTN_OK;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
   a.accumulate = acc ? 1 : 0;
-  a.ds_out = (uint16_t*)ds_out;
-  a.kb_max = pl.kb_max;
+  if (ds_area) {
+    DsTableArgs t{};
+    t.seq_lens = a.seq_lens;
+    t.chunks = a.chunks;
+    t.dev_err = a.dev_err;
+    t.tab = (int64_t*)ds_area;
+    t.num_chunks = p->num_chunks;
+    t.causal = p->causal;
+    int r = hip_check(launch_ds_table(t, s), "dS table launch");
+    if (r) return r;
+    a.ds_tab = (const int64_t*)ds_area;
+    a.ds_out = (uint16_t*)((char*)ds_area + (pl.off_ds_blocks - pl.off_ds));
+  }
   return hip_check(launch_dkdv(a, pl.D, p->causal != 0, pl.bias, pl.grid_dkdv, s), "dK/dV launch");
 }
 
@@ -526,8 +554,8 @@ int enqueue_dq_ds(const cpattn_problem* p, const Plan& pl, AttnArgs a, const voi
                   hipStream_t s) {
   if (empty(pl.grid_dqds)) return CPATTN_OK;
   a.dq = (uint16_t*)dq;
-  a.ds = (const uint16_t*)((const char*)ws + pl.off_ds);
-  a.kb_max = pl.kb_max;
+  a.ds_tab = (const int64_t*)((const char*)ws + pl.off_ds);
+  a.ds = (const uint16_t*)((const char*)ws + pl.off_ds_blocks);
   a.blocks_per_chunk = pl.bpc_dqds;
   return hip_check(launch_dq_ds(a, pl.D, p->causal != 0, pl.grid_dqds, s), "dQ (stored dS) launch");
 }
@@ -550,8 +578,8 @@ int enqueue_dbias_ds(const cpattn_problem* p, const Plan& pl, AttnArgs a, float*
   if (!pl.bias || empty(pl.grid_dbias_ds)) return CPATTN_OK;
   float* partial = pl.parts > 1 ? (float*)((char*)ws + pl.off_partials) : dbias;
   a.dbias = partial;
-  a.ds = (const uint16_t*)((const char*)ws + pl.off_ds);
-  a.kb_max = pl.kb_max;
+  a.ds_tab = (const int64_t*)((const char*)ws + pl.off_ds);
+  a.ds = (const uint16_t*)((const char*)ws + pl.off_ds_blocks);
   int r = hip_check(launch_dbias_ds(a, pl.grid_dbias_ds, s), "dBias (stored dS) launch");
   if (r || pl.parts == 1) return r;
   return hip_check(launch_dbias_reduce(partial, dbias, pl.bias_bytes / 4, pl.parts, a.dev_err, s),
@@ -595,7 +623,7 @@ int cpattn_bwd(const cpattn_problem* p, const void* q, const void* k, const void
 
   hipStream_t s = (hipStream_t)stream;
   if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
-  if ((r = enqueue_prepass(p, pl, q_chunk_map, q, o, dout, ws, dev_err, s))) return r;
+  if ((r = enqueue_prepass(p, pl, q_chunk_map, q, o, dout, lse, ws, dev_err, s))) return r;
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   if (use_ds) {
     if ((r = enqueue_dkdv(p, pl, a, dk, dv, dkv_accumulate, s, (char*)ws + pl.off_ds))) return r;
@@ -649,7 +677,7 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
   hipStream_t s = (hipStream_t)stream;
   if (prepass) {
     if ((r = run_validate(p, seq_offsets, seq_lens, q_chunk_map, dev_err, s))) return r;
-    if ((r = enqueue_prepass(p, pl, q_chunk_map, q, o, dout, ws, dev_err, s))) return r;
+    if ((r = enqueue_prepass(p, pl, q_chunk_map, q, o, dout, lse, ws, dev_err, s))) return r;
   }
   AttnArgs a = bwd_args(p, pl, q, k, v, seq_offsets, seq_lens, q_chunk_map, bias, lse, dout, ws, dev_err);
   a.kv_lo = kv_lo;
@@ -664,14 +692,14 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
 }
 
 int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
-                       const void* o, const void* dout, void* ws, size_t ws_bytes,
-                       const int32_t* dev_err, cpattn_stream_t stream) {
+                       const void* o, const void* dout, const float* lse, void* ws,
+                       size_t ws_bytes, const int32_t* dev_err, cpattn_stream_t stream) {
   g_last_error.clear();
   Plan pl;
   int r;
   if ((r = make_plan(p, pl))) return r;
   if ((r = check_ptr(q, pl.q_bytes, 16, "q")) || (r = check_ptr(o, pl.q_bytes, 16, "o")) ||
-      (r = check_ptr(dout, pl.q_bytes, 16, "dout")) ||
+      (r = check_ptr(dout, pl.q_bytes, 16, "dout")) || (r = check_ptr(lse, pl.stat_bytes, 4, "lse")) ||
       (r = check_ptr(q_chunk_map, (uint64_t)p->num_chunks * 16, 16, "q_chunk_map")) ||
       (r = check_ptr(dev_err, 4, 4, "dev_err")))
     return r;
@@ -679,11 +707,11 @@ int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_
     return fail(CPATTN_EINVAL, "workspace too small: %zu < %lld", ws_bytes, (long long)pl.ws_core);
   if ((r = check_ptr(ws, pl.ws_core, 256, "ws"))) return r;
   std::vector<Range> rs = {rq(pl, "q", q, false), rq(pl, "o", o, false),
-                           rq(pl, "dout", dout, false),
+                           rq(pl, "dout", dout, false), rng("lse", lse, pl.stat_bytes, false),
                            rng("q_chunk_map", q_chunk_map, (uint64_t)p->num_chunks * 16, false),
                            rng("dev_err", dev_err, 4, false), rng("ws", ws, pl.ws_core, true)};
   if ((r = alias_audit(rs))) return r;
-  return enqueue_prepass(p, pl, q_chunk_map, q, o, dout, ws, dev_err, (hipStream_t)stream);
+  return enqueue_prepass(p, pl, q_chunk_map, q, o, dout, lse, ws, dev_err, (hipStream_t)stream);
 }
 
 namespace {

@@ -84,10 +84,16 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(const AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) ds[e] += __shfl_xor(ds[e], m, 64);
       if (dg == 0) {
+        // the tile's row statistics for dK/dV: log2(e) LSE (+inf past the chunk end, so
+        // that those rows' probabilities come out 0), then Delta (0 past the end)
+        float* st = a.stats_out + (tile * a.hq + h) * 64;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int qi = qbase + sigma16(qsub + e);
-          if (qi < nq) a.delta_out[(int64_t)h * a.q_rows + ch.q_row + r0 + qi] = ds[e];
+          const int64_t row = (int64_t)h * a.q_rows + ch.q_row + r0 + qi;
+          if (qi < nq) a.delta_out[row] = ds[e];
+          st[qi] = qi < nq ? a.lse[row] * kLog2e : INFINITY;
+          st[32 + qi] = qi < nq ? ds[e] : 0.f;
         }
       }
     }

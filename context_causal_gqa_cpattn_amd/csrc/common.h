@@ -187,6 +187,24 @@ __device__ __forceinline__ void dma16_at(const char* base, uint32_t off, uint32_
                : "memory", "m0");
 }
 
+// The same copy with the LDS address given as two wave-uniform parts (M0 is formed by
+// one scalar add inside the block).
+__device__ __forceinline__ void dma16_add(const char* base, uint32_t off, uint32_t lds,
+                                          uint32_t lds_off) {
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base), "s"(lds_off)
+               : "memory", "m0", "scc");
+}
+
+// 4 bytes per lane: lane i's dword from base + off lands at LDS address lds + 4 i.
+__device__ __forceinline__ void dma4_at(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
 // The same copy with the non-temporal hint, for data read once (a stream that should not
 // push reused tiles out of L2).
 __device__ __forceinline__ void dma16_nt_at(const char* base, uint32_t off, uint32_t lds) {
@@ -381,6 +399,19 @@ __device__ __forceinline__ int64_t tile_slot(int c, int q_row, int qt) {
   return (int64_t)(q_row >> 5) + c + qt;
 }
 
+// The dS store keeps, for every 32-query tile and query head of a chunk, the 32-key
+// blocks that the chunk's last row sees: ceil(K_c / 32) of them, K_c = pos0 + len with
+// causal masking, else the sequence length L.  Chunk c's blocks start at block
+// ds_tab[c] * hq (ds_tab: the running sum of ceil(len / 32) * ceil(K_c / 32) over the
+// chunks before c), ordered [tile][head][key block].
+__device__ __forceinline__ int ds_chunk_kb(const Chunk& ch, int L, bool causal) {
+  return ((causal ? ch.pos0 + ch.len : L) + 31) >> 5;
+}
+// First block of (tile qt, head h) of a chunk whose store starts at tab * hq.
+__device__ __forceinline__ int64_t ds_block0(int64_t tab, int kb_c, int qt, int h, int hq) {
+  return (tab + (int64_t)qt * kb_c) * hq + (int64_t)h * kb_c;
+}
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -401,9 +432,11 @@ struct AttnArgs {
   uint16_t* dot_out;     // pre-pass output: transposed dO tiles
   const uint16_t* qt;    // transposed Q tiles [slot][hq][D][32]
   const uint16_t* dot;   // transposed dO tiles
+  float* stats_out;      // pre-pass output: per-tile row statistics [slot][hq][64]
+  const float* stats;    // the same, read by dK/dV: log2(e) LSE (+inf past the end), Delta
   uint16_t* ds_out;      // dK/dV: where to store dS blocks (null: not stored)
   const uint16_t* ds;    // dQ from stored dS: the dS blocks
-  int64_t kb_max;        // 32-key blocks per (query tile slot, head) in the dS store
+  const int64_t* ds_tab; // per chunk: first dS block / hq (see ds_block0)
   int64_t q_pitch;       // heads per row in memory: Q, O, dO, dQ
   int64_t kv_pitch;      // heads per row in memory: K, V, dK, dV
   int kv_lo, kv_hi;      // key window [kv_lo, kv_hi) in sequence positions (0, INT_MAX: all)

@@ -150,7 +150,7 @@ hipError_t launch_dbias_reduce(const float* partial, float* out, int64_t n, int 
 namespace cpattn {
 
 // dBias from the stored dS: with the dS store filled by dK/dV (BF16 blocks of 32 keys x
-// 32 queries per (query tile slot, head, 32-key block)), dBias[h, p, k] is the sum over
+// 32 queries per (chunk tile, head, 32-key block)), dBias[h, p, k] is the sum over
 // every chunk row at position p of that row's dS[h, k]: a streaming reduction over the
 // blocks instead of forming S, P and dP again.
 //
@@ -185,8 +185,8 @@ __global__ __launch_bounds__(128) void dbias_ds_kernel(const AttnArgs a) {
     return Chunk{m[0], m[1], m[2], m[3]};
   };
   auto block_ptr = [&](int c, const Chunk& ch, int tile) {
-    const int64_t blk = ((int64_t)tile_slot(c, ch.q_row, tile) * a.hq + h) * a.kb_max + kb;
-    return a.ds + blk * 1024;
+    const int kbc = ds_chunk_kb(ch, a.seq_lens[ch.seq], false);
+    return a.ds + (ds_block0(a.ds_tab[c], kbc, tile, h, a.hq) + kb) * 1024;
   };
   // Does the unit hold a chunk whose tiles do not line up with 32-position tiles?
   bool aligned = true;

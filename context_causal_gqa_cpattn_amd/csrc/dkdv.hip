@@ -48,14 +48,25 @@ constexpr int kWaves = 4;   // waves per workgroup, 32 keys each
 constexpr int kKvThreads = kWaves * 64;
 static_assert(kWaves * 32 == kDkdvKeys, "keys per workgroup");
 
+// The workgroup's walk over (chunk, query head of the group, query tile): tile qt
+// innermost, then the head, then the chunks of the sequence.  Besides the position it
+// carries the running indices that the step needs, so that a step costs a few scalar
+// additions: the tile's unit (tile slot * hq + query head: its index among the
+// transposed tiles and their statistics) and its first dS block.
 struct QTileIter {
   int c, hh, qt, qt_first, n_qt;
   Chunk ch;
+  int unit, ubase;        // this tile's unit; the unit of (qt_first, head 0 of the group)
+  int64_t ds, dsbase;     // dS block of (this tile, head, key block 0); of (qt_first, head 0)
+  int64_t ds_step;        // dS blocks from one tile to the next (ceil(K_c / 32) hq)
+  int kbc;                // dS blocks per (tile, head) of the chunk
 };
 
-// Advance to the next chunk (from it.c) that has query tiles seeing keys >= key0.
+// Advance to the next chunk (from it.c) that has query tiles seeing keys >= key0.  h0:
+// the group's first query head; L: the sequence length.
 template <bool CAUSAL>
-__device__ __forceinline__ bool seek_chunk(const AttnArgs& a, QTileIter& it, int c_end, int key0) {
+__device__ __forceinline__ bool seek_chunk(const AttnArgs& a, QTileIter& it, int c_end, int key0,
+                                           int h0, int L) {
   for (; it.c < c_end; ++it.c) {
     it.ch = load_chunk_uniform(a.chunks, it.c);
     const int first_row = CAUSAL ? max(0, key0 - it.ch.pos0) : 0;
@@ -64,6 +75,16 @@ __device__ __forceinline__ bool seek_chunk(const AttnArgs& a, QTileIter& it, int
       it.n_qt = (it.ch.len + kTq - 1) / kTq;
       it.qt = it.qt_first;
       it.hh = 0;
+      it.ubase = (int)tile_slot(it.c, it.ch.q_row, it.qt_first) * a.hq + h0;
+      it.unit = it.ubase;
+      if (a.ds_out != nullptr) {
+        it.kbc = ds_chunk_kb(it.ch, L, CAUSAL);
+        const int64_t* t = a.ds_tab + it.c;
+        const int64_t tab = (int64_t)(((uint64_t)rfl((int)(*t >> 32)) << 32) | (uint32_t)rfl((int)*t));
+        it.dsbase = ds_block0(tab, it.kbc, it.qt_first, h0, a.hq);
+        it.ds = it.dsbase;
+        it.ds_step = (int64_t)it.kbc * a.hq;
+      }
       return true;
     }
   }
@@ -71,34 +92,34 @@ __device__ __forceinline__ bool seek_chunk(const AttnArgs& a, QTileIter& it, int
 }
 
 template <bool CAUSAL>
-__device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_end, int key0) {
-  if (++it.qt < it.n_qt) return true;
+__device__ __forceinline__ bool advance(const AttnArgs& a, QTileIter& it, int c_end, int key0, int h0,
+                                        int L) {
+  if (++it.qt < it.n_qt) {
+    it.unit += a.hq;
+    it.ds += it.ds_step;
+    return true;
+  }
   it.qt = it.qt_first;
-  if (++it.hh < a.group) return true;
+  if (++it.hh < a.group) {
+    it.unit = it.ubase + it.hh;
+    it.ds = it.dsbase + (int64_t)it.hh * it.kbc;
+    return true;
+  }
   ++it.c;
-  return seek_chunk<CAUSAL>(a, it, c_end, key0);
+  return seek_chunk<CAUSAL>(a, it, c_end, key0, h0, L);
 }
-
 
 template <int D>
 __device__ __forceinline__ void dma_tiles(uint16_t* lqt, uint16_t* ldot, const AttnArgs& a,
-                                          const QTileIter& it, int g, int wave, int lane) {
-  const int64_t unit = tile_slot(it.c, it.ch.q_row, it.qt) * a.hq + g * a.group + it.hh;
-  dma_flat<D * kTq * 2 / 1024, kWaves>(lqt, a.qt + unit * D * kTq, wave, lane);
-  dma_flat<D * kTq * 2 / 1024, kWaves>(ldot, a.dot + unit * D * kTq, wave, lane);
+                                          const QTileIter& it, int wave, int lane) {
+  dma_flat<D * kTq * 2 / 1024, kWaves>(lqt, a.qt + (int64_t)it.unit * D * kTq, wave, lane);
+  dma_flat<D * kTq * 2 / 1024, kWaves>(ldot, a.dot + (int64_t)it.unit * D * kTq, wave, lane);
 }
 
-// LSE and Delta of tile row r (clamped to the valid rows), as loaded: the values are
-// first used after the step's wait for all loads, so the loads never make a wave wait
-// for the tile DMA issued after them.  Rows past the chunk end get LSE = +inf, so that
-// their probabilities come out 0 without a mask.
-__device__ __forceinline__ void load_stats(const AttnArgs& a, const QTileIter& it, int g, int r,
-                                           float& lse, float& dl) {
-  const int h = g * a.group + it.hh;
-  const int nq = min(kTq, it.ch.len - it.qt * kTq);
-  const int64_t idx = (int64_t)h * a.q_rows + it.ch.q_row + it.qt * kTq + min(r, nq - 1);
-  lse = r < nq ? a.lse[idx] : INFINITY;
-  dl = a.delta[idx];
+// The tile's row statistics (64 floats: log2(e) LSE of its 32 rows, +inf past the chunk
+// end, then Delta) into LDS, one dword per lane; issued by one wave.
+__device__ __forceinline__ void dma_stats(float* lds, const AttnArgs& a, int unit, int lane) {
+  dma4_at(uniform_ptr(a.stats + (int64_t)unit * 64), (uint32_t)lane * 4u, lds_addr(lds));
 }
 
 // P and dS of accumulator elements [r0, r0 + n) of a lane, in place (s -> P, dp -> dS).
@@ -450,8 +471,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   constexpr bool SPLIT = D == 256;
   constexpr bool PIPE = !SPLIT;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_t[kBufs][2][TE];  // [buf][Q^T, dO^T]
-  __shared__ __attribute__((aligned(16))) float lds_lse[kBufs][kTq];
-  __shared__ __attribute__((aligned(16))) float lds_dl[kBufs][kTq];
+  // per buffer: log2(e) LSE of the tile's rows, then their Delta
+  __shared__ __attribute__((aligned(16))) float lds_st[kBufs][2 * kTq];
 
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,9 +531,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   const int tr_off1 = n * kTq + (((2 + hl) ^ tswz(n)) * 8);
 
   const int c_end = chunk_lower_bound(a.chunks, a.num_chunks, b + 1);
+  const int h0 = g * a.group;  // the group's first query head
   QTileIter cur;
   cur.c = chunk_lower_bound(a.chunks, a.num_chunks, b);
-  bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0);
+  bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0, h0, L);
   // With a bias: the lane's 16 bias values of a tile (element r is query 8 (r / 4) +
   // 4 hl + r % 4 of the tile, key `key`), loaded one step ahead so that their latency
   // is spent under the previous step's products; used only after the step's wait.
@@ -528,14 +550,11 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     }
   };
   if (BIAS && have) load_bias(cur, bias_cur);
-  float st_lse = 0.f, st_dl = 0.f;  // stats staged for the next tile (threads < kTq)
+  // the wave that copies each step's row statistics
+  const bool stats_wave = __builtin_amdgcn_readfirstlane(wave) == kWaves - 1;
   if (have) {
-    dma_tiles<D>(lds_t[0][0], lds_t[0][1], a, cur, g, wave, lane);
-    if (tid < kTq) {
-      load_stats(a, cur, g, tid, st_lse, st_dl);
-      lds_lse[0][tid] = st_lse * kLog2e;
-      lds_dl[0][tid] = st_dl;
-    }
+    dma_tiles<D>(lds_t[0][0], lds_t[0][1], a, cur, wave, lane);
+    if (stats_wave) dma_stats(lds_st[0], a, cur.unit, lane);
   }
   wait_vm_all();
   __syncthreads();
@@ -580,33 +599,33 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     const uint32_t boff = (uint32_t)pb * (2u * TE * 2u);
     residue_products<NB, TE * 2>(dvt, dkt, res_a0 + boff, res_a1 + boff, rp, rd, flag);
   };
+  // Tile copies of the next step: for D >= 128 one instruction every other S/dP k-step
+  // (every wave issues D / 32 of them; without a next tile the current one is re-copied
+  // into the free buffer), for smaller D all at once.  Copy k of a tensor by this wave
+  // moves the tile's 1 KB piece i = wave + kWaves k: the lane offsets are fixed.
+  constexpr bool SPREAD = D >= 128;
+  constexpr int TI = D * kTq * 2 / 1024 / kWaves;  // copies per wave per tensor
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t voff[SPREAD ? TI : 1];
+#pragma unroll
+  for (int k = 0; k < (SPREAD ? TI : 1); ++k) voff[k] = (uint32_t)lane * 16u + (uint32_t)(wu + kWaves * k) * 1024u;
+  const char* const qt_base = uniform_ptr(a.qt);
+  const char* const dot_base = uniform_ptr(a.dot);
   while (have) {
     QTileIter nxt = cur;
-    const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0);
+    const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0, h0, L);
     const int nbuf = (buf + 1 == kBufs) ? 0 : buf + 1;
-    // Tile copies of the next step: for D >= 128 one instruction every other S/dP k-step
-    // (every wave issues D / 32 of them; without a next tile the current one is re-copied
-    // into the free buffer), for smaller D all at once.
-    constexpr bool SPREAD = D >= 128;
-    constexpr int TI = D * kTq * 2 / 1024 / kWaves;  // copies per wave per tensor
-    const char* cb[2];
-    uint32_t cl[2];
-    if (SPREAD) {
-      const QTileIter& src = have_next ? nxt : cur;
-      const int64_t unit = tile_slot(src.c, src.ch.q_row, src.qt) * a.hq + g * a.group + src.hh;
-      cb[0] = uniform_ptr(a.qt + unit * D * kTq);
-      cb[1] = uniform_ptr(a.dot + unit * D * kTq);
-      cl[0] = lds_addr(lds_t[nbuf][0]);
-      cl[1] = lds_addr(lds_t[nbuf][1]);
-    }
-    const int wu = __builtin_amdgcn_readfirstlane(wave);
-    auto copy_one = [&](int p) {  // p < 2 TI: tensor p / TI, instruction w + kWaves (p % TI)
-      const int which = p / TI, i = wu + kWaves * (p % TI);
-      dma16_at(cb[which] + i * 1024, (uint32_t)lane * 16u, cl[which] + i * 1024);
+    const int src_unit = have_next ? nxt.unit : cur.unit;
+    const int64_t src_off = (int64_t)src_unit * (D * kTq * 2);
+    const char* cb[2] = {qt_base + src_off, dot_base + src_off};
+    const uint32_t clw = lds_addr(lds_t[nbuf][0]) + (uint32_t)wu * 1024u;
+    auto copy_one = [&](int p) {  // p < 2 TI: tensor p / TI, copy p % TI
+      const int which = p / TI, k = p % TI;
+      dma16_add(cb[which], voff[k], clw, (uint32_t)(which * TE * 2 + k * kWaves * 1024));
     };
-    if (have_next && tid < kTq) load_stats(a, nxt, g, tid, st_lse, st_dl);
+    if (stats_wave) dma_stats(lds_st[nbuf], a, src_unit, lane);
     if (BIAS && have_next) load_bias(nxt, bias_nxt);
-    if (!SPREAD && have_next) dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, g, wave, lane);
+    if (!SPREAD && have_next) dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, wave, lane);
 
     // Every wave runs every tile of the loop: tiles that a wave's keys do not see (at the
     // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
@@ -675,7 +694,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
           s = mfma32_v0(A, kf[0]);
         else
           mfma32_v(s, A, kf[i]);
-        if (i == 12) row16(lds_lse[buf], lv);
+        if (i == 12) row16(lds_st[buf], lv);
         __builtin_amdgcn_sched_barrier(0);
       }
       // (2) dP; P two elements per product, then the mask, the packing, the residue decision
@@ -704,7 +723,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
           pp[1] = to_bf16x8(s, 8);
         }
         if (st == 11) flag = wave_has_large_p(s);
-        if (st == 12) row16(lds_dl[buf], dlv);
+        if (st == 12) row16(lds_st[buf] + kTq, dlv);
         if (st == 13 && flag) {
           sp[0] = residue_bf16x8(s, pp[0], 0);
           sp[1] = residue_bf16x8(s, pp[1], 8);
@@ -767,8 +786,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       }
 
       // Softmax of this tile, between the dV/dK products of the previous one.
-      const float* lse = lds_lse[buf];
-      const float* dl = lds_dl[buf];
+      const float* lse = lds_st[buf];
+      const float* dl = lds_st[buf] + kTq;
       auto sm_block = [&](int blk) {
         softmax_part<EPB, true, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
                                               nq, tile_pos0, bias_cur);
@@ -795,20 +814,13 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     }
 
     wait_vm_all();
-    if (have_next && tid < kTq) {
-      lds_lse[nbuf][tid] = st_lse * kLog2e;
-      lds_dl[nbuf][tid] = st_dl;
-    }
     __syncthreads();
-    // Stored dS for the dQ product: block (tile slot, head, key block of this wave), key row
+    // Stored dS for the dQ product: block (tile, head, key block of this wave), key row
     // n, granules 2 e + hl (pd[e]).  Only blocks with a visible pair are stored; they are
     // the blocks that dQ reads.  Issued after the step's wait for its copies, so that the
     // stores complete during the next step instead of extending this one.
     if (a.ds_out != nullptr && wkey0 < L && (!CAUSAL || wkey0 <= tile_pos0 + nq - 1)) {
-      const int64_t blk =
-          ((int64_t)tile_slot(cur.c, cur.ch.q_row, cur.qt) * a.hq + g * a.group + cur.hh) * a.kb_max +
-          (wkey0 >> 5);
-      uint16_t* dst = a.ds_out + blk * 1024 + n * 32 + hl * 8;
+      uint16_t* dst = a.ds_out + (cur.ds + (wkey0 >> 5)) * 1024 + n * 32 + hl * 8;
       // streaming stores: dS is read back only by the dQ product, long after
       __builtin_nontemporal_store(pd[0], reinterpret_cast<u32x4*>(dst));
       __builtin_nontemporal_store(pd[1], reinterpret_cast<u32x4*>(dst + 16));

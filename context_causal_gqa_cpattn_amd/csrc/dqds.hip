@@ -11,8 +11,9 @@
 //
 // dS block (2 KB, written by dK/dV): 32 key rows of 64 bytes; granule v = 2 e + hl of key
 // row n holds queries 16 e + 8 (i / 4) + 4 hl + i % 4, i = 0..7 (the order in which a
-// 32x32 accumulator lane holds its rows).  Block kb of (query tile slot, head h) is at
-// ((slot hq + h) kb_max + kb) 2 KB of the dS area.
+// 32x32 accumulator lane holds its rows).  Block kb of (tile qt of chunk c, head h) is
+// block ds_block0(ds_tab[c], ceil(K_c / 32), qt, h, hq) + kb of the dS area (the chunk's
+// blocks in [tile][head][key block] order, K_c the keys its last row sees).
 //
 // With a key window [kv_lo, kv_hi) only the window's key blocks are multiplied, and
 // with dq_accumulate the result is added to the existing BF16 dQ (one rounding): a ring
@@ -116,6 +117,8 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   const int n_steps = (kv_end + kBlk - 1) / kBlk;
 
   // The slot's two tiles: rows, key blocks with a visible pair, first dS block.
+  const int kbc = ds_chunk_kb(ch, L, CAUSAL);
+  const int64_t tab = (int64_t)(((uint64_t)rfl((int)(a.ds_tab[c] >> 32)) << 32) | (uint32_t)rfl((int)a.ds_tab[c]));
   int nq[2], nkb[2];
   const uint16_t* dsrc[2];
 #pragma unroll
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
     nkb[i] = nq[i] > 0 ? (min(min(L, CAUSAL ? last + 1 : L), a.kv_hi) + kBlk - 1) / kBlk : 0;
     dsrc[i] = a.ds;
     if (nq[i] > 0)
-      dsrc[i] = a.ds + ((int64_t)tile_slot(c, ch.q_row, r / 32) * a.hq + h) * a.kb_max * kBlkElems;
+      dsrc[i] = a.ds + ds_block0(tab, kbc, r / 32, h, a.hq) * kBlkElems;
   }
 
   const int64_t kv_stride = a.kv_pitch * D;

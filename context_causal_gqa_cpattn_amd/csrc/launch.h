@@ -16,7 +16,20 @@ struct ValidateArgs {
   int64_t q_rows;
   int num_seqs, num_chunks, max_chunk_len, max_kv_len, bias_len;
   int s_pitch;            // layout copies: BHSD pitch (0 for attention)
+  int causal;
+  int64_t ds_blocks;      // promised dS store bound (0: none to check)
 };
+
+// Per-chunk first dS block (divided by hq) of the stored-dS backward: the running sum of
+// ceil(len / 32) * ceil(K_c / 32) over the chunks before each one.
+struct DsTableArgs {
+  const int32_t* seq_lens;
+  const int32_t* chunks;
+  const int32_t* dev_err;
+  int64_t* tab;
+  int num_chunks, causal;
+};
+hipError_t launch_ds_table(const DsTableArgs& a, hipStream_t s);
 
 struct LayoutArgs {
   const uint16_t* src;

@@ -9,11 +9,11 @@
 // device address is looked up once with hipGetSymbolAddress, with that device current,
 // and kept per device.
 //
-// No part of the workspace has to start at zero: the pre-pass writes Delta and the
-// transposed tiles before dK/dV reads them, dQ reads only the dS blocks that dK/dV wrote in
-// the same call, and the dBias kernel writes its partial sums before they are added.  So the
-// array needs no clearing between calls, and whatever an earlier call left in it is never
-// read.  Calls that overlap in time on one GPU (different streams, or different host
+// No part of the workspace has to start at zero: the pre-pass writes Delta, the transposed
+// tiles and their row statistics before dK/dV reads them, the chunks' dS offsets are
+// written before dK/dV, dQ reads only the dS blocks that dK/dV wrote in the same call, and
+// the dBias kernel writes its partial sums before they are added.  So the array needs no
+// clearing between calls, and whatever an earlier call left in it is never read.  Calls that overlap in time on one GPU (different streams, or different host
 // threads) share the one array and race; serialize them.
 #include <mutex>
 

@@ -83,6 +83,7 @@ typedef enum cpattn_status {
 #define CPATTN_DEV_ECHUNK_POS  0x10 /* len < 0, len > max_chunk_len, pos0 < 0 or pos0+len > L */
 #define CPATTN_DEV_EBIAS       0x20 /* a sequence longer than bias_len                 */
 #define CPATTN_DEV_ELAYOUT     0x40 /* pack/unpack: L_b > S_pitch or THD rows out of range */
+#define CPATTN_DEV_EDS_BLOCKS  0x80 /* stored-dS backward: the chunks need more than ds_blocks */
 
 /* Shape and variant of one rank share. */
 typedef struct cpattn_problem {
@@ -101,6 +102,12 @@ typedef struct cpattn_problem {
                             indexed [h, query position, key position]; needs causal = 0 */
   int32_t q_head_pitch;  /* heads per row in the memory of Q, O, dO, dQ (0: hq); >= hq */
   int32_t kv_head_pitch; /* heads per row in the memory of K, V, dK, dV (0: hkv); >= hkv */
+  int64_t ds_blocks;     /* host-known bound that sizes the stored-dS backward's dS store:
+                            the sum over chunks of ceil(len / 32) * ceil(K_c / 32), where
+                            K_c is the keys the chunk's last row sees (causal: pos0 + len;
+                            else L of its sequence).  0: no bound known, every query-tile
+                            slot is sized for ceil(max_kv_len / 32) key blocks.  Checked on
+                            the device (CPATTN_DEV_EDS_BLOCKS). */
 } cpattn_problem;
 /* Head pitches let one call cover a group of heads of larger tensors in place ("First-
  * gradient buffer reuse" / head partitioning: H16/H8 head-group calls on strided
@@ -128,15 +135,19 @@ int cpattn_version(void);
  * each part starting on a 256-byte boundary: Delta (fp32 [hq, q_rows], at offset
  * 0); Q^T and dO^T as BF16 tiles [slot][hq][head_dim][32 queries, in an internal
  * order] with ceil(q_rows/32) + num_chunks slots (tile t of chunk c is slot
- * floor(q_row_c / 32) + c + t; queries past the chunk end are zero); and, with a
- * bias, the per-partition dBias partial sums.
- * op = CPATTN_OP_BWD_DS: the backward workspace followed by the dS store, BF16
- * blocks of 32 keys x 32 queries (2 KB, internal order), one per (tile slot, query
- * head, 32-key block < ceil(max_kv_len / 32)): with it dK/dV stores dS and dQ is a
- * product with the stored dS instead of a second pass that forms S, P and dP
- * again.  It is 2 bytes per (query row slot, head, key position up to max_kv_len):
- * e.g. 36.5 GB for 128 chunks of 512 rows, 32 heads and max_kv_len 8192.  Every
- * supported head dim (32 to 256).
+ * floor(q_row_c / 32) + c + t; queries past the chunk end are zero); the tiles' row
+ * statistics, fp32 [slot][hq][64] (log2(e) * LSE of the 32 rows, +inf past the chunk
+ * end, then Delta, 0 past the end); and, with a bias, the per-partition dBias partial
+ * sums.
+ * op = CPATTN_OP_BWD_DS: the backward workspace followed by the chunks' dS store
+ * offsets (int64 per chunk) and the dS store, BF16 blocks of 32 keys x 32 queries
+ * (2 KB, internal order), one per (chunk tile, query head, 32-key block the chunk
+ * sees): with it dK/dV stores dS and dQ is a product with the stored dS instead of
+ * a second pass that forms S, P and dP again.  It is hq * ds_blocks blocks (hq *
+ * (ceil(q_rows/32) + num_chunks) * ceil(max_kv_len/32) when ds_blocks is 0): e.g.
+ * 18.3 GB for 64 sequences of 8192 keys holding two 512-row chunks each (one at the
+ * start, one at the end), 32 heads and causal masking, against 36.5 GB without the
+ * bound.  Every supported head dim (32 to 256).
  * Returns 0 for an invalid problem (check it with the entry point for the reason). */
 size_t cpattn_workspace_size(const cpattn_problem* p, int op);
 
@@ -229,8 +240,9 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
  * sums may be left off, so ws_bytes may be that size minus them).
  *  cpattn_bwd_prepass: writes Delta[h, r] = sum_d dO[r,h,d] O[r,h,d] (fp32) on
  *      chunk rows ("CP8 AllGather: composition with first-gradient reuse": the
- *      row dot of dO and O, loaded at their physical pitch), and the transposed
- *      32-query tiles of Q and dO that dK/dV multiplies with.
+ *      row dot of dO and O, loaded at their physical pitch), the transposed
+ *      32-query tiles of Q and dO that dK/dV multiplies with, and each tile's row
+ *      statistics (LSE, the forward's output, and Delta).
  *  cpattn_bwd_dkdv: dK/dV as in cpattn_bwd from the pre-pass results.
  *  cpattn_bwd_dq: dQ as in cpattn_bwd from the pre-pass results.
  *  cpattn_bwd_dbias: dBias as in cpattn_bwd from the pre-pass results; ws must
@@ -251,8 +263,8 @@ int cpattn_bwd_window(const cpattn_problem* p, const void* q, const void* k, con
  *      store (cpattn_workspace_size(p, CPATTN_OP_BWD_DS) bytes); reads the
  *      descriptors and the dS store only. */
 int cpattn_bwd_prepass(const cpattn_problem* p, const void* q, const int32_t* q_chunk_map,
-                       const void* o, const void* dout, void* ws, size_t ws_bytes,
-                       const int32_t* dev_err, cpattn_stream_t stream);
+                       const void* o, const void* dout, const float* lse, void* ws,
+                       size_t ws_bytes, const int32_t* dev_err, cpattn_stream_t stream);
 int cpattn_bwd_dkdv(const cpattn_problem* p, const void* q, const void* k, const void* v,
                     const int32_t* seq_offsets, const int32_t* seq_lens,
                     const int32_t* q_chunk_map, const float* bias, const float* lse,

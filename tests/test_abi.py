@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = cp.load()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.cpattn_version() == 10000
+    assert lib.cpattn_version() == 10100
     assert lib.cpattn_status_str(0) == b"CPATTN_OK"
 
 
@@ -106,7 +106,8 @@ def _ws_layout(hq, q_rows, num_chunks, head_dim):
     """Backward workspace bytes without dBias partials, from the layout the header states."""
     r256 = lambda x: (x + 255) // 256 * 256
     tiles = -(-q_rows // 32) + num_chunks
-    return r256(hq * q_rows * 4) + 2 * r256(tiles * hq * head_dim * 32 * 2)
+    return (r256(hq * q_rows * 4) + 2 * r256(tiles * hq * head_dim * 32 * 2)
+            + r256(tiles * hq * 64 * 4))
 
 
 def test_workspace_sizes():
@@ -132,10 +133,10 @@ def test_backward_steps_check_workspace():
     so, sl, cm = A + (3 << 24), A + (3 << 24) + 256, A + (3 << 24) + 512
     o, lse, do, err, ws = A + (4 << 24), A + (5 << 24), A + (8 << 24), A + (6 << 24), A + (12 << 24)
     dk, dv, dq = A + (9 << 24), A + (10 << 24), A + (11 << 24)
-    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, ws, core - 256, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, lse, ws, core - 256, err, None) == cp.EINVAL
     assert "workspace" in _err()
-    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, ws + 16, core, err, None) == cp.EINVAL
-    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, o, core, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, lse, ws + 16, core, err, None) == cp.EINVAL
+    assert lib.cpattn_bwd_prepass(ctypes.byref(p), q, cm, o, do, lse, o, core, err, None) == cp.EINVAL
     assert "alias" in _err()
     args = [ctypes.byref(p), q, k, v, so, sl, cm, None, lse, do]
     assert lib.cpattn_bwd_dkdv(*args, ws, core - 1, dk, dv, 0, err, None) == cp.EINVAL
@@ -158,11 +159,14 @@ def test_layout_copy_host_checks():
                              A + (3 << 24), None) == cp.EINVAL
 
 
-def _ds_bytes(hq, q_rows, num_chunks, max_kv_len):
-    """dS store bytes from the layout the header states: 2 KB per (tile slot, head, 32-key block)."""
+def _ds_bytes(hq, q_rows, num_chunks, max_kv_len, ds_blocks=0):
+    """dS store bytes from the layout the header states: the chunks' int64 offsets, then
+    2 KB per (chunk tile, head, 32-key block), ds_blocks blocks per head when given, else
+    every tile slot sized for max_kv_len."""
     r256 = lambda x: (x + 255) // 256 * 256
     tiles = -(-q_rows // 32) + num_chunks
-    return r256(tiles * hq * (-(-max_kv_len // 32)) * 2048)
+    blocks = ds_blocks if ds_blocks else tiles * (-(-max_kv_len // 32))
+    return r256(num_chunks * 8) + r256(blocks * hq * 2048)
 
 
 def test_stored_ds_workspace_size():
@@ -173,9 +177,23 @@ def test_stored_ds_workspace_size():
     p3 = _prob(num_seqs=64, hq=32, hkv=8, head_dim=256, q_rows=64 * 1024, kv_rows=64 * 8192,
                num_chunks=128, max_chunk_len=512, max_kv_len=8192)
     ds3 = _ds_bytes(32, 64 * 1024, 128, 8192)
-    assert ds3 == 36_507_222_016  # the figure the header quotes
+    assert ds3 == 36_507_222_016 + 1024  # the figure the header quotes (+ the offsets)
     assert lib.cpattn_workspace_size(ctypes.byref(p3), cp.OP_BWD_DS) == \
         _ws_layout(32, 64 * 1024, 128, 256) + ds3
+    # with the chunks' bound: two 512-row chunks per 8192-key sequence, at its start
+    # (16 key blocks) and end (256 key blocks), 16 tiles each
+    chunks = [(b, 1024 * b + 512 * j, 7680 * j, 512) for b in range(64) for j in range(2)]
+    dsb = cp.ds_blocks(chunks, [8192] * 64, causal=True)
+    assert dsb == 64 * (16 * 16 + 16 * 256)
+    p3.ds_blocks = dsb
+    ds3b = _ds_bytes(32, 64 * 1024, 128, 8192, dsb)
+    assert ds3b == 18_253_612_032  # the figure the header quotes
+    assert lib.cpattn_workspace_size(ctypes.byref(p3), cp.OP_BWD_DS) == \
+        _ws_layout(32, 64 * 1024, 128, 256) + ds3b
+    # without causal masking every chunk keeps all of its sequence's key blocks
+    assert cp.ds_blocks(chunks, [8192] * 64, causal=False) == 128 * 16 * 256
+    p3.ds_blocks = -1
+    assert lib.cpattn_workspace_size(ctypes.byref(p3), cp.OP_BWD_DS) == 0
     # after the dBias partial sums when there is a bias
     pb = _prob(head_dim=64, bias_len=256, causal=0, hq=4, hkv=4, num_chunks=64, q_rows=1 << 14,
                kv_rows=1 << 14, max_chunk_len=256, max_kv_len=256)

@@ -246,7 +246,7 @@ def test_stored_ds_steps_match_fused_entry_over_stale_workspace(gpu_lib):
     err = gpu_lib.new_dev_err()
     dq, dk, dv = torch.empty_like(run.q), torch.empty_like(run.k), torch.empty_like(run.v)
     gpu_lib.validate(prob, run.layout, err)
-    gpu_lib.bwd_prepass(prob, run.layout, run.q, run.o, run.do, ws, err)
+    gpu_lib.bwd_prepass(prob, run.layout, run.q, run.o, run.do, run.lse, ws, err)
     gpu_lib.bwd_dkdv_ds(prob, run.layout, run.q, run.k, run.v, None, run.lse, run.do, ws, dk, dv,
                         False, err)
     gpu_lib.bwd_dq_ds(prob, run.layout, run.k, ws, dq, err)
@@ -284,7 +284,7 @@ def test_stored_ds_dbias_steps_match_fused_entry_over_stale_workspace(gpu_lib):
     dq, dk, dv = torch.empty_like(run.q), torch.empty_like(run.k), torch.empty_like(run.v)
     dbias = torch.full_like(run.bias, float("nan"))
     gpu_lib.validate(prob, run.layout, err)
-    gpu_lib.bwd_prepass(prob, run.layout, run.q, run.o, run.do, ws, err)
+    gpu_lib.bwd_prepass(prob, run.layout, run.q, run.o, run.do, run.lse, ws, err)
     gpu_lib.bwd_dkdv_ds(prob, run.layout, run.q, run.k, run.v, run.bias, run.lse, run.do, ws, dk, dv,
                         False, err)
     gpu_lib.bwd_dq_ds(prob, run.layout, run.k, ws, dq, err)
