@@ -119,7 +119,7 @@ struct Plan {
   int64_t off_qt, off_dot, off_stats, off_partials, ws_core;
   bool ds_ok;            // the stored-dS backward applies (every supported head_dim, 32 to 256)
   int64_t ds_head_blocks;  // dS blocks per query head
-  int64_t off_ds, off_ds_blocks, ds_bytes;  // ds_bytes: offsets and blocks
+  int64_t off_ds, off_ds_zero, off_ds_blocks, ds_bytes;  // ds_bytes: offsets, zero block, blocks
   dim3 grid_fwd, grid_fwd1d, grid_fwdk, grid_prepass, grid_dkdv, grid_dbias, grid_dbias_ds, grid_dqds;
   int bpc_fwd, bpc_fwdk, bpc_prepass, bpc_dqds, kv_tiles;
 };
@@ -236,7 +236,8 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   if (pl.ds_head_blocks > (int64_t(1) << 40) / std::max(1, p->hq))
     return fail(CPATTN_EUNSUPPORTED, "dS store too large");
   pl.off_ds = pl.ws_core + pl.partial_bytes;
-  pl.off_ds_blocks = pl.off_ds + round256((int64_t)p->num_chunks * 8);
+  pl.off_ds_zero = pl.off_ds + round256((int64_t)p->num_chunks * 8);
+  pl.off_ds_blocks = pl.off_ds_zero + kDsBlockKeys * kPrepassRows * 2;
   pl.ds_bytes = pl.ds_ok ? (pl.off_ds_blocks - pl.off_ds) +
                                round256(pl.ds_head_blocks * p->hq * kDsBlockKeys * kPrepassRows * 2)
                          : 0;
@@ -533,6 +534,7 @@ int enqueue_dkdv(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dk, 
     t.chunks = a.chunks;
     t.dev_err = a.dev_err;
     t.tab = (int64_t*)ds_area;
+    t.zero = (uint16_t*)((char*)ds_area + (pl.off_ds_zero - pl.off_ds));
     t.num_chunks = p->num_chunks;
     t.causal = p->causal;
     int r = hip_check(launch_ds_table(t, s), "dS table launch");
@@ -555,6 +557,7 @@ int enqueue_dq_ds(const cpattn_problem* p, const Plan& pl, AttnArgs a, const voi
   if (empty(pl.grid_dqds)) return CPATTN_OK;
   a.dq = (uint16_t*)dq;
   a.ds_tab = (const int64_t*)((const char*)ws + pl.off_ds);
+  a.ds_zero = (const uint16_t*)((const char*)ws + pl.off_ds_zero);
   a.ds = (const uint16_t*)((const char*)ws + pl.off_ds_blocks);
   a.blocks_per_chunk = pl.bpc_dqds;
   return hip_check(launch_dq_ds(a, pl.D, p->causal != 0, pl.grid_dqds, s), "dQ (stored dS) launch");

@@ -437,6 +437,7 @@ struct AttnArgs {
   uint16_t* ds_out;      // dK/dV: where to store dS blocks (null: not stored)
   const uint16_t* ds;    // dQ from stored dS: the dS blocks
   const int64_t* ds_tab; // per chunk: first dS block / hq (see ds_block0)
+  const uint16_t* ds_zero;  // a dS block of zeros (read for blocks that a tile does not use)
   int64_t q_pitch;       // heads per row in memory: Q, O, dO, dQ
   int64_t kv_pitch;      // heads per row in memory: K, V, dK, dV
   int kv_lo, kv_hi;      // key window [kv_lo, kv_hi) in sequence positions (0, INT_MAX: all)

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   __shared__ __attribute__((aligned(1024))) uint16_t lds_s[kStages][kSlots * 2 * kBlkElems];
 
   if (*a.dev_err) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = rfl(tid >> 6);  // wave-uniform, so that everything derived from it is scalar
   const int slot = wave / kSplit, part = wave % kSplit;
   const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk, a.hq / a.hpw);
   const int n_hg = a.hq / a.hpw;
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
     nq[i] = max(0, min(32, ch.len - r));
     const int last = ch.pos0 + r + nq[i] - 1;
     nkb[i] = nq[i] > 0 ? (min(min(L, CAUSAL ? last + 1 : L), a.kv_hi) + kBlk - 1) / kBlk : 0;
-    dsrc[i] = a.ds;
+    dsrc[i] = a.ds_zero;
     if (nq[i] > 0)
       dsrc[i] = a.ds + ds_block0(tab, kbc, r / 32, h, a.hq) * kBlkElems;
   }
@@ -136,10 +137,11 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)kvh * D;
   // Copy instruction p (0 <= p < PER) of this wave for step kb into stage kb % kStages:
   // the K tile (rows past L repeat the last key), then the slot's dS blocks (with two
-  // waves per slot, wave `part` copies tile `part`).  A block the tile does not use is
-  // still copied (from the start of the dS area, in bounds) so that every wave issues
-  // PER copies per step; steps past the last re-copy the last step into a free stage.
-  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  // waves per slot, wave `part` copies tile `part`).  For a block that the tile does not
+  // use (no visible pair: dK/dV did not store it) a block of zeros is copied, so that
+  // the products need no mask and every wave issues PER copies per step; steps past the
+  // last re-copy the last step into a free stage.
+  const int wu = wave;
   const uint32_t rs_bytes = (uint32_t)(kv_stride * 2);
   auto issue_one = [&](int kb_req, int p) {
     const int kb = min(kb_req, n_steps - 1);
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
       const int q = p - KI;
       const int ti = kSplit == 2 ? part : (q >> 1);
       const int half = q & 1;
-      const uint16_t* src = kb < nkb[ti] ? dsrc[ti] + (int64_t)kb * kBlkElems : a.ds;
+      const uint16_t* src = kb < nkb[ti] ? dsrc[ti] + (int64_t)kb * kBlkElems : a.ds_zero;
       dma16_nt_at(uniform_ptr(src) + half * 1024, (uint32_t)lane * 16u,
                lds_addr(lds_s[sb] + (slot * 2 + ti) * kBlkElems) + half * 1024);
     }
@@ -197,18 +199,14 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
     wait_vm<(kStages - 2) * PER>();  // stage kb has landed (later stages may be in flight)
     __syncthreads();                 // stage kb is in LDS for every wave; stage kb - 1 is free
 
-    // A tile without a visible pair in this block multiplies zeros (its dS block was not
-    // written); no branch around the products, which would move the accumulators.  The
-    // copies of step kb + kStages - 1 are spread between the products.
-    const uint32_t m0 = kb < nkb[0] ? ~0u : 0u, m1 = kb < nkb[1] ? ~0u : 0u;
+    // A tile without a visible pair in this block multiplies the zero block copied in
+    // its place.  The copies of step kb + kStages - 1 are spread between the products.
     const int sb = kb % kStages;
     const uint16_t* kt = lds_k[sb];
     const uint16_t* s0 = lds_s[sb] + (slot * 2) * kBlkElems;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const u32x4 t0 = ds_frag(s0, dso, st), t1 = ds_frag(s0 + kBlkElems, dso, st);
-      const u32x4 b0 = {t0[0] & m0, t0[1] & m0, t0[2] & m0, t0[3] & m0};
-      const u32x4 b1 = {t1[0] & m1, t1[1] & m1, t1[2] & m1, t1[3] & m1};
+      const u32x4 b0 = ds_frag(s0, dso, st), b1 = ds_frag(s0 + kBlkElems, dso, st);
       u32x4 ka = kfrag(kt, st, 0);
 #pragma unroll
       for (int j = 0; j < NDB; ++j) {

@@ -27,6 +27,7 @@ struct DsTableArgs {
   const int32_t* chunks;
   const int32_t* dev_err;
   int64_t* tab;
+  uint16_t* zero;  // 2 KB set to zero
   int num_chunks, causal;
 };
 hipError_t launch_ds_table(const DsTableArgs& a, hipStream_t s);

@@ -64,6 +64,7 @@ __global__ __launch_bounds__(1024) void ds_table_kernel(const DsTableArgs a) {
   __shared__ int64_t sm[1024];
   int64_t carry = 0;
   const int t = threadIdx.x;
+  if (t < 128) st16(a.zero + 8 * t, u32x4{0u, 0u, 0u, 0u});
   for (int c0 = 0; c0 < a.num_chunks; c0 += 1024) {
     const int c = c0 + t;
     int64_t v = 0;
@@ -86,7 +87,6 @@ __global__ __launch_bounds__(1024) void ds_table_kernel(const DsTableArgs a) {
 }
 
 hipError_t launch_ds_table(const DsTableArgs& a, hipStream_t s) {
-  if (a.num_chunks <= 0) return hipSuccess;
   hipLaunchKernelGGL(ds_table_kernel, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }

@@ -140,7 +140,8 @@ int cpattn_version(void);
  * end, then Delta, 0 past the end); and, with a bias, the per-partition dBias partial
  * sums.
  * op = CPATTN_OP_BWD_DS: the backward workspace followed by the chunks' dS store
- * offsets (int64 per chunk) and the dS store, BF16 blocks of 32 keys x 32 queries
+ * offsets (int64 per chunk), a 2 KB block of zeros and the dS store, BF16 blocks of
+ * 32 keys x 32 queries
  * (2 KB, internal order), one per (chunk tile, query head, 32-key block the chunk
  * sees): with it dK/dV stores dS and dQ is a product with the stored dS instead of
  * a second pass that forms S, P and dP again.  It is hq * ds_blocks blocks (hq *

@@ -166,7 +166,7 @@ def _ds_bytes(hq, q_rows, num_chunks, max_kv_len, ds_blocks=0):
     r256 = lambda x: (x + 255) // 256 * 256
     tiles = -(-q_rows // 32) + num_chunks
     blocks = ds_blocks if ds_blocks else tiles * (-(-max_kv_len // 32))
-    return r256(num_chunks * 8) + r256(blocks * hq * 2048)
+    return r256(num_chunks * 8) + 2048 + r256(blocks * hq * 2048)
 
 
 def test_stored_ds_workspace_size():
@@ -177,7 +177,7 @@ def test_stored_ds_workspace_size():
     p3 = _prob(num_seqs=64, hq=32, hkv=8, head_dim=256, q_rows=64 * 1024, kv_rows=64 * 8192,
                num_chunks=128, max_chunk_len=512, max_kv_len=8192)
     ds3 = _ds_bytes(32, 64 * 1024, 128, 8192)
-    assert ds3 == 36_507_222_016 + 1024  # the figure the header quotes (+ the offsets)
+    assert ds3 == 36_507_222_016 + 1024 + 2048  # the figure the header quotes (+ offsets, zeros)
     assert lib.cpattn_workspace_size(ctypes.byref(p3), cp.OP_BWD_DS) == \
         _ws_layout(32, 64 * 1024, 128, 256) + ds3
     # with the chunks' bound: two 512-row chunks per 8192-key sequence, at its start
@@ -187,7 +187,7 @@ def test_stored_ds_workspace_size():
     assert dsb == 64 * (16 * 16 + 16 * 256)
     p3.ds_blocks = dsb
     ds3b = _ds_bytes(32, 64 * 1024, 128, 8192, dsb)
-    assert ds3b == 18_253_612_032  # the figure the header quotes
+    assert ds3b == 18_253_614_080  # the figure the header quotes
     assert lib.cpattn_workspace_size(ctypes.byref(p3), cp.OP_BWD_DS) == \
         _ws_layout(32, 64 * 1024, 128, 256) + ds3b
     # without causal masking every chunk keeps all of its sequence's key blocks

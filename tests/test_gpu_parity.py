@@ -379,6 +379,41 @@ def test_device_promise_violation_fails_closed(gpu_lib, bad):
         gpu_lib.check(err)
 
 
+def test_ds_blocks_promise_fails_closed(gpu_lib):
+    """A dS store bound below what the chunks need is a broken promise: the validation
+    step reports CPATTN_DEV_EDS_BLOCKS and nothing is written (the store sized from the
+    bound would be too small for the chunks)."""
+    import torch
+    w = _small_case()
+    run = DeviceRun(gpu_lib, w)
+    run.forward()
+    lay = gpu_lib.make_layout(w.seq_offsets, w.seq_lens, w.chunks, max_chunk_len=w.max_chunk_len,
+                              max_kv_len=w.max_kv_len)
+    true_bound = gpu_lib.ds_blocks(w.chunks, w.seq_lens, True)
+    # the host copy claims that the second chunk (positions 120..149) sits 64 positions
+    # earlier: a bound 2 blocks per tile too small
+    host = lay.host_chunks.copy()
+    assert host[1, 2] == 120
+    host[1, 2] -= 64
+    lay.host_chunks = host
+    assert gpu_lib.ds_blocks(lay.host_chunks, lay.host_seq_lens, True) < true_bound
+    o = torch.full_like(run.q, 7.0)
+    lse = torch.full((w.hq, w.q_rows), 7.0, device="cuda")
+    dk = torch.full_like(run.k, 3.0)
+    dv = torch.full_like(run.v, 3.0)
+    dq = torch.full_like(run.q, 3.0)
+    _, _, _, _, err = gpu_lib.bwd(run.q, run.k, run.v, lay, run.o, run.lse, run.do, causal=True,
+                                  scale=w.scale, dq=dq, dk=dk, dv=dv, store_ds=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 0x80, hex(int(err.item()))
+    assert bool((dk == 3.0).all()) and bool((dv == 3.0).all()) and bool((dq == 3.0).all())
+    # the exact bound passes
+    lay.host_chunks = w.chunks.copy()
+    _, _, _, _, err = gpu_lib.bwd(run.q, run.k, run.v, lay, run.o, run.lse, run.do, causal=True,
+                                  scale=w.scale, dq=dq, dk=dk, dv=dv, store_ds=True)
+    gpu_lib.check(err)
+
+
 # ---------------------------------------------------------------- layout copies
 
 @pytest.mark.parametrize("D", [128, 256])
