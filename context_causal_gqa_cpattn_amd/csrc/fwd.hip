@@ -25,14 +25,20 @@
 
 namespace cpattn {
 
-// Keys per K/V tile and waves per workgroup.  D <= 128: 64-key tiles, four waves (the
-// tiles leave room for a second workgroup per CU).  D = 256: 32-key tiles and eight
-// waves, two per SIMD: a 64-key tile pair (128 KB of LDS) would leave one wave per SIMD,
-// and a tile now serves 256 query rows instead of 128, half the copied bytes per FLOP.
+// Keys per K/V tile, waves per workgroup and K/V buffers.  D <= 128: 64-key tiles, four
+// waves, double-buffered (the tiles leave room for a second workgroup per CU).  D = 256:
+// 32-key tiles and eight waves, two per SIMD: a 64-key tile pair (128 KB of LDS) would
+// leave one wave per SIMD, and a tile now serves 256 query rows instead of 128, half the
+// copied bytes per FLOP.  A 32-key tile is computed in about a microsecond, less than
+// the latency of its copy from L2 or HBM, so the tiles are copied AHEAD = STAGES - 1
+// tiles ahead (three 32 KB stages: 3% faster than two on the 64 x 8192 D256 rank share;
+// a fourth gains nothing).
 template <int D>
 struct FwdShape {
   static constexpr int BN = D == 256 ? 32 : 64;
   static constexpr int NW = D == 256 ? 8 : 4;
+  static constexpr int STAGES = D == 256 ? 3 : 2;
+  static constexpr int AHEAD = STAGES - 1;
 };
 
 // Scores of one 64-key tile in base 2 (+ bias), masked when MASK (keys outside
@@ -93,9 +99,15 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
   constexpr int NKB = kBN / 32;         // 32-key blocks of S^T
   constexpr int NST = D / 16;  // 16-wide k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  constexpr int STAGES = FwdShape<D>::STAGES;
+  constexpr int AHEAD = FwdShape<D>::AHEAD;  // tiles copied ahead of the one computed
+  static_assert(AHEAD >= 1, "at least one tile ahead");
   static_assert(!BIAS || kBN == 64, "bias tiles are 64 keys");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][kBN * D];
+  // With a bias each tile's bias loads are issued before its copies, and the tile-end
+  // wait below counts on the copies being the only newer vector-memory operations.
+  static_assert(!BIAS || AHEAD == 1, "bias tiles double-buffered");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[STAGES][kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[STAGES][kBN * D];
 
   if (*a.dev_err) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -167,19 +179,12 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
   const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)g * D;
 
-  if (n_tiles > t_first) {
-    const int64_t first = (int64_t)t_first * kBN * kv_stride;
-    dma_rows<D, kBN, NW>(lds_k[0], kbase + first, kv_stride, L - t_first * kBN, wave, lane);
-    dma_rows<D, kBN, NW>(lds_v[0], vbase + first, kv_stride, L - t_first * kBN, wave, lane);
-  }
-  wait_vm_all();
-  __syncthreads();
-
-  // Copies of the next tile, one instruction at a time between the S^T products: CPW per
-  // wave (K then V, CPW / 2 each), one every NST / CPW k-steps.  Copy p of a tensor is
-  // tile instruction i = w + NW p, rows i RPI + lane / G (clamped to the valid rows),
-  // swizzled granule of the row.  The last tile re-copies itself into the free buffer so
-  // that the loop has no branch.
+  // Copies of tile t + STAGES - 1, one instruction at a time between the S^T products of
+  // tile t: CPW per wave (K then V, CPW / 2 each), one every NST / CPW k-steps.  Copy p
+  // of a tensor is tile instruction i = w + NW p, rows i RPI + lane / G (clamped to the
+  // valid rows), swizzled granule of the row.  Tiles past the last re-copy the last one
+  // into a free buffer, so that the loop has no branch and every wave issues CPW copies
+  // per tile.
   constexpr int G = D / 8, RPI = 64 / G;
   constexpr int CPW = 2 * (kBN * G / 64 / NW);
   static_assert(CPW >= 2 && NST % CPW == 0, "copies spread evenly over the S^T k-steps");
@@ -214,24 +219,35 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
     dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
   };
 
+  if (n_tiles > t_first) {
+    for (int j = 0; j < AHEAD; ++j) {
+      const CopyStep c0 = copy_step(t_first + j, j);
+#pragma unroll
+      for (int p = 0; p < CPW; ++p) copy_one(c0, p);
+    }
+  }
+  wait_vm<(AHEAD - 1) * CPW>();  // the first tile has landed
+  __syncthreads();
+
+  int buf = 0;  // (t - t_first) % STAGES
   for (int t = t_first; t < n_tiles; ++t) {
     const int key0 = t * kBN;
-    const int buf = (t - t_first) & 1;
-    const CopyStep cs = copy_step(t + 1, buf ^ 1);
+    const int buf_fill = (buf + AHEAD) % STAGES;  // tile t + AHEAD
+    const CopyStep cs = copy_step(t + AHEAD, buf_fill);
     if (BIAS && t + 1 < n_tiles) load_bias_tile(bias_nxt, bias_row, key0 + kBN, L, kg, a.bias_len);
-
-    if (nrows > 0 && !(CAUSAL && key0 > wave_last_pos)) {
+    const bool active = nrows > 0 && !(CAUSAL && key0 > wave_last_pos);
+    const uint16_t* kt = lds_k[buf];
+    const uint16_t* vt = lds_v[buf];
+    // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
+    // fragments for step st+1 are requested before the MFMAs of step st.
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    if (active) {
       // scheduling hint: interleave the step's MFMAs with its LDS reads and VALU work
       // (on the 64x8192 D256 rank share: 10% faster than no hint; strategy 1 another
       // 0.7% over strategy 0)
       if (D != 256) __builtin_amdgcn_iglp_opt(1);
-      const uint16_t* kt = lds_k[buf];
-      const uint16_t* vt = lds_v[buf];
-      // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
-      // fragments for step st+1 are requested before the MFMAs of step st.
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
       {
         u32x4 kf[NKB];
 #pragma unroll
@@ -251,7 +267,11 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
           for (int kb = 0; kb < NKB; ++kb) kf[kb] = nf[kb];
         }
       }
-
+    } else {
+#pragma unroll
+      for (int p = 0; p < CPW; ++p) copy_one(cs, p);
+    }
+    if (active) {
       // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.  The
       // masked and unmasked tiles take separate, wave-uniform paths.
       const bool need_mask = (key0 + kBN > kv_hi) || (key0 < kv_lo) ||
@@ -305,17 +325,18 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
           va = nv;
         }
       }
-    } else {
-#pragma unroll
-      for (int p = 0; p < CPW; ++p) copy_one(cs, p);
     }
-    wait_vm_all();
+    // tile t + 1 has landed in every wave's share (later tiles may be in flight), and
+    // every wave is past its last read of buffer `buf`, which the next copies fill
+    wait_vm<(AHEAD - 1) * CPW>();
     __syncthreads();
+    buf = buf + 1 == STAGES ? 0 : buf + 1;
     if (BIAS) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) bias_cur[i] = bias_nxt[i];
     }
   }
+  wait_vm_all();  // no copy into LDS outlives the workgroup
 
   if (col >= nrows) return;
   // A row with no visible key in the window: O = 0 and LSE = -inf (merges as nothing).
