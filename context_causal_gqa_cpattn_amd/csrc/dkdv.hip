@@ -190,6 +190,9 @@ __device__ __forceinline__ void mfma32_v(f32x16& c, u32x4 a, u32x4 b) {
 __device__ __forceinline__ void xdl_fence(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x));
 }
+__device__ __forceinline__ void xdl_fence2(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
+}
 
 // The residue products of one tile, dV^T += dO^T rp and dK^T += Q^T rd for every 32-row
 // block, only when flag (wave-uniform) is non-zero.  The branch and the products are one
@@ -777,20 +780,32 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
             nq_ = tr_a(qtt, st + 1);
             nd_ = tr_a(dtt, st + 1);
           }
-          s = mfma32(fq, kf[st], s);
-          dp = mfma32(fd, vf[st], dp);
+          if (st == 0) {
+            s = mfma32_v0(fq, kf[0]);
+            dp = mfma32_v0(fd, vf[0]);
+          } else {
+            mfma32_v(s, fq, kf[st]);
+            mfma32_v(dp, fd, vf[st]);
+          }
           fq = nq_;
           fd = nd_;
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      xdl_fence2(s, dp);
 
-      // Softmax of this tile, between the dV/dK products of the previous one.
+      // Softmax of this tile, between the dV/dK products of the previous one, without a
+      // mask; on the steps that need one (the causal diagonal, keys past the sequence
+      // end or outside the key window: element r is visible iff c(r) >= thr, c(r) =
+      // 8 (r / 4) + r % 4 its query less 4 hl) the hidden elements' P and dS are set to
+      // 0 afterwards.  Queries past the chunk end have LSE = +inf: P = 0 already.
+      const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
+      const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
       const float* lse = lds_st[buf];
       const float* dl = lds_st[buf] + kTq;
       auto sm_block = [&](int blk) {
-        softmax_part<EPB, true, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
-                                              nq, tile_pos0, bias_cur);
+        softmax_part<EPB, false, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
+                                               nq, tile_pos0, bias_cur);
       };
       if (have_prev) {
         residue(pbuf, rp, rd, res_prev);
@@ -798,6 +813,14 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       } else {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) sm_block(blk);
+      }
+      if (fix) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool vis = 8 * (r >> 2) + (r & 3) >= thr;
+          s[r] = vis ? s[r] : 0.f;
+          dp[r] = vis ? dp[r] : 0.f;
+        }
       }
       // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
       pp[0] = to_bf16x8(s, 0);
