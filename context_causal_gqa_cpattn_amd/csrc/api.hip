@@ -121,7 +121,7 @@ struct Plan {
   int64_t ds_head_blocks;  // dS blocks per query head
   int64_t off_ds, off_ds_zero, off_ds_blocks, ds_bytes;  // ds_bytes: offsets, zero block, blocks
   dim3 grid_fwd, grid_fwd1d, grid_fwdk, grid_prepass, grid_dkdv, grid_dbias, grid_dbias_ds, grid_dqds;
-  int bpc_fwd, bpc_fwdk, bpc_prepass, bpc_dqds, kv_tiles;
+  int bpc_fwd, bpc_fwdk, bpc_prepass, bpc_dqds, kv_tiles, kv_slots;
 };
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -184,7 +184,9 @@ int make_plan(const cpattn_problem* p, Plan& pl) {
   pl.kv_tiles = (int)cdiv(p->max_kv_len, kDkdvKeys);
   const int64_t gx_fwd = (int64_t)p->num_chunks * pl.bpc_fwd;
   const int64_t gx_pre = (int64_t)p->num_chunks * pl.bpc_prepass;
-  const int64_t gx_kv = (int64_t)p->num_seqs * pl.kv_tiles;
+  // causal: a dK/dV workgroup takes key tiles j and n - 1 - j of its sequence
+  pl.kv_slots = p->causal ? (int)cdiv(pl.kv_tiles, 2) : pl.kv_tiles;
+  const int64_t gx_kv = (int64_t)p->num_seqs * pl.kv_slots;
   if (gx_fwd > kGridMax || gx_pre > kGridMax || gx_kv > kGridMax || p->hq / pl.hpw > 65535 ||
       p->hkv > 65535)
     return fail(CPATTN_EUNSUPPORTED, "problem too large for one launch");
@@ -528,6 +530,8 @@ int enqueue_dkdv(const cpattn_problem* p, const Plan& pl, AttnArgs a, void* dk, 
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
   a.accumulate = acc ? 1 : 0;
+  a.kv_tiles = pl.kv_slots;
+  a.kv_pair = pl.kv_slots != pl.kv_tiles;
   if (ds_area) {
     DsTableArgs t{};
     t.seq_lens = a.seq_lens;

@@ -450,7 +450,8 @@ struct AttnArgs {
   int num_seqs, num_chunks;
   int hq, hkv, group, hpw;  // group = hq/hkv; hpw = query heads per workgroup
   int blocks_per_chunk;     // position blocks per chunk (forward / dQ / pre-pass)
-  int kv_tiles;             // KV tiles per sequence (dK/dV)
+  int kv_tiles;             // KV tiles per sequence (dK/dV): workgroups per (sequence, KV head)
+  int kv_pair;              // dK/dV: each workgroup takes two key tiles (see dkdv_kernel)
   int bias_len;
   int accumulate;           // dK/dV: 0 store, 1 add
   int parts;                // dBias partitions of the chunk list

@@ -481,418 +481,428 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, n = lane & 31;
   const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.kv_tiles, a.kv_tiles, a.hkv);
-  const int kt = logical % a.kv_tiles;
+  const int kslot = logical % a.kv_tiles;
   const int rest = logical / a.kv_tiles;
   const int g = rest % a.hkv;
   const int b = rest / a.hkv;
   const int L = rfl(a.seq_lens[b]);
-  const int wg_key0 = kt * kDkdvKeys;
-  // no key of the tile in the sequence or in the key window [kv_lo, kv_hi)
-  if (wg_key0 >= L || wg_key0 >= a.kv_hi || wg_key0 + kDkdvKeys <= a.kv_lo) return;
-  const int64_t koff = rfl(a.seq_offsets[b]);
-  const int wkey0 = wg_key0 + wave * 32;
-  const int nk = max(0, min(32, L - wkey0));
-  const int key = wkey0 + n;  // this lane's key (column of S, dP, dK^T, dV^T)
-  const bool key_ok = n < nk && key >= a.kv_lo && key < a.kv_hi;  // in the sequence and the window
-  const bool wave_in_window = wkey0 >= a.kv_lo && wkey0 + 32 <= a.kv_hi;
+  // With a.kv_pair (causal masking) the workgroup takes two key tiles of its sequence,
+  // kslot and nt - 1 - kslot (nt = the sequence's tiles), one after the other: a tile's
+  // work falls with its position, and the pairs even it out across workgroups.
+  const int nt = (L + kDkdvKeys - 1) / kDkdvKeys;
+  for (int pass = 0; pass < (a.kv_pair ? 2 : 1); ++pass) {
+    const int kt = !a.kv_pair ? kslot : pass == 0 ? (kslot < (nt + 1) / 2 ? kslot : -1)
+                                                  : (kslot < nt / 2 ? nt - 1 - kslot : -1);
+    if (kt < 0) continue;
+    if (pass > 0) __syncthreads();  // the first pass's last reads of the tile buffers are done
+    const int wg_key0 = kt * kDkdvKeys;
+    // no key of the tile in the sequence or in the key window [kv_lo, kv_hi)
+    if (wg_key0 >= L || wg_key0 >= a.kv_hi || wg_key0 + kDkdvKeys <= a.kv_lo) continue;
+    const int64_t koff = rfl(a.seq_offsets[b]);
+    const int wkey0 = wg_key0 + wave * 32;
+    const int nk = max(0, min(32, L - wkey0));
+    const int key = wkey0 + n;  // this lane's key (column of S, dP, dK^T, dV^T)
+    const bool key_ok = n < nk && key >= a.kv_lo && key < a.kv_hi;  // in the sequence and the window
+    const bool wave_in_window = wkey0 >= a.kv_lo && wkey0 + 32 <= a.kv_hi;
 
-  // K and V as B operands: lane (hl, n) holds key n, dimensions 16 st + 8 hl + [0, 8).
-  // Lanes past the sequence end load its last key (finite values; their P and dS are 0).
-  const int64_t kv_stride = a.kv_pitch * D;
-  u32x4 kf[NS], vf[NS];
-  {
-    const int64_t off = (koff + min(key, L - 1)) * kv_stride + (int64_t)g * D + hl * 8;
+    // K and V as B operands: lane (hl, n) holds key n, dimensions 16 st + 8 hl + [0, 8).
+    // Lanes past the sequence end load its last key (finite values; their P and dS are 0).
+    const int64_t kv_stride = a.kv_pitch * D;
+    u32x4 kf[NS], vf[NS];
+    {
+      const int64_t off = (koff + min(key, L - 1)) * kv_stride + (int64_t)g * D + hl * 8;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      kf[st] = ld16(a.k + off + st * 16);
-      vf[st] = ld16(a.v + off + st * 16);
+      for (int st = 0; st < NS; ++st) {
+        kf[st] = ld16(a.k + off + st * 16);
+        vf[st] = ld16(a.v + off + st * 16);
+      }
     }
-  }
-  f32x16 dkt[NB], dvt[NB];
+    f32x16 dkt[NB], dvt[NB];
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    dkt[blk] = f32x16{};
-    dvt[blk] = f32x16{};
-  }
-  // S/dP A operand, k-step st: row n of S is tile query n; its 8 values are dimensions
-  // 16 st + 8 hl + 4 r + j (r = 0, 1 reads), gathered by transposing reads in which
-  // source lane 4 j + m of each 16-lane group reads dimension row 16 st + 8 hl + 4 r + j
-  // at stored query positions c0 .. c0 + 3, c0 = 16 (group & 1) + 4 swap2(m) (the stored
-  // order sigma16 within 16 queries, undone).  The row's granule swizzle is
-  // tswz = 2 hl + r, the same for every st.
-  int tra[2];
-  {
-    const int grp = lane >> 4, j = (lane >> 2) & 3, m = lane & 3;
-    const int sm = ((m & 1) << 1) | (m >> 1);
-    const int gq = 2 * (grp & 1) + (sm >> 1);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      tra[r] = (8 * hl + 4 * r + j) * kTq + ((gq ^ (2 * hl + r)) * 8) + 4 * (sm & 1);
-  }
-  // dV/dK A operand, k-step t: row 32 blk + n, granule (2 t + hl) ^ tswz(n).
-  const int tr_off0 = n * kTq + ((hl ^ tswz(n)) * 8);
-  const int tr_off1 = n * kTq + (((2 + hl) ^ tswz(n)) * 8);
-
-  const int c_end = chunk_lower_bound(a.chunks, a.num_chunks, b + 1);
-  const int h0 = g * a.group;  // the group's first query head
-  QTileIter cur;
-  cur.c = chunk_lower_bound(a.chunks, a.num_chunks, b);
-  bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0, h0, L);
-  // With a bias: the lane's 16 bias values of a tile (element r is query 8 (r / 4) +
-  // 4 hl + r % 4 of the tile, key `key`), loaded one step ahead so that their latency
-  // is spent under the previous step's products; used only after the step's wait.
-  float bias_cur[16] = {}, bias_nxt[16] = {};
-  auto load_bias = [&](const QTileIter& it, float (&bv)[16]) {
-    const float* bh = a.bias + (int64_t)(g * a.group + it.hh) * a.bias_len * a.bias_len;
-    const int tp0 = it.ch.pos0 + it.qt * kTq;
-    const int kk = min(key, a.bias_len - 1);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = 8 * (r >> 2) + 4 * hl + (r & 3);
-      bv[r] = bh[(int64_t)min(tp0 + qi, a.bias_len - 1) * a.bias_len + kk];
+    for (int blk = 0; blk < NB; ++blk) {
+      dkt[blk] = f32x16{};
+      dvt[blk] = f32x16{};
     }
-  };
-  if (BIAS && have) load_bias(cur, bias_cur);
-  // the wave that copies each step's row statistics
-  const bool stats_wave = __builtin_amdgcn_readfirstlane(wave) == kWaves - 1;
-  if (have) {
-    dma_tiles<D>(lds_t[0][0], lds_t[0][1], a, cur, wave, lane);
-    if (stats_wave) dma_stats(lds_st[0], a, cur.unit, lane);
-  }
-  wait_vm_all();
-  __syncthreads();
+    // S/dP A operand, k-step st: row n of S is tile query n; its 8 values are dimensions
+    // 16 st + 8 hl + 4 r + j (r = 0, 1 reads), gathered by transposing reads in which
+    // source lane 4 j + m of each 16-lane group reads dimension row 16 st + 8 hl + 4 r + j
+    // at stored query positions c0 .. c0 + 3, c0 = 16 (group & 1) + 4 swap2(m) (the stored
+    // order sigma16 within 16 queries, undone).  The row's granule swizzle is
+    // tswz = 2 hl + r, the same for every st.
+    int tra[2];
+    {
+      const int grp = lane >> 4, j = (lane >> 2) & 3, m = lane & 3;
+      const int sm = ((m & 1) << 1) | (m >> 1);
+      const int gq = 2 * (grp & 1) + (sm >> 1);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        tra[r] = (8 * hl + 4 * r + j) * kTq + ((gq ^ (2 * hl + r)) * 8) + 4 * (sm & 1);
+    }
+    // dV/dK A operand, k-step t: row 32 blk + n, granule (2 t + hl) ^ tswz(n).
+    const int tr_off0 = n * kTq + ((hl ^ tswz(n)) * 8);
+    const int tr_off1 = n * kTq + (((2 + hl) ^ tswz(n)) * 8);
 
-  // dV/dK products of one tile: A operands from buffer pb, B = packed P / dS.  The
-  // operand stream (per block: dO^T steps 0 and 1, then Q^T steps 0 and 1) is read
-  // three products ahead.  Between the blocks, body(blk) issues independent work.
-  auto dvdk = [&](int pb, const u32x4 (&pp)[2], const u32x4 (&pd)[2], auto&& body) {
-    const uint16_t* qtt = lds_t[pb][0];
-    const uint16_t* dtt = lds_t[pb][1];
-    constexpr int NOP = 4 * NB;
-    auto operand = [&](int i) {
-      const int blk = i >> 2, which = i & 3;
-      const uint16_t* t = (which < 2) ? dtt : qtt;
-      return ld16(t + blk * 32 * kTq + ((which & 1) ? tr_off1 : tr_off0));
+    const int c_end = chunk_lower_bound(a.chunks, a.num_chunks, b + 1);
+    const int h0 = g * a.group;  // the group's first query head
+    QTileIter cur;
+    cur.c = chunk_lower_bound(a.chunks, a.num_chunks, b);
+    bool have = seek_chunk<CAUSAL>(a, cur, c_end, wg_key0, h0, L);
+    // With a bias: the lane's 16 bias values of a tile (element r is query 8 (r / 4) +
+    // 4 hl + r % 4 of the tile, key `key`), loaded one step ahead so that their latency
+    // is spent under the previous step's products; used only after the step's wait.
+    float bias_cur[16] = {}, bias_nxt[16] = {};
+    auto load_bias = [&](const QTileIter& it, float (&bv)[16]) {
+      const float* bh = a.bias + (int64_t)(g * a.group + it.hh) * a.bias_len * a.bias_len;
+      const int tp0 = it.ch.pos0 + it.qt * kTq;
+      const int kk = min(key, a.bias_len - 1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 8 * (r >> 2) + 4 * hl + (r & 3);
+        bv[r] = bh[(int64_t)min(tp0 + qi, a.bias_len - 1) * a.bias_len + kk];
+      }
     };
-    u32x4 f[4];
-    f[0] = operand(0);
-    f[1] = operand(1);
-    f[2] = operand(2);
-#pragma unroll
-    for (int i = 0; i < NOP; ++i) {
-      if (i + 3 < NOP) f[(i + 3) & 3] = operand(i + 3);
-      const int blk = i >> 2, which = i & 3;
-      if (which < 2) dvt[blk] = mfma32(f[i & 3], pp[which], dvt[blk]);
-      else dkt[blk] = mfma32(f[i & 3], pd[which & 1], dkt[blk]);
-      if (which == 3) body(blk);
-      __builtin_amdgcn_sched_barrier(0);
+    if (BIAS && have) load_bias(cur, bias_cur);
+    // the wave that copies each step's row statistics
+    const bool stats_wave = __builtin_amdgcn_readfirstlane(wave) == kWaves - 1;
+    if (have) {
+      dma_tiles<D>(lds_t[0][0], lds_t[0][1], a, cur, wave, lane);
+      if (stats_wave) dma_stats(lds_st[0], a, cur.unit, lane);
     }
-  };
-
-  u32x4 pp[2] = {}, pd[2] = {};  // packed P and dS of the previous tile
-  u32x4 rp[2] = {}, rd[2] = {};  // their BF16 residues, when res_prev
-  int buf = 0, pbuf = 0;
-  bool have_prev = false;
-  uint32_t res_prev = 0;
-  auto nop = [](int) {};
-  // Residue products of the tile in buffer pb (lane addresses of its k-step 0 / 1 operands).
-  const uint32_t res_a0 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off0;
-  const uint32_t res_a1 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off1;
-  auto residue = [&](int pb, const u32x4 (&rp)[2], const u32x4 (&rd)[2], uint32_t flag) {
-    const uint32_t boff = (uint32_t)pb * (2u * TE * 2u);
-    residue_products<NB, TE * 2>(dvt, dkt, res_a0 + boff, res_a1 + boff, rp, rd, flag);
-  };
-  // Tile copies of the next step: for D >= 128 one instruction every other S/dP k-step
-  // (every wave issues D / 32 of them; without a next tile the current one is re-copied
-  // into the free buffer), for smaller D all at once.  Copy k of a tensor by this wave
-  // moves the tile's 1 KB piece i = wave + kWaves k: the lane offsets are fixed.
-  constexpr bool SPREAD = D >= 128;
-  constexpr int TI = D * kTq * 2 / 1024 / kWaves;  // copies per wave per tensor
-  const int wu = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t voff[SPREAD ? TI : 1];
-#pragma unroll
-  for (int k = 0; k < (SPREAD ? TI : 1); ++k) voff[k] = (uint32_t)lane * 16u + (uint32_t)(wu + kWaves * k) * 1024u;
-  const char* const qt_base = uniform_ptr(a.qt);
-  const char* const dot_base = uniform_ptr(a.dot);
-  while (have) {
-    QTileIter nxt = cur;
-    const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0, h0, L);
-    const int nbuf = (buf + 1 == kBufs) ? 0 : buf + 1;
-    const int src_unit = have_next ? nxt.unit : cur.unit;
-    const int64_t src_off = (int64_t)src_unit * (D * kTq * 2);
-    const char* cb[2] = {qt_base + src_off, dot_base + src_off};
-    const uint32_t clw = lds_addr(lds_t[nbuf][0]) + (uint32_t)wu * 1024u;
-    auto copy_one = [&](int p) {  // p < 2 TI: tensor p / TI, copy p % TI
-      const int which = p / TI, k = p % TI;
-      dma16_add(cb[which], voff[k], clw, (uint32_t)(which * TE * 2 + k * kWaves * 1024));
-    };
-    if (stats_wave) dma_stats(lds_st[nbuf], a, src_unit, lane);
-    if (BIAS && have_next) load_bias(nxt, bias_nxt);
-    if (!SPREAD && have_next) dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, wave, lane);
-
-    // Every wave runs every tile of the loop: tiles that a wave's keys do not see (at the
-    // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
-    const int nq = min(kTq, cur.ch.len - cur.qt * kTq);
-    const int tile_pos0 = cur.ch.pos0 + cur.qt * kTq;
-    uint32_t res_cur = 0;
-
-    // A operand of the S / dP products, k-step st, from the transposed tile t.
-    auto tr_a = [&](const uint16_t* t, int st) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[0]));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[1]));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      return u32x4{l2[0], l2[1], h2[0], h2[1]};
-    };
-    if constexpr (SPLIT) {
-      // One tile as a stream of 64 products in four phases, so that the softmax runs on
-      // the vector ALU while the matrix core works: (1) S, (2) dP, with P = exp2(S c - LSE)
-      // formed element by element under it, (3) dV^T += dO^T P, with dS = P (dP - Delta)
-      // formed under it, (4) dK^T += Q^T dS.  The A operands of the stream are read from
-      // LDS three products ahead.
-      static_assert(!BIAS, "no bias term at this head dimension");
-      const uint16_t* qtt = lds_t[buf][0];
-      const uint16_t* dtt = lds_t[buf][1];
-      // Elements that a mask may hide this step: the causal diagonal, and keys past the
-      // sequence end or outside the key window (queries past the chunk end have LSE =
-      // +inf, so their P is 0 already).  Element r is visible iff c(r) >= thr, with
-      // c(r) = 8 (r / 4) + r % 4 its query less 4 hl.
-      const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
-      const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
-      // the lane's 16 LSE / Delta values (element r: query 8 (r / 4) + 4 hl + r % 4)
-      auto row16 = [&](const float* x, float (&out)[16]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(x + 8 * i + 4 * hl);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) out[4 * i + j] = v[j];
-        }
-      };
-      auto opnd = [&](int i) -> u32x4 {
-        if (i < NS) return tr_a(qtt, i);
-        if (i < 2 * NS) return tr_a(dtt, i - NS);
-        const int j = i & 15;  // (3) dO^T, (4) Q^T: block j / 2, k-step j % 2
-        return ld16((i < 48 ? dtt : qtt) + (j >> 1) * 32 * kTq + ((j & 1) ? tr_off1 : tr_off0));
-      };
-      static_assert(2 * NS == 32 && 4 * NB == 32, "64 products per step");
-      f32x16 s, dp;
-      float lv[16], dlv[16];
-      u32x4 sp[2], sd[2];  // BF16 residues of P and dS (set when flag)
-      uint32_t flag = 0;
-      const uint32_t boff = (uint32_t)buf * (2u * TE * 2u);
-      u32x4 ring[4];
-      ring[0] = opnd(0);
-      ring[1] = opnd(1);
-      ring[2] = opnd(2);
-      // product i of the stream: its A operand, with the read of product i + 3 issued
-      auto next_a = [&](int i) {
-        if (i + 3 < 64) ring[(i + 3) & 3] = opnd(i + 3);
-        return ring[i & 3];
-      };
-      // (1) S; the next tile's copies every other k-step
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const u32x4 A = next_a(i);
-        if ((i & 1) == 0) copy_one(i >> 1);
-        if (i == 0)
-          s = mfma32_v0(A, kf[0]);
-        else
-          mfma32_v(s, A, kf[i]);
-        if (i == 12) row16(lds_st[buf], lv);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // (2) dP; P two elements per product, then the mask, the packing, the residue decision
-#pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        const u32x4 A = next_a(16 + st);
-        if (st == 0) {
-          dp = mfma32_v0(A, vf[0]);
-          xdl_fence(s);
-        } else {
-          mfma32_v(dp, A, vf[st]);
-        }
-        if (st >= 1 && st <= 8) {
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * (st - 1) + e;
-            s[r] = exp2f_fast(fmaf(s[r], a.scale_log2, -lv[r]));
-          }
-        }
-        if (st == 9 && fix) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) >= thr) ? s[r] : 0.f;
-        }
-        if (st == 10) {
-          pp[0] = to_bf16x8(s, 0);
-          pp[1] = to_bf16x8(s, 8);
-        }
-        if (st == 11) flag = wave_has_large_p(s);
-        if (st == 12) row16(lds_st[buf] + kTq, dlv);
-        if (st == 13 && flag) {
-          sp[0] = residue_bf16x8(s, pp[0], 0);
-          sp[1] = residue_bf16x8(s, pp[1], 8);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // (3) dV^T += dO^T P; dS two elements per product, its packing and residues
-      residue_half<NB, TE * 2>(dvt, res_a0 + boff, res_a1 + boff, sp, flag);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const u32x4 A = next_a(32 + j);
-        dvt[j >> 1] = mfma32(A, pp[j & 1], dvt[j >> 1]);
-        if (j == 0) xdl_fence(dp);
-        if (j >= 1 && j <= 8) {
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * (j - 1) + e;
-            dp[r] = s[r] * (dp[r] - dlv[r]);
-          }
-        }
-        if (j == 9) {
-          pd[0] = to_bf16x8(dp, 0);
-          pd[1] = to_bf16x8(dp, 8);
-        }
-        if (j == 10 && flag) {
-          sd[0] = residue_bf16x8(dp, pd[0], 0);
-          sd[1] = residue_bf16x8(dp, pd[1], 8);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // (4) dK^T += Q^T dS
-      residue_half<NB, 0>(dkt, res_a0 + boff, res_a1 + boff, sd, flag);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const u32x4 A = next_a(48 + j);
-        dkt[j >> 1] = mfma32(A, pd[j & 1], dkt[j >> 1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      // S and dP of this tile; each A operand is read one k-step ahead.
-      f32x16 s = {}, dp = {};
-      {
-        const uint16_t* qtt = lds_t[buf][0];
-        const uint16_t* dtt = lds_t[buf][1];
-        u32x4 fq = tr_a(qtt, 0), fd = tr_a(dtt, 0);
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          if (SPREAD && (st & 1) == 0) copy_one(st >> 1);
-          u32x4 nq_ = fq, nd_ = fd;
-          if (st + 1 < NS) {
-            nq_ = tr_a(qtt, st + 1);
-            nd_ = tr_a(dtt, st + 1);
-          }
-          if (st == 0) {
-            s = mfma32_v0(fq, kf[0]);
-            dp = mfma32_v0(fd, vf[0]);
-          } else {
-            mfma32_v(s, fq, kf[st]);
-            mfma32_v(dp, fd, vf[st]);
-          }
-          fq = nq_;
-          fd = nd_;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      xdl_fence2(s, dp);
-
-      // Softmax of this tile, between the dV/dK products of the previous one, without a
-      // mask; on the steps that need one (the causal diagonal, keys past the sequence
-      // end or outside the key window: element r is visible iff c(r) >= thr, c(r) =
-      // 8 (r / 4) + r % 4 its query less 4 hl) the hidden elements' P and dS are set to
-      // 0 afterwards.  Queries past the chunk end have LSE = +inf: P = 0 already.
-      const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
-      const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
-      const float* lse = lds_st[buf];
-      const float* dl = lds_st[buf] + kTq;
-      auto sm_block = [&](int blk) {
-        softmax_part<EPB, false, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
-                                               nq, tile_pos0, bias_cur);
-      };
-      if (have_prev) {
-        residue(pbuf, rp, rd, res_prev);
-        dvdk(pbuf, pp, pd, sm_block);
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) sm_block(blk);
-      }
-      if (fix) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool vis = 8 * (r >> 2) + (r & 3) >= thr;
-          s[r] = vis ? s[r] : 0.f;
-          dp[r] = vis ? dp[r] : 0.f;
-        }
-      }
-      // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
-      pp[0] = to_bf16x8(s, 0);
-      pp[1] = to_bf16x8(s, 8);
-      pd[0] = to_bf16x8(dp, 0);
-      pd[1] = to_bf16x8(dp, 8);
-      res_cur = wave_has_large_p(s);
-      if (res_cur) {  // kept for the next step, with pp / pd
-        rp[0] = residue_bf16x8(s, pp[0], 0);
-        rp[1] = residue_bf16x8(s, pp[1], 8);
-        rd[0] = residue_bf16x8(dp, pd[0], 0);
-        rd[1] = residue_bf16x8(dp, pd[1], 8);
-      }
-    }
-
     wait_vm_all();
     __syncthreads();
-    // Stored dS for the dQ product: block (tile, head, key block of this wave), key row
-    // n, granules 2 e + hl (pd[e]).  Only blocks with a visible pair are stored; they are
-    // the blocks that dQ reads.  Issued after the step's wait for its copies, so that the
-    // stores complete during the next step instead of extending this one.
-    if (a.ds_out != nullptr && wkey0 < L && (!CAUSAL || wkey0 <= tile_pos0 + nq - 1)) {
-      uint16_t* dst = a.ds_out + (cur.ds + (wkey0 >> 5)) * 1024 + n * 32 + hl * 8;
-      // streaming stores: dS is read back only by the dQ product, long after
-      __builtin_nontemporal_store(pd[0], reinterpret_cast<u32x4*>(dst));
-      __builtin_nontemporal_store(pd[1], reinterpret_cast<u32x4*>(dst + 16));
-    }
-    cur = nxt;
-    if (BIAS) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bias_cur[r] = bias_nxt[r];
-    }
-    have = have_next;
-    have_prev = true;
-    res_prev = res_cur;
-    pbuf = buf;
-    buf = nbuf;
-  }
-  if (PIPE && have_prev) {
-    residue(pbuf, rp, rd, res_prev);
-    dvdk(pbuf, pp, pd, nop);
-  }
 
-  if (!key_ok) return;
-  // element r of block blk is dimension 32 blk + 8 (r / 4) + 4 hl + r % 4
-  const int64_t off = (koff + key) * kv_stride + (int64_t)g * D + hl * 4;
-  if (a.accumulate) {
+    // dV/dK products of one tile: A operands from buffer pb, B = packed P / dS.  The
+    // operand stream (per block: dO^T steps 0 and 1, then Q^T steps 0 and 1) is read
+    // three products ahead.  Between the blocks, body(blk) issues independent work.
+    auto dvdk = [&](int pb, const u32x4 (&pp)[2], const u32x4 (&pd)[2], auto&& body) {
+      const uint16_t* qtt = lds_t[pb][0];
+      const uint16_t* dtt = lds_t[pb][1];
+      constexpr int NOP = 4 * NB;
+      auto operand = [&](int i) {
+        const int blk = i >> 2, which = i & 3;
+        const uint16_t* t = (which < 2) ? dtt : qtt;
+        return ld16(t + blk * 32 * kTq + ((which & 1) ? tr_off1 : tr_off0));
+      };
+      u32x4 f[4];
+      f[0] = operand(0);
+      f[1] = operand(1);
+      f[2] = operand(2);
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t o = off + blk * 32 + i * 8;
-        const u32x2 ok = ld8(a.dk + o), ov = ld8(a.dv + o);
-        const float k0 = fmaf(dkt[blk][4 * i], a.scale, bf16_lo(ok[0]));
-        const float k1 = fmaf(dkt[blk][4 * i + 1], a.scale, bf16_hi(ok[0]));
-        const float k2 = fmaf(dkt[blk][4 * i + 2], a.scale, bf16_lo(ok[1]));
-        const float k3 = fmaf(dkt[blk][4 * i + 3], a.scale, bf16_hi(ok[1]));
-        st8(a.dk + o, u32x2{pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)});
-        st8(a.dv + o, u32x2{pack_bf16x2(dvt[blk][4 * i] + bf16_lo(ov[0]), dvt[blk][4 * i + 1] + bf16_hi(ov[0])),
-                            pack_bf16x2(dvt[blk][4 * i + 2] + bf16_lo(ov[1]), dvt[blk][4 * i + 3] + bf16_hi(ov[1]))});
+      for (int i = 0; i < NOP; ++i) {
+        if (i + 3 < NOP) f[(i + 3) & 3] = operand(i + 3);
+        const int blk = i >> 2, which = i & 3;
+        if (which < 2) dvt[blk] = mfma32(f[i & 3], pp[which], dvt[blk]);
+        else dkt[blk] = mfma32(f[i & 3], pd[which & 1], dkt[blk]);
+        if (which == 3) body(blk);
+        __builtin_amdgcn_sched_barrier(0);
       }
-  } else {
+    };
+
+    u32x4 pp[2] = {}, pd[2] = {};  // packed P and dS of the previous tile
+    u32x4 rp[2] = {}, rd[2] = {};  // their BF16 residues, when res_prev
+    int buf = 0, pbuf = 0;
+    bool have_prev = false;
+    uint32_t res_prev = 0;
+    auto nop = [](int) {};
+    // Residue products of the tile in buffer pb (lane addresses of its k-step 0 / 1 operands).
+    const uint32_t res_a0 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off0;
+    const uint32_t res_a1 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off1;
+    auto residue = [&](int pb, const u32x4 (&rp)[2], const u32x4 (&rd)[2], uint32_t flag) {
+      const uint32_t boff = (uint32_t)pb * (2u * TE * 2u);
+      residue_products<NB, TE * 2>(dvt, dkt, res_a0 + boff, res_a1 + boff, rp, rd, flag);
+    };
+    // Tile copies of the next step: for D >= 128 one instruction every other S/dP k-step
+    // (every wave issues D / 32 of them; without a next tile the current one is re-copied
+    // into the free buffer), for smaller D all at once.  Copy k of a tensor by this wave
+    // moves the tile's 1 KB piece i = wave + kWaves k: the lane offsets are fixed.
+    constexpr bool SPREAD = D >= 128;
+    constexpr int TI = D * kTq * 2 / 1024 / kWaves;  // copies per wave per tensor
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t voff[SPREAD ? TI : 1];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+    for (int k = 0; k < (SPREAD ? TI : 1); ++k) voff[k] = (uint32_t)lane * 16u + (uint32_t)(wu + kWaves * k) * 1024u;
+    const char* const qt_base = uniform_ptr(a.qt);
+    const char* const dot_base = uniform_ptr(a.dot);
+    while (have) {
+      QTileIter nxt = cur;
+      const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0, h0, L);
+      const int nbuf = (buf + 1 == kBufs) ? 0 : buf + 1;
+      const int src_unit = have_next ? nxt.unit : cur.unit;
+      const int64_t src_off = (int64_t)src_unit * (D * kTq * 2);
+      const char* cb[2] = {qt_base + src_off, dot_base + src_off};
+      const uint32_t clw = lds_addr(lds_t[nbuf][0]) + (uint32_t)wu * 1024u;
+      auto copy_one = [&](int p) {  // p < 2 TI: tensor p / TI, copy p % TI
+        const int which = p / TI, k = p % TI;
+        dma16_add(cb[which], voff[k], clw, (uint32_t)(which * TE * 2 + k * kWaves * 1024));
+      };
+      if (stats_wave) dma_stats(lds_st[nbuf], a, src_unit, lane);
+      if (BIAS && have_next) load_bias(nxt, bias_nxt);
+      if (!SPREAD && have_next) dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, wave, lane);
+
+      // Every wave runs every tile of the loop: tiles that a wave's keys do not see (at the
+      // causal diagonal, or past the sequence end) give P = dS = 0 and add nothing.
+      const int nq = min(kTq, cur.ch.len - cur.qt * kTq);
+      const int tile_pos0 = cur.ch.pos0 + cur.qt * kTq;
+      uint32_t res_cur = 0;
+
+      // A operand of the S / dP products, k-step st, from the transposed tile t.
+      auto tr_a = [&](const uint16_t* t, int st) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[0]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[1]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+      };
+      if constexpr (SPLIT) {
+        // One tile as a stream of 64 products in four phases, so that the softmax runs on
+        // the vector ALU while the matrix core works: (1) S, (2) dP, with P = exp2(S c - LSE)
+        // formed element by element under it, (3) dV^T += dO^T P, with dS = P (dP - Delta)
+        // formed under it, (4) dK^T += Q^T dS.  The A operands of the stream are read from
+        // LDS three products ahead.
+        static_assert(!BIAS, "no bias term at this head dimension");
+        const uint16_t* qtt = lds_t[buf][0];
+        const uint16_t* dtt = lds_t[buf][1];
+        // Elements that a mask may hide this step: the causal diagonal, and keys past the
+        // sequence end or outside the key window (queries past the chunk end have LSE =
+        // +inf, so their P is 0 already).  Element r is visible iff c(r) >= thr, with
+        // c(r) = 8 (r / 4) + r % 4 its query less 4 hl.
+        const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
+        const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
+        // the lane's 16 LSE / Delta values (element r: query 8 (r / 4) + 4 hl + r % 4)
+        auto row16 = [&](const float* x, float (&out)[16]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t o = off + blk * 32 + i * 8;
-        st8(a.dk + o, u32x2{pack_bf16x2(dkt[blk][4 * i] * a.scale, dkt[blk][4 * i + 1] * a.scale),
-                            pack_bf16x2(dkt[blk][4 * i + 2] * a.scale, dkt[blk][4 * i + 3] * a.scale)});
-        st8(a.dv + o, u32x2{pack_bf16x2(dvt[blk][4 * i], dvt[blk][4 * i + 1]),
-                            pack_bf16x2(dvt[blk][4 * i + 2], dvt[blk][4 * i + 3])});
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(x + 8 * i + 4 * hl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[4 * i + j] = v[j];
+          }
+        };
+        auto opnd = [&](int i) -> u32x4 {
+          if (i < NS) return tr_a(qtt, i);
+          if (i < 2 * NS) return tr_a(dtt, i - NS);
+          const int j = i & 15;  // (3) dO^T, (4) Q^T: block j / 2, k-step j % 2
+          return ld16((i < 48 ? dtt : qtt) + (j >> 1) * 32 * kTq + ((j & 1) ? tr_off1 : tr_off0));
+        };
+        static_assert(2 * NS == 32 && 4 * NB == 32, "64 products per step");
+        f32x16 s, dp;
+        float lv[16], dlv[16];
+        u32x4 sp[2], sd[2];  // BF16 residues of P and dS (set when flag)
+        uint32_t flag = 0;
+        const uint32_t boff = (uint32_t)buf * (2u * TE * 2u);
+        u32x4 ring[4];
+        ring[0] = opnd(0);
+        ring[1] = opnd(1);
+        ring[2] = opnd(2);
+        // product i of the stream: its A operand, with the read of product i + 3 issued
+        auto next_a = [&](int i) {
+          if (i + 3 < 64) ring[(i + 3) & 3] = opnd(i + 3);
+          return ring[i & 3];
+        };
+        // (1) S; the next tile's copies every other k-step
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const u32x4 A = next_a(i);
+          if ((i & 1) == 0) copy_one(i >> 1);
+          if (i == 0)
+            s = mfma32_v0(A, kf[0]);
+          else
+            mfma32_v(s, A, kf[i]);
+          if (i == 12) row16(lds_st[buf], lv);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // (2) dP; P two elements per product, then the mask, the packing, the residue decision
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+          const u32x4 A = next_a(16 + st);
+          if (st == 0) {
+            dp = mfma32_v0(A, vf[0]);
+            xdl_fence(s);
+          } else {
+            mfma32_v(dp, A, vf[st]);
+          }
+          if (st >= 1 && st <= 8) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 2 * (st - 1) + e;
+              s[r] = exp2f_fast(fmaf(s[r], a.scale_log2, -lv[r]));
+            }
+          }
+          if (st == 9 && fix) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) >= thr) ? s[r] : 0.f;
+          }
+          if (st == 10) {
+            pp[0] = to_bf16x8(s, 0);
+            pp[1] = to_bf16x8(s, 8);
+          }
+          if (st == 11) flag = wave_has_large_p(s);
+          if (st == 12) row16(lds_st[buf] + kTq, dlv);
+          if (st == 13 && flag) {
+            sp[0] = residue_bf16x8(s, pp[0], 0);
+            sp[1] = residue_bf16x8(s, pp[1], 8);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // (3) dV^T += dO^T P; dS two elements per product, its packing and residues
+        residue_half<NB, TE * 2>(dvt, res_a0 + boff, res_a1 + boff, sp, flag);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const u32x4 A = next_a(32 + j);
+          dvt[j >> 1] = mfma32(A, pp[j & 1], dvt[j >> 1]);
+          if (j == 0) xdl_fence(dp);
+          if (j >= 1 && j <= 8) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 2 * (j - 1) + e;
+              dp[r] = s[r] * (dp[r] - dlv[r]);
+            }
+          }
+          if (j == 9) {
+            pd[0] = to_bf16x8(dp, 0);
+            pd[1] = to_bf16x8(dp, 8);
+          }
+          if (j == 10 && flag) {
+            sd[0] = residue_bf16x8(dp, pd[0], 0);
+            sd[1] = residue_bf16x8(dp, pd[1], 8);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // (4) dK^T += Q^T dS
+        residue_half<NB, 0>(dkt, res_a0 + boff, res_a1 + boff, sd, flag);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const u32x4 A = next_a(48 + j);
+          dkt[j >> 1] = mfma32(A, pd[j & 1], dkt[j >> 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // S and dP of this tile; each A operand is read one k-step ahead.
+        f32x16 s = {}, dp = {};
+        {
+          const uint16_t* qtt = lds_t[buf][0];
+          const uint16_t* dtt = lds_t[buf][1];
+          u32x4 fq = tr_a(qtt, 0), fd = tr_a(dtt, 0);
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            if (SPREAD && (st & 1) == 0) copy_one(st >> 1);
+            u32x4 nq_ = fq, nd_ = fd;
+            if (st + 1 < NS) {
+              nq_ = tr_a(qtt, st + 1);
+              nd_ = tr_a(dtt, st + 1);
+            }
+            if (st == 0) {
+              s = mfma32_v0(fq, kf[0]);
+              dp = mfma32_v0(fd, vf[0]);
+            } else {
+              mfma32_v(s, fq, kf[st]);
+              mfma32_v(dp, fd, vf[st]);
+            }
+            fq = nq_;
+            fd = nd_;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        xdl_fence2(s, dp);
+
+        // Softmax of this tile, between the dV/dK products of the previous one, without a
+        // mask; on the steps that need one (the causal diagonal, keys past the sequence
+        // end or outside the key window: element r is visible iff c(r) >= thr, c(r) =
+        // 8 (r / 4) + r % 4 its query less 4 hl) the hidden elements' P and dS are set to
+        // 0 afterwards.  Queries past the chunk end have LSE = +inf: P = 0 already.
+        const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
+        const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
+        const float* lse = lds_st[buf];
+        const float* dl = lds_st[buf] + kTq;
+        auto sm_block = [&](int blk) {
+          softmax_part<EPB, false, CAUSAL, BIAS>(s, dp, blk * EPB, lse, dl, hl, a.scale_log2, key, key_ok,
+                                                 nq, tile_pos0, bias_cur);
+        };
+        if (have_prev) {
+          residue(pbuf, rp, rd, res_prev);
+          dvdk(pbuf, pp, pd, sm_block);
+        } else {
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk) sm_block(blk);
+        }
+        if (fix) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool vis = 8 * (r >> 2) + (r & 3) >= thr;
+            s[r] = vis ? s[r] : 0.f;
+            dp[r] = vis ? dp[r] : 0.f;
+          }
+        }
+        // k-step t of the dV/dK products = accumulator rows 8t .. 8t+7 of each lane
+        pp[0] = to_bf16x8(s, 0);
+        pp[1] = to_bf16x8(s, 8);
+        pd[0] = to_bf16x8(dp, 0);
+        pd[1] = to_bf16x8(dp, 8);
+        res_cur = wave_has_large_p(s);
+        if (res_cur) {  // kept for the next step, with pp / pd
+          rp[0] = residue_bf16x8(s, pp[0], 0);
+          rp[1] = residue_bf16x8(s, pp[1], 8);
+          rd[0] = residue_bf16x8(dp, pd[0], 0);
+          rd[1] = residue_bf16x8(dp, pd[1], 8);
+        }
       }
+
+      wait_vm_all();
+      __syncthreads();
+      // Stored dS for the dQ product: block (tile, head, key block of this wave), key row
+      // n, granules 2 e + hl (pd[e]).  Only blocks with a visible pair are stored; they are
+      // the blocks that dQ reads.  Issued after the step's wait for its copies, so that the
+      // stores complete during the next step instead of extending this one.
+      if (a.ds_out != nullptr && wkey0 < L && (!CAUSAL || wkey0 <= tile_pos0 + nq - 1)) {
+        uint16_t* dst = a.ds_out + (cur.ds + (wkey0 >> 5)) * 1024 + n * 32 + hl * 8;
+        // streaming stores: dS is read back only by the dQ product, long after
+        __builtin_nontemporal_store(pd[0], reinterpret_cast<u32x4*>(dst));
+        __builtin_nontemporal_store(pd[1], reinterpret_cast<u32x4*>(dst + 16));
+      }
+      cur = nxt;
+      if (BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bias_cur[r] = bias_nxt[r];
+      }
+      have = have_next;
+      have_prev = true;
+      res_prev = res_cur;
+      pbuf = buf;
+      buf = nbuf;
+    }
+    if (PIPE && have_prev) {
+      residue(pbuf, rp, rd, res_prev);
+      dvdk(pbuf, pp, pd, nop);
+    }
+
+    if (!key_ok) continue;  // (no barrier follows in this pass)
+    // element r of block blk is dimension 32 blk + 8 (r / 4) + 4 hl + r % 4
+    const int64_t off = (koff + key) * kv_stride + (int64_t)g * D + hl * 4;
+    if (a.accumulate) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t o = off + blk * 32 + i * 8;
+          const u32x2 ok = ld8(a.dk + o), ov = ld8(a.dv + o);
+          const float k0 = fmaf(dkt[blk][4 * i], a.scale, bf16_lo(ok[0]));
+          const float k1 = fmaf(dkt[blk][4 * i + 1], a.scale, bf16_hi(ok[0]));
+          const float k2 = fmaf(dkt[blk][4 * i + 2], a.scale, bf16_lo(ok[1]));
+          const float k3 = fmaf(dkt[blk][4 * i + 3], a.scale, bf16_hi(ok[1]));
+          st8(a.dk + o, u32x2{pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)});
+          st8(a.dv + o, u32x2{pack_bf16x2(dvt[blk][4 * i] + bf16_lo(ov[0]), dvt[blk][4 * i + 1] + bf16_hi(ov[0])),
+                              pack_bf16x2(dvt[blk][4 * i + 2] + bf16_lo(ov[1]), dvt[blk][4 * i + 3] + bf16_hi(ov[1]))});
+        }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t o = off + blk * 32 + i * 8;
+          st8(a.dk + o, u32x2{pack_bf16x2(dkt[blk][4 * i] * a.scale, dkt[blk][4 * i + 1] * a.scale),
+                              pack_bf16x2(dkt[blk][4 * i + 2] * a.scale, dkt[blk][4 * i + 3] * a.scale)});
+          st8(a.dv + o, u32x2{pack_bf16x2(dvt[blk][4 * i], dvt[blk][4 * i + 1]),
+                              pack_bf16x2(dvt[blk][4 * i + 2], dvt[blk][4 * i + 3])});
+        }
+    }
   }
 }
 
