@@ -39,6 +39,7 @@ struct FwdShape {
   static constexpr int NW = D == 256 ? 8 : 4;
   static constexpr int STAGES = D == 256 ? 3 : 2;
   static constexpr int AHEAD = STAGES - 1;
+  static constexpr bool PAIR = D <= 128;  // with causal masking: two position blocks each
 };
 
 // Scores of one 64-key tile in base 2 (+ bias), masked when MASK (keys outside
@@ -115,245 +116,261 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
 
   const int logical = xcd_group_order(blockIdx.x, gridDim.x / a.blocks_per_chunk, a.blocks_per_chunk, a.hq / a.hpw);
   const int n_hg = a.hq / a.hpw;
-  const int pb = logical % a.blocks_per_chunk;
+  const int pslot = logical % a.blocks_per_chunk;
   const int rest = logical / a.blocks_per_chunk;
   const int hg = rest % n_hg;
   const int c = rest / n_hg;
   const Chunk ch = load_chunk_uniform(a.chunks, c);
   const int segs = NW / a.hpw;
-  const int wg_row0 = pb * 32 * segs;
-  if (wg_row0 >= ch.len) return;
-  const int h = hg * a.hpw + (wave % a.hpw);
-  const int g = h / a.group;
-  const int row0 = wg_row0 + (wave / a.hpw) * 32;  // first chunk row of this wave
-  const int nrows = max(0, min(32, ch.len - row0));
-  const int L = rfl(a.seq_lens[ch.seq]);
-  const int64_t koff = rfl(a.seq_offsets[ch.seq]);
+  // With causal masking and D <= 128, in a chunk whose last block sees more than twice
+  // the keys of its first (one that starts near its sequence's start), workgroup pslot
+  // < nb / 2 takes position blocks pslot and nb - 1 - pslot (nb = the chunk's blocks),
+  // one after the other, and the other workgroups of the chunk exit: a block's work
+  // grows with its position, and the pairs even it out.  (At D = 256 the registers the
+  // second pass would hold are not there.)
+  constexpr bool PAIR = FwdShape<D>::PAIR && CAUSAL;
+  const int nb = (ch.len + 32 * segs - 1) / (32 * segs);
+  const bool pair = PAIR && ch.pos0 + ch.len > 2 * (ch.pos0 + 32 * segs);
+  for (int pass = 0; pass < (PAIR ? 2 : 1); ++pass) {
+    const int pb = !pair ? (pass == 0 ? pslot : -1)
+                         : pass == 0 ? (pslot < (nb + 1) / 2 ? pslot : -1)
+                                     : (pslot < nb / 2 ? nb - 1 - pslot : -1);
+    if (pb < 0) continue;
+    if (pass > 0) __syncthreads();  // the first pass's last reads of the K/V buffers are done
+    const int wg_row0 = pb * 32 * segs;
+    if (wg_row0 >= ch.len) continue;
+    const int h = hg * a.hpw + (wave % a.hpw);
+    const int g = h / a.group;
+    const int row0 = wg_row0 + (wave / a.hpw) * 32;  // first chunk row of this wave
+    const int nrows = max(0, min(32, ch.len - row0));
+    const int L = rfl(a.seq_lens[ch.seq]);
+    const int64_t koff = rfl(a.seq_offsets[ch.seq]);
 
-  const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + 32 * segs) - 1;
-  // Keys [kv_lo, kv_end) are visible to some row of the workgroup: the key window
-  // (the whole sequence without one) cut at the last position when causal.
-  const int kv_lo = a.kv_lo;
-  const int kv_hi = min(L, a.kv_hi);
-  const int kv_end = min(CAUSAL ? min(L, wg_last_pos + 1) : L, kv_hi);
-  const int t_first = kv_lo / kBN;                // first tile (absolute index)
-  const int n_tiles = (kv_end + kBN - 1) / kBN;   // one past the last tile
-  const int wave_first_pos = ch.pos0 + row0;
-  const int wave_last_pos = wave_first_pos + nrows - 1;
-  const int qpos = wave_first_pos + col;  // this lane's query position
+    const int wg_last_pos = ch.pos0 + min(ch.len, wg_row0 + 32 * segs) - 1;
+    // Keys [kv_lo, kv_end) are visible to some row of the workgroup: the key window
+    // (the whole sequence without one) cut at the last position when causal.
+    const int kv_lo = a.kv_lo;
+    const int kv_hi = min(L, a.kv_hi);
+    const int kv_end = min(CAUSAL ? min(L, wg_last_pos + 1) : L, kv_hi);
+    const int t_first = kv_lo / kBN;                // first tile (absolute index)
+    const int n_tiles = (kv_end + kBN - 1) / kBN;   // one past the last tile
+    const int wave_first_pos = ch.pos0 + row0;
+    const int wave_last_pos = wave_first_pos + nrows - 1;
+    const int qpos = wave_first_pos + col;  // this lane's query position
 
-  // Q^T as B operand: lane holds query `col`, dims [16*st + 8*kg, +8).
-  u32x4 qf[NST];
-  {
-    const uint16_t* qp = a.q + ((int64_t)(ch.q_row + row0 + col) * a.q_pitch + h) * D + kg * 8;
+    // Q^T as B operand: lane holds query `col`, dims [16*st + 8*kg, +8).
+    u32x4 qf[NST];
+    {
+      const uint16_t* qp = a.q + ((int64_t)(ch.q_row + row0 + col) * a.q_pitch + h) * D + kg * 8;
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
-      qf[st] = (col < nrows) ? ld16(qp + st * 16) : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  // Without a bias the scale is folded in after the max (max(c s) = c max(s) for c > 0)
-  // and into the FMA before each exponential; a negative scale is applied as |c| with Q
-  // negated (exact in BF16), a zero one as a tiny positive one (every score 0 either way).
-  const float c_eff = BIAS ? a.scale_log2 : fmaxf(fabsf(a.scale_log2), 1e-30f);
-  if (!BIAS && a.scale_log2 < 0.f) {
-#pragma unroll
-    for (int st = 0; st < NST; ++st) qf[st] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-  }
-
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  const TrOffsets<D> tro(lane);
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // With a bias, each tile's bias values are loaded one tile ahead (their latency is
-  // spent under the previous tile's products) and used after that tile's wait.
-  const float* bias_row = nullptr;
-  f32x4 bias_cur[8] = {}, bias_nxt[8] = {};
-  if (BIAS) {
-    bias_row = a.bias + ((int64_t)h * a.bias_len + min(qpos, a.bias_len - 1)) * a.bias_len;
-    if (n_tiles > t_first) load_bias_tile(bias_cur, bias_row, t_first * kBN, L, kg, a.bias_len);
-  }
-
-  const int64_t kv_stride = a.kv_pitch * D;
-  const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
-  const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)g * D;
-
-  // Copies of tile t + STAGES - 1, one instruction at a time between the S^T products of
-  // tile t: CPW per wave (K then V, CPW / 2 each), one every NST / CPW k-steps.  Copy p
-  // of a tensor is tile instruction i = w + NW p, rows i RPI + lane / G (clamped to the
-  // valid rows), swizzled granule of the row.  Tiles past the last re-copy the last one
-  // into a free buffer, so that the loop has no branch and every wave issues CPW copies
-  // per tile.
-  constexpr int G = D / 8, RPI = 64 / G;
-  constexpr int CPW = 2 * (kBN * G / 64 / NW);
-  static_assert(CPW >= 2 && NST % CPW == 0, "copies spread evenly over the S^T k-steps");
-  constexpr int CEVERY = NST / CPW;
-  const int wu = __builtin_amdgcn_readfirstlane(wave);
-  const int lane_row = lane / G;
-  const uint32_t rs_bytes = (uint32_t)(kv_stride * 2);
-  uint32_t gran[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) gran[e] = (uint32_t)(((lane % G) ^ swz<D>((wu + NW * e) * RPI + lane_row)) * 16);
-  struct CopyStep {
-    const char* bk;
-    const char* bv;
-    uint32_t lk, lv;
-    int last_row;
-  };
-  auto copy_step = [&](int t_next, int buf_next) {
-    const int tsrc = min(t_next, n_tiles - 1);
-    CopyStep c;
-    c.bk = uniform_ptr(kbase + (int64_t)tsrc * kBN * kv_stride);
-    c.bv = uniform_ptr(vbase + (int64_t)tsrc * kBN * kv_stride);
-    c.lk = lds_addr(lds_k[buf_next]);
-    c.lv = lds_addr(lds_v[buf_next]);
-    c.last_row = L - tsrc * kBN - 1;
-    return c;
-  };
-  auto copy_one = [&](const CopyStep& c, int p) {
-    const bool is_v = p >= CPW / 2;
-    const int pp = is_v ? p - CPW / 2 : p;
-    const int i = wu + NW * pp;
-    const int row = min(i * RPI + lane_row, c.last_row);
-    dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
-  };
-
-  if (n_tiles > t_first) {
-    for (int j = 0; j < AHEAD; ++j) {
-      const CopyStep c0 = copy_step(t_first + j, j);
-#pragma unroll
-      for (int p = 0; p < CPW; ++p) copy_one(c0, p);
+      for (int st = 0; st < NST; ++st)
+        qf[st] = (col < nrows) ? ld16(qp + st * 16) : u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  wait_vm<(AHEAD - 1) * CPW>();  // the first tile has landed
-  __syncthreads();
 
-  int buf = 0;  // (t - t_first) % STAGES
-  for (int t = t_first; t < n_tiles; ++t) {
-    const int key0 = t * kBN;
-    const int buf_fill = (buf + AHEAD) % STAGES;  // tile t + AHEAD
-    const CopyStep cs = copy_step(t + AHEAD, buf_fill);
-    if (BIAS && t + 1 < n_tiles) load_bias_tile(bias_nxt, bias_row, key0 + kBN, L, kg, a.bias_len);
-    const bool active = nrows > 0 && !(CAUSAL && key0 > wave_last_pos);
-    const uint16_t* kt = lds_k[buf];
-    const uint16_t* vt = lds_v[buf];
-    // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
-    // fragments for step st+1 are requested before the MFMAs of step st.
-    f32x16 s[NKB];
+    // Without a bias the scale is folded in after the max (max(c s) = c max(s) for c > 0)
+    // and into the FMA before each exponential; a negative scale is applied as |c| with Q
+    // negated (exact in BF16), a zero one as a tiny positive one (every score 0 either way).
+    const float c_eff = BIAS ? a.scale_log2 : fmaxf(fabsf(a.scale_log2), 1e-30f);
+    if (!BIAS && a.scale_log2 < 0.f) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-    if (active) {
-      // scheduling hint: interleave the step's MFMAs with its LDS reads and VALU work
-      // (on the 64x8192 D256 rank share: 10% faster than no hint; strategy 1 another
-      // 0.7% over strategy 0)
-      if (D != 256) __builtin_amdgcn_iglp_opt(1);
-      {
-        u32x4 kf[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kf[kb] = lds_row16<D>(kt, 32 * kb + col, kg);
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          u32x4 nf[NKB];
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            nf[kb] = kf[kb];
-            if (st + 1 < NST) nf[kb] = lds_row16<D>(kt, 32 * kb + col, (st + 1) * 2 + kg);
-          }
-          if (st % CEVERY == 0) copy_one(cs, st / CEVERY);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kf[kb], qf[st], s[kb]);
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) kf[kb] = nf[kb];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int p = 0; p < CPW; ++p) copy_one(cs, p);
+      for (int st = 0; st < NST; ++st) qf[st] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
     }
-    if (active) {
-      // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.  The
-      // masked and unmasked tiles take separate, wave-uniform paths.
-      const bool need_mask = (key0 + kBN > kv_hi) || (key0 < kv_lo) ||
-                             (CAUSAL && key0 + kBN - 1 > wave_first_pos);
-      float mx = -INFINITY;
-      if (need_mask) {
-        asm volatile("" ::: "memory");
-        scale_tile<BIAS, true, CAUSAL, NKB>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
-      } else {
-        scale_tile<BIAS, false, CAUSAL, NKB>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
-      }
-      mx = halves_max(mx);
-      if (!BIAS) mx *= c_eff;
-      // Lazy rescale: move the reference max only when it grows by more than 8 (x256).
-      if (__builtin_expect(__any(mx > m_run + 8.f), 0)) {
-        // A real branch: the rescale must not be if-converted into every tile.
-        asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f_fast(m_run - m_new);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs[2] = {0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = BIAS ? exp2f_fast(s[kb][r] - m_use) : exp2f_fast(fmaf(s[kb][r], c_eff, -m_use));
-          s[kb][r] = p;
-          rs[r & 1] += p;
-        }
-      l_run += rs[0] + rs[1];
 
-      // O^T += V^T P^T over the tile's 16-key steps; the V^T fragment of the next MFMA is
-      // requested before the current one issues.
-      {
-        constexpr int NPS = kBN / 16;
-        u32x4 pf[NPS];
+    f32x16 oacc[NDB];
 #pragma unroll
-        for (int st = 0; st < NPS; ++st) pf[st] = to_bf16x8(s[st >> 1], (st & 1) * 8);
-        u32x4 va = tr_frag_at<D>(vt, tro, 0, 0);
-#pragma unroll
-        for (int it = 0; it < NPS * NDB; ++it) {
-          const int st = it / NDB, db = it % NDB;
-          u32x4 nv = va;
-          if (it + 1 < NPS * NDB) nv = tr_frag_at<D>(vt, tro, (it + 1) / NDB, (it + 1) % NDB);
-          oacc[db] = mfma32(va, pf[st], oacc[db]);
-          va = nv;
-        }
-      }
-    }
-    // tile t + 1 has landed in every wave's share (later tiles may be in flight), and
-    // every wave is past its last read of buffer `buf`, which the next copies fill
-    wait_vm<(AHEAD - 1) * CPW>();
-    __syncthreads();
-    buf = buf + 1 == STAGES ? 0 : buf + 1;
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    const TrOffsets<D> tro(lane);
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // With a bias, each tile's bias values are loaded one tile ahead (their latency is
+    // spent under the previous tile's products) and used after that tile's wait.
+    const float* bias_row = nullptr;
+    f32x4 bias_cur[8] = {}, bias_nxt[8] = {};
     if (BIAS) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bias_cur[i] = bias_nxt[i];
+      bias_row = a.bias + ((int64_t)h * a.bias_len + min(qpos, a.bias_len - 1)) * a.bias_len;
+      if (n_tiles > t_first) load_bias_tile(bias_cur, bias_row, t_first * kBN, L, kg, a.bias_len);
     }
-  }
-  wait_vm_all();  // no copy into LDS outlives the workgroup
 
-  if (col >= nrows) return;
-  // A row with no visible key in the window: O = 0 and LSE = -inf (merges as nothing).
-  const float l = halves_sum(l_run);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* op = a.o_out + ((int64_t)(ch.q_row + row0 + col) * a.q_pitch + h) * D + kg * 4;
+    const int64_t kv_stride = a.kv_pitch * D;
+    const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)g * D;
+    const uint16_t* vbase = a.v + koff * kv_stride + (int64_t)g * D;
+
+    // Copies of tile t + STAGES - 1, one instruction at a time between the S^T products of
+    // tile t: CPW per wave (K then V, CPW / 2 each), one every NST / CPW k-steps.  Copy p
+    // of a tensor is tile instruction i = w + NW p, rows i RPI + lane / G (clamped to the
+    // valid rows), swizzled granule of the row.  Tiles past the last re-copy the last one
+    // into a free buffer, so that the loop has no branch and every wave issues CPW copies
+    // per tile.
+    constexpr int G = D / 8, RPI = 64 / G;
+    constexpr int CPW = 2 * (kBN * G / 64 / NW);
+    static_assert(CPW >= 2 && NST % CPW == 0, "copies spread evenly over the S^T k-steps");
+    constexpr int CEVERY = NST / CPW;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int lane_row = lane / G;
+    const uint32_t rs_bytes = (uint32_t)(kv_stride * 2);
+    uint32_t gran[2];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int e = 0; e < 2; ++e) gran[e] = (uint32_t)(((lane % G) ^ swz<D>((wu + NW * e) * RPI + lane_row)) * 16);
+    struct CopyStep {
+      const char* bk;
+      const char* bv;
+      uint32_t lk, lv;
+      int last_row;
+    };
+    auto copy_step = [&](int t_next, int buf_next) {
+      const int tsrc = min(t_next, n_tiles - 1);
+      CopyStep c;
+      c.bk = uniform_ptr(kbase + (int64_t)tsrc * kBN * kv_stride);
+      c.bv = uniform_ptr(vbase + (int64_t)tsrc * kBN * kv_stride);
+      c.lk = lds_addr(lds_k[buf_next]);
+      c.lv = lds_addr(lds_v[buf_next]);
+      c.last_row = L - tsrc * kBN - 1;
+      return c;
+    };
+    auto copy_one = [&](const CopyStep& c, int p) {
+      const bool is_v = p >= CPW / 2;
+      const int pp = is_v ? p - CPW / 2 : p;
+      const int i = wu + NW * pp;
+      const int row = min(i * RPI + lane_row, c.last_row);
+      dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
+    };
+
+    if (n_tiles > t_first) {
+      for (int j = 0; j < AHEAD; ++j) {
+        const CopyStep c0 = copy_step(t_first + j, j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[db][i * 4 + 0] * inv, oacc[db][i * 4 + 1] * inv);
-      w[1] = pack_bf16x2(oacc[db][i * 4 + 2] * inv, oacc[db][i * 4 + 3] * inv);
-      st8(op + db * 32 + i * 8, w);
+        for (int p = 0; p < CPW; ++p) copy_one(c0, p);
+      }
     }
-  if (kg == 0)
-    a.lse_out[(int64_t)h * a.q_rows + ch.q_row + row0 + col] = l > 0.f ? (m_run + log2f_fast(l)) * kLn2 : -INFINITY;
+    wait_vm<(AHEAD - 1) * CPW>();  // the first tile has landed
+    __syncthreads();
+
+    int buf = 0;  // (t - t_first) % STAGES
+    for (int t = t_first; t < n_tiles; ++t) {
+      const int key0 = t * kBN;
+      const int buf_fill = (buf + AHEAD) % STAGES;  // tile t + AHEAD
+      const CopyStep cs = copy_step(t + AHEAD, buf_fill);
+      if (BIAS && t + 1 < n_tiles) load_bias_tile(bias_nxt, bias_row, key0 + kBN, L, kg, a.bias_len);
+      const bool active = nrows > 0 && !(CAUSAL && key0 > wave_last_pos);
+      const uint16_t* kt = lds_k[buf];
+      const uint16_t* vt = lds_v[buf];
+      // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
+      // fragments for step st+1 are requested before the MFMAs of step st.
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+      if (active) {
+        // scheduling hint: interleave the step's MFMAs with its LDS reads and VALU work
+        // (on the 64x8192 D256 rank share: 10% faster than no hint; strategy 1 another
+        // 0.7% over strategy 0)
+        if (D != 256) __builtin_amdgcn_iglp_opt(1);
+        {
+          u32x4 kf[NKB];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) kf[kb] = lds_row16<D>(kt, 32 * kb + col, kg);
+#pragma unroll
+          for (int st = 0; st < NST; ++st) {
+            u32x4 nf[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+              nf[kb] = kf[kb];
+              if (st + 1 < NST) nf[kb] = lds_row16<D>(kt, 32 * kb + col, (st + 1) * 2 + kg);
+            }
+            if (st % CEVERY == 0) copy_one(cs, st / CEVERY);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(kf[kb], qf[st], s[kb]);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) kf[kb] = nf[kb];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < CPW; ++p) copy_one(cs, p);
+      }
+      if (active) {
+        // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.  The
+        // masked and unmasked tiles take separate, wave-uniform paths.
+        const bool need_mask = (key0 + kBN > kv_hi) || (key0 < kv_lo) ||
+                               (CAUSAL && key0 + kBN - 1 > wave_first_pos);
+        float mx = -INFINITY;
+        if (need_mask) {
+          asm volatile("" ::: "memory");
+          scale_tile<BIAS, true, CAUSAL, NKB>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
+        } else {
+          scale_tile<BIAS, false, CAUSAL, NKB>(s, a.scale_log2, bias_cur, key0, kv_lo, kv_hi, qpos, kg, mx);
+        }
+        mx = halves_max(mx);
+        if (!BIAS) mx *= c_eff;
+        // Lazy rescale: move the reference max only when it grows by more than 8 (x256).
+        if (__builtin_expect(__any(mx > m_run + 8.f), 0)) {
+          // A real branch: the rescale must not be if-converted into every tile.
+          asm volatile("" ::: "memory");
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = (m_new == -INFINITY) ? 1.f : exp2f_fast(m_run - m_new);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float rs[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = BIAS ? exp2f_fast(s[kb][r] - m_use) : exp2f_fast(fmaf(s[kb][r], c_eff, -m_use));
+            s[kb][r] = p;
+            rs[r & 1] += p;
+          }
+        l_run += rs[0] + rs[1];
+
+        // O^T += V^T P^T over the tile's 16-key steps; the V^T fragment of the next MFMA is
+        // requested before the current one issues.
+        {
+          constexpr int NPS = kBN / 16;
+          u32x4 pf[NPS];
+#pragma unroll
+          for (int st = 0; st < NPS; ++st) pf[st] = to_bf16x8(s[st >> 1], (st & 1) * 8);
+          u32x4 va = tr_frag_at<D>(vt, tro, 0, 0);
+#pragma unroll
+          for (int it = 0; it < NPS * NDB; ++it) {
+            const int st = it / NDB, db = it % NDB;
+            u32x4 nv = va;
+            if (it + 1 < NPS * NDB) nv = tr_frag_at<D>(vt, tro, (it + 1) / NDB, (it + 1) % NDB);
+            oacc[db] = mfma32(va, pf[st], oacc[db]);
+            va = nv;
+          }
+        }
+      }
+      // tile t + 1 has landed in every wave's share (later tiles may be in flight), and
+      // every wave is past its last read of buffer `buf`, which the next copies fill
+      wait_vm<(AHEAD - 1) * CPW>();
+      __syncthreads();
+      buf = buf + 1 == STAGES ? 0 : buf + 1;
+      if (BIAS) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bias_cur[i] = bias_nxt[i];
+      }
+    }
+    wait_vm_all();  // no copy into LDS outlives the workgroup
+
+    if (col >= nrows) continue;  // (no barrier follows in this pass)
+    // A row with no visible key in the window: O = 0 and LSE = -inf (merges as nothing).
+    const float l = halves_sum(l_run);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = a.o_out + ((int64_t)(ch.q_row + row0 + col) * a.q_pitch + h) * D + kg * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][i * 4 + 0] * inv, oacc[db][i * 4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][i * 4 + 2] * inv, oacc[db][i * 4 + 3] * inv);
+        st8(op + db * 32 + i * 8, w);
+      }
+    if (kg == 0)
+      a.lse_out[(int64_t)h * a.q_rows + ch.q_row + row0 + col] = l > 0.f ? (m_run + log2f_fast(l)) * kLn2 : -INFINITY;
+  }
 }
 
 template <int D, bool CAUSAL, bool BIAS>
