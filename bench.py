@@ -440,6 +440,31 @@ def kernel_rooflines(w, per_kernel, pairs):
     return out
 
 
+# The FP32 transcendental pipe: a wave64 v_exp_f32 takes four issue cycles of a 16-lane
+# SIMD at a quarter of the full rate, i.e. 4 lanes per cycle per SIMD: 256 CUs x 4 SIMDs x
+# 4 lanes x 2.4 GHz.
+PEAK_EXP_PER_S = 256 * 4 * 4 * 2.4e9
+
+
+def exp_roofline(w, per_kernel, pairs, ms):
+    """The exponentials of a step against the transcendental pipe: one per visible pair
+    and head in the forward, in dK/dV, and in the dBias pass that forms dS again (fp32),
+    none in dQ from the stored dS."""
+    per = {"fwd": pairs, "dkdv": pairs}
+    if w.bias is not None or getattr(w, "bias_len", 0):
+        per["dbias"] = pairs
+    out = {"peak_exp_per_s": PEAK_EXP_PER_S, "exp_per_step": sum(per.values())}
+    rate = out["exp_per_step"] / (ms * 1e-3)
+    out["step_exp_per_s"] = round(rate, 1)
+    out["step_frac"] = round(rate / PEAK_EXP_PER_S, 4)
+    out["kernels"] = {}
+    for n, cnt in per.items():
+        if n in per_kernel and per_kernel[n] > 0:
+            r = cnt / (per_kernel[n] * 1e-3)
+            out["kernels"][n] = {"exp_per_s": round(r, 1), "frac": round(r / PEAK_EXP_PER_S, 4)}
+    return out
+
+
 def ds_store_bytes(w):
     """Stored dS: one 2 KB block per (32-query tile, head, 32-key block with a visible pair)."""
     n = 0
@@ -504,10 +529,15 @@ def time_workload(cp, torch, W, cfg, args, seed, headline):
             cp.bwd_dbias(prob, lay, q, k, v, bias, lse, do, ws, dbias, err)
             mark(6)
 
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     cp.check(err)
+    # the step's device memory: inputs, outputs and the backward workspace (the library
+    # allocates nothing itself)
+    step_peak_gib = round(torch.cuda.max_memory_allocated() / 2 ** 30, 2)
     progress(f"config {cfg}: {args.warmup} warmup steps done; timing {args.steps}")
 
     n_ev = len(names) + 1
@@ -560,6 +590,7 @@ def time_workload(cp, torch, W, cfg, args, seed, headline):
         "bwd_tflops": round(bwd_tflops, 2),
         "kernel_ms_median": {n: round(x, 4) for n, x in per_kernel.items()},
         "kernel_rooflines": kernel_rooflines(w, per_kernel, pairs),
+        "exp_roofline": exp_roofline(w, per_kernel, pairs, ms),
         "prepass_gbs": round(pre_bytes / (per_kernel["prepass"] * 1e-3) / 1e9, 1),
         "dq_path": "stored dS" if use_ds else "recompute",
         "ds_bytes_per_step": ds_bytes,
@@ -583,6 +614,7 @@ def time_workload(cp, torch, W, cfg, args, seed, headline):
         res["ring_step"] = None if args.no_ring else ring_step_rates(cp, torch, w, q, k, v, do, bias, lay, fl)
         res["head_groups"] = None if args.no_heads else head_group_rates(cp, torch, w, q, k, v, do, bias, lay, fl)
     res["peak_mem_gib"] = round(torch.cuda.max_memory_allocated() / 2 ** 30, 2)
+    res["step_peak_mem_gib"] = step_peak_gib
     if not args.no_cpu:
         progress(f"config {cfg}: CPU baseline (oracle)")
         budget = args.cpu_seconds if headline.get("full") else args.extra_cpu_seconds
