@@ -254,12 +254,14 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
       const bool active = nrows > 0 && !(CAUSAL && key0 > wave_last_pos);
       const uint16_t* kt = lds_k[buf];
       const uint16_t* vt = lds_v[buf];
-      // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
-      // fragments for step st+1 are requested before the MFMAs of step st.
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
       if (active) {
+        // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
+        // fragments for step st+1 are requested before the MFMAs of step st.  (One
+        // branch for the products and the softmax: split in two, the S^T registers
+        // would have to hold zeros on the other path, 23 moves per tile.)
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
         // scheduling hint: interleave the step's MFMAs with its LDS reads and VALU work
         // (on the 64x8192 D256 rank share: 10% faster than no hint; strategy 1 another
         // 0.7% over strategy 0)
@@ -283,11 +285,6 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
             for (int kb = 0; kb < NKB; ++kb) kf[kb] = nf[kb];
           }
         }
-      } else {
-#pragma unroll
-        for (int p = 0; p < CPW; ++p) copy_one(cs, p);
-      }
-      if (active) {
         // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.  The
         // masked and unmasked tiles take separate, wave-uniform paths.
         const bool need_mask = (key0 + kBN > kv_hi) || (key0 < kv_lo) ||
@@ -341,6 +338,9 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
             va = nv;
           }
         }
+      } else {
+#pragma unroll
+        for (int p = 0; p < CPW; ++p) copy_one(cs, p);
       }
       // tile t + 1 has landed in every wave's share (later tiles may be in flight), and
       // every wave is past its last read of buffer `buf`, which the next copies fill
