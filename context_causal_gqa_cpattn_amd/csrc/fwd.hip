@@ -179,8 +179,48 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
     f32x16 oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-    const TrOffsets<D> tro(lane);
     float m_run = -INFINITY, l_run = 0.f;
+
+    // LDS operand reads as a lane pointer plus a constant (the tile loop is unrolled over
+    // the K/V buffers, so the buffer, the k-step and the block are all offset-field
+    // constants and a read costs no address arithmetic).
+    //  K (A operand of S^T): row 32 kb + col, logical granule 2 st + kg, stored at granule
+    //    g ^ swz(row); swz(row) < 16 and depends on the row mod 16, so kb and the granule's
+    //    bit 4 (st >= 8) enter as constants: KN lane pointers for st mod 8.
+    //  V^T (A operand of O^T): the tr_frag_at addresses, four lane parts lo(m) (m = db
+    //    mod 4) and their second reads hi_delta further on.
+    constexpr int KN = NST < 8 ? NST : 8;
+    constexpr int TILE_BYTES = kBN * D * 2;
+    using lds_cptr = const __attribute__((address_space(3))) char*;
+    lds_cptr kp[KN];
+#pragma unroll
+    for (int j = 0; j < KN; ++j)
+      kp[j] = CPATTN_LDS(const char, lds_k[0]) + (col * D + (((2 * j + kg) ^ swz<D>(col)) << 3)) * 2;
+    constexpr int VM = TrOffsets<D>::NM;
+    lds_cptr vlo[VM], vhi[VM];
+    {
+      const TrOffsets<D> tro(lane);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) {
+        vlo[m] = CPATTN_LDS(const char, lds_v[0]) + tro.lo(m) * 2;
+        vhi[m] = vlo[m] + tro.hi_delta * 2;
+      }
+    }
+    // K fragment of block kb, k-step st, buffer u
+    auto kread = [&](int u, int st, int kb) -> u32x4 {
+      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          kp[st & 7] + u * TILE_BYTES + (st >> 3) * 256 + kb * 64 * D);
+    };
+    // V^T fragment of rows [16 st, +16) and columns [32 db, +32), buffer u
+    auto vread = [&](int u, int st, int db) -> u32x4 {
+      const int off = u * TILE_BYTES + st * 32 * D + (db >> 2) * 256;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<__attribute__((address_space(3))) char*>(vlo[db & 3] + off)));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<__attribute__((address_space(3))) char*>(vhi[db & 3] + off)));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
 
     // With a bias, each tile's bias values are loaded one tile ahead (their latency is
     // spent under the previous tile's products) and used after that tile's wait.
@@ -235,25 +275,37 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
       dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
     };
 
+    // The copies are inline assembly, which the compiler's wait-count bookkeeping does
+    // not see; it does see the Q (and bias) loads above.  A full wait here, after the
+    // first tile's copies, shows it that Q has landed.  (With a partial count it places a
+    // wait for Q inside the loop, which then also drains the copies in flight.)
     if (n_tiles > t_first) {
-      for (int j = 0; j < AHEAD; ++j) {
+      const CopyStep c0 = copy_step(t_first, 0);
+#pragma unroll
+      for (int p = 0; p < CPW; ++p) copy_one(c0, p);
+    }
+    wait_vm_all();  // Q and the first tile have landed
+    if (n_tiles > t_first) {
+      for (int j = 1; j < AHEAD; ++j) {
         const CopyStep c0 = copy_step(t_first + j, j);
 #pragma unroll
         for (int p = 0; p < CPW; ++p) copy_one(c0, p);
       }
     }
-    wait_vm<(AHEAD - 1) * CPW>();  // the first tile has landed
     __syncthreads();
 
-    int buf = 0;  // (t - t_first) % STAGES
-    for (int t = t_first; t < n_tiles; ++t) {
+    // The tile loop, unrolled over the STAGES buffers: tile t uses buffer u = (t - t_first)
+    // mod STAGES.
+    for (int t0 = t_first; t0 < n_tiles; t0 += STAGES)
+#pragma unroll
+    for (int buf = 0; buf < STAGES; ++buf) {
+      const int t = t0 + buf;
+      if (t >= n_tiles) break;
       const int key0 = t * kBN;
       const int buf_fill = (buf + AHEAD) % STAGES;  // tile t + AHEAD
       const CopyStep cs = copy_step(t + AHEAD, buf_fill);
       if (BIAS && t + 1 < n_tiles) load_bias_tile(bias_nxt, bias_row, key0 + kBN, L, kg, a.bias_len);
       const bool active = nrows > 0 && !(CAUSAL && key0 > wave_last_pos);
-      const uint16_t* kt = lds_k[buf];
-      const uint16_t* vt = lds_v[buf];
       if (active) {
         // S^T for the tile's 32-key blocks, as interleaved accumulator chains; the LDS
         // fragments for step st+1 are requested before the MFMAs of step st.  (One
@@ -269,14 +321,14 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
         {
           u32x4 kf[NKB];
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) kf[kb] = lds_row16<D>(kt, 32 * kb + col, kg);
+          for (int kb = 0; kb < NKB; ++kb) kf[kb] = kread(buf, 0, kb);
 #pragma unroll
           for (int st = 0; st < NST; ++st) {
             u32x4 nf[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
               nf[kb] = kf[kb];
-              if (st + 1 < NST) nf[kb] = lds_row16<D>(kt, 32 * kb + col, (st + 1) * 2 + kg);
+              if (st + 1 < NST) nf[kb] = kread(buf, st + 1, kb);
             }
             if (st % CEVERY == 0) copy_one(cs, st / CEVERY);
 #pragma unroll
@@ -328,12 +380,12 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
           u32x4 pf[NPS];
 #pragma unroll
           for (int st = 0; st < NPS; ++st) pf[st] = to_bf16x8(s[st >> 1], (st & 1) * 8);
-          u32x4 va = tr_frag_at<D>(vt, tro, 0, 0);
+          u32x4 va = vread(buf, 0, 0);
 #pragma unroll
           for (int it = 0; it < NPS * NDB; ++it) {
             const int st = it / NDB, db = it % NDB;
             u32x4 nv = va;
-            if (it + 1 < NPS * NDB) nv = tr_frag_at<D>(vt, tro, (it + 1) / NDB, (it + 1) % NDB);
+            if (it + 1 < NPS * NDB) nv = vread(buf, (it + 1) / NDB, (it + 1) % NDB);
             oacc[db] = mfma32(va, pf[st], oacc[db]);
             va = nv;
           }
@@ -346,7 +398,6 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
       // every wave is past its last read of buffer `buf`, which the next copies fill
       wait_vm<(AHEAD - 1) * CPW>();
       __syncthreads();
-      buf = buf + 1 == STAGES ? 0 : buf + 1;
       if (BIAS) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) bias_cur[i] = bias_nxt[i];

@@ -48,6 +48,7 @@ SWEEP = [
     ([200, 150], 8, 8, 64, False, None),
     ([129], 2, 1, 256, False, "three"),
     ([64, 64], 4, 1, 128, True, "tail"),
+    ([300, 45], 3, 3, 256, True, None),
 ]
 
 
