@@ -140,7 +140,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
     const int wg_row0 = pb * 32 * segs;
     if (wg_row0 >= ch.len) continue;
     const int h = hg * a.hpw + (wave % a.hpw);
-    const int g = h / a.group;
+    const int g = rfl(hg * a.hpw / a.group);  // hpw divides the group: one KV head per workgroup
     const int row0 = wg_row0 + (wave / a.hpw) * 32;  // first chunk row of this wave
     const int nrows = max(0, min(32, ch.len - row0));
     const int L = rfl(a.seq_lens[ch.seq]);
@@ -251,11 +251,17 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
     uint32_t gran[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) gran[e] = (uint32_t)(((lane % G) ^ swz<D>((wu + NW * e) * RPI + lane_row)) * 16);
+    // the lane's source offset of copy pp of a tensor (row * row stride + granule; the
+    // granule is below the row stride, so clamping the row is a min of the offsets)
+    uint32_t roff[CPW / 2];
+#pragma unroll
+    for (int pp = 0; pp < CPW / 2; ++pp)
+      roff[pp] = (uint32_t)((wu + NW * pp) * RPI + lane_row) * rs_bytes + gran[pp & 1];
     struct CopyStep {
       const char* bk;
       const char* bv;
       uint32_t lk, lv;
-      int last_row;
+      uint32_t lim[2];  // offset of the last valid row's granule (clamp)
     };
     auto copy_step = [&](int t_next, int buf_next) {
       const int tsrc = min(t_next, n_tiles - 1);
@@ -264,15 +270,16 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
       c.bv = uniform_ptr(vbase + (int64_t)tsrc * kBN * kv_stride);
       c.lk = lds_addr(lds_k[buf_next]);
       c.lv = lds_addr(lds_v[buf_next]);
-      c.last_row = L - tsrc * kBN - 1;
+      const uint32_t last = (uint32_t)min(L - tsrc * kBN - 1, kBN - 1) * rs_bytes;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) c.lim[e] = last + gran[e];
       return c;
     };
     auto copy_one = [&](const CopyStep& c, int p) {
       const bool is_v = p >= CPW / 2;
       const int pp = is_v ? p - CPW / 2 : p;
       const int i = wu + NW * pp;
-      const int row = min(i * RPI + lane_row, c.last_row);
-      dma16_at(is_v ? c.bv : c.bk, (uint32_t)row * rs_bytes + gran[pp & 1], (is_v ? c.lv : c.lk) + i * 1024);
+      dma16_at(is_v ? c.bv : c.bk, min(roff[pp], c.lim[pp & 1]), (is_v ? c.lv : c.lk) + i * 1024);
     };
 
     // The copies are inline assembly, which the compiler's wait-count bookkeeping does
