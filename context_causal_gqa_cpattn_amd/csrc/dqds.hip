@@ -65,14 +65,6 @@ __device__ __forceinline__ int ds_tr_off(int lane) {
   return (4 * (G >> 1) + j) * 32 + (2 * (G & 1) + (u & 1)) * 8 + (u >> 1) * 4;
 }
 
-__device__ __forceinline__ u32x4 ds_frag(const uint16_t* blk, int off, int st) {
-  const uint16_t* b = blk + st * 16 * 32 + off;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + 8 * 32));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2[0], l2[1], h2[0], h2[1]};
-}
-
 }  // namespace
 
 template <int D, bool CAUSAL>
@@ -135,7 +127,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
 
   const int64_t kv_stride = a.kv_pitch * D;
   const uint16_t* kbase = a.k + koff * kv_stride + (int64_t)kvh * D;
-  // Copy instruction p (0 <= p < PER) of this wave for step kb into stage kb % kStages:
+  // Copy instruction p (0 <= p < PER) of this wave for step kb into its stage:
   // the K tile (rows past L repeat the last key), then the slot's dS blocks (with two
   // waves per slot, wave `part` copies tile `part`).  For a block that the tile does not
   // use (no visible pair: dK/dV did not store it) a block of zeros is copied, so that
@@ -143,17 +135,27 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   // last re-copy the last step into a free stage.
   const int wu = wave;
   const uint32_t rs_bytes = (uint32_t)(kv_stride * 2);
-  auto issue_one = [&](int kb_req, int p) {
+  // The lane's source offset of K-tile copy p (row * row stride + swizzled granule; the
+  // granule is below the row stride, so clamping the row is a min of the offsets), and
+  // the granule part alone.
+  constexpr int KG = D / 8, KRPI = 64 / KG;
+  uint32_t kroff[KI], kgran[KI];
+#pragma unroll
+  for (int p = 0; p < KI; ++p) {
+    const int i = KTI >= kWaves ? wu + kWaves * p : wu % KTI;  // instruction of the tile
+    const int r = i * KRPI + lane / KG;                        // tile row of this lane
+    kgran[p] = (uint32_t)(((lane % KG) ^ swz<D, 0>(r)) * 16);
+    kroff[p] = (uint32_t)r * rs_bytes + kgran[p];
+  }
+  // Stage of step kb: (kb - kb_first) mod kStages (the loop below is unrolled over the
+  // stages, so that LDS addresses are constants).
+  auto issue_one = [&](int kb_req, int p, int sb) {
     const int kb = min(kb_req, n_steps - 1);
-    const int sb = kb_req % kStages;
     if (p < KI) {
-      constexpr int G = D / 8, RPI = 64 / G;
       const int i = KTI >= kWaves ? wu + kWaves * p : wu % KTI;  // instruction of the tile
-      const int r = i * RPI + lane / G;  // tile row of this lane
-      const int row = min(r, L - kb * kBlk - 1);
+      const uint32_t last = (uint32_t)min(L - kb * kBlk - 1, kBlk - 1) * rs_bytes;
       const char* b = uniform_ptr(kbase + (int64_t)kb * kBlk * kv_stride);
-      dma16_at(b, (uint32_t)row * rs_bytes + (uint32_t)(((lane % G) ^ swz<D, 0>(r)) * 16),
-               lds_addr(lds_k[sb]) + i * 1024);
+      dma16_at(b, min(kroff[p], last + kgran[p]), lds_addr(lds_k[sb]) + i * 1024);
     } else {
       const int q = p - KI;
       const int ti = kSplit == 2 ? part : (q >> 1);
@@ -179,43 +181,60 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
       khi[j] = klo[j] + tro.hi_delta;
     }
   }
-  auto kfrag = [&](const uint16_t* kt, int st, int j) {
-    const uint16_t* b = kt + st * 16 * D;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + klo[j]));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, b + khi[j]));
+  // LDS reads as lane pointers plus constants (stage, k-step, block).
+  using lds_p = __attribute__((address_space(3))) uint16_t*;
+  lds_p klp[NDB], khp[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    klp[j] = CPATTN_LDS(uint16_t, lds_k[0]) + klo[j];
+    khp[j] = CPATTN_LDS(uint16_t, lds_k[0]) + khi[j];
+  }
+  auto kfrag = [&](int sb, int st, int j) {
+    const int o = sb * kBlk * D + st * 16 * D;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(klp[j] + o));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(khp[j] + o));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2[0], l2[1], h2[0], h2[1]};
   };
-  const int dso = ds_tr_off(lane);
+  // dS^T fragment of tile i, k-step st, stage sb
+  const lds_p dsp = CPATTN_LDS(uint16_t, lds_s[0]) + (slot * 2) * kBlkElems + ds_tr_off(lane);
+  auto dsfrag = [&](int sb, int i, int st) {
+    const int o = sb * kSlots * 2 * kBlkElems + i * kBlkElems + st * 16 * 32;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(dsp + o));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(dsp + o + 8 * 32));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
 
   if (n_steps > kb_first) {
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
 #pragma unroll
-      for (int p = 0; p < PER; ++p) issue_one(kb_first + s, p);
+      for (int p = 0; p < PER; ++p) issue_one(kb_first + s, p, s);
   }
 
-  for (int kb = kb_first; kb < n_steps; ++kb) {
-    wait_vm<(kStages - 2) * PER>();  // stage kb has landed (later stages may be in flight)
-    __syncthreads();                 // stage kb is in LDS for every wave; stage kb - 1 is free
+  for (int kb0 = kb_first; kb0 < n_steps; kb0 += kStages)
+#pragma unroll
+  for (int sb = 0; sb < kStages; ++sb) {
+    const int kb = kb0 + sb;
+    if (kb >= n_steps) break;
+    wait_vm<(kStages - 2) * PER>();  // stage sb has landed (later stages may be in flight)
+    __syncthreads();                 // stage sb is in LDS for every wave; the previous one is free
 
     // A tile without a visible pair in this block multiplies the zero block copied in
     // its place.  The copies of step kb + kStages - 1 are spread between the products.
-    const int sb = kb % kStages;
-    const uint16_t* kt = lds_k[sb];
-    const uint16_t* s0 = lds_s[sb] + (slot * 2) * kBlkElems;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const u32x4 b0 = ds_frag(s0, dso, st), b1 = ds_frag(s0 + kBlkElems, dso, st);
-      u32x4 ka = kfrag(kt, st, 0);
+      const u32x4 b0 = dsfrag(sb, 0, st), b1 = dsfrag(sb, 1, st);
+      u32x4 ka = kfrag(sb, st, 0);
 #pragma unroll
       for (int j = 0; j < NDB; ++j) {
         const int it = st * NDB + j;
 #pragma unroll
         for (int p = 0; p < PER; ++p)
-          if (p * 2 * NDB / PER == it) issue_one(kb + kStages - 1, p);
+          if (p * 2 * NDB / PER == it) issue_one(kb + kStages - 1, p, (sb + kStages - 1) % kStages);
         u32x4 nk = ka;
-        if (j + 1 < NDB) nk = kfrag(kt, st, j + 1);
+        if (j + 1 < NDB) nk = kfrag(sb, st, j + 1);
         acc[0][j] = mfma32(ka, b0, acc[0][j]);
         acc[1][j] = mfma32(ka, b1, acc[1][j]);
         ka = nk;
