@@ -98,7 +98,7 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   const int wg_row0 = pb * wg_pos;
   if (wg_row0 >= ch.len) return;  // uniform over the workgroup, before any barrier
   const int h = hg * a.hpw + (slot % a.hpw);
-  const int kvh = h / a.group;
+  const int kvh = rfl(h / a.group);
   const int row0 = wg_row0 + (slot / a.hpw) * 64;  // first chunk row of this slot (a tile start)
   const int L = rfl(a.seq_lens[ch.seq]);
   const int64_t koff = rfl(a.seq_offsets[ch.seq]);
@@ -149,20 +149,29 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   }
   // Stage of step kb: (kb - kb_first) mod kStages (the loop below is unrolled over the
   // stages, so that LDS addresses are constants).
+  // LDS addresses of stage 0 (converted once; a stage's are constants further on) and the
+  // dS sources as wave-uniform byte pointers (a block past a tile's visible ones is taken
+  // from the zero block by a select, not a branch).
+  const uint32_t lk0 = lds_addr(lds_k[0]);
+  const uint32_t ls0 = lds_addr(lds_s[0]) + (uint32_t)(slot * 2 * kBlkElems * 2);
+  const char* const zsrc = uniform_ptr(a.ds_zero);
+  const char* const dsrc_b[2] = {uniform_ptr(dsrc[0]), uniform_ptr(dsrc[1])};
   auto issue_one = [&](int kb_req, int p, int sb) {
     const int kb = min(kb_req, n_steps - 1);
     if (p < KI) {
       const int i = KTI >= kWaves ? wu + kWaves * p : wu % KTI;  // instruction of the tile
       const uint32_t last = (uint32_t)min(L - kb * kBlk - 1, kBlk - 1) * rs_bytes;
       const char* b = uniform_ptr(kbase + (int64_t)kb * kBlk * kv_stride);
-      dma16_at(b, min(kroff[p], last + kgran[p]), lds_addr(lds_k[sb]) + i * 1024);
+      dma16_at(b, min(kroff[p], last + kgran[p]), lk0 + (uint32_t)(sb * kBlk * D * 2 + i * 1024));
     } else {
       const int q = p - KI;
       const int ti = kSplit == 2 ? part : (q >> 1);
       const int half = q & 1;
-      const uint16_t* src = kb < nkb[ti] ? dsrc[ti] + (int64_t)kb * kBlkElems : a.ds_zero;
-      dma16_nt_at(uniform_ptr(src) + half * 1024, (uint32_t)lane * 16u,
-               lds_addr(lds_s[sb] + (slot * 2 + ti) * kBlkElems) + half * 1024);
+      const uint64_t blk = (uint64_t)(uintptr_t)(dsrc_b[ti] + (int64_t)kb * (kBlkElems * 2));
+      const uint64_t m = 0 - (uint64_t)(kb < nkb[ti]);  // all ones when the block is stored
+      const char* src = (const char*)(uintptr_t)((blk & m) | ((uint64_t)(uintptr_t)zsrc & ~m));
+      dma16_nt_at(src + half * 1024, (uint32_t)lane * 16u,
+                  ls0 + (uint32_t)(sb * kSlots * 2 * kBlkElems * 2 + ti * kBlkElems * 2 + half * 1024));
     }
   };
   f32x16 acc[2][NDB];
