@@ -623,6 +623,20 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     for (int k = 0; k < (SPREAD ? TI : 1); ++k) voff[k] = (uint32_t)lane * 16u + (uint32_t)(wu + kWaves * k) * 1024u;
     const char* const qt_base = uniform_ptr(a.qt);
     const char* const dot_base = uniform_ptr(a.dot);
+    // D = 256: the first three A operands of a step (S, k-steps 0-2, from its Q^T tile)
+    // are read right after the previous step's barrier, so that their latency passes
+    // under the step's scalar set-up instead of delaying its first product.
+    auto s_opnd = [&](const uint16_t* t, int st) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[0]));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(CPATTN_LDS(v4i16, t + st * 16 * kTq + tra[1]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+    u32x4 ring0[3];
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) ring0[k] = s_opnd(lds_t[0][0], k);
+    }
     while (have) {
       QTileIter nxt = cur;
       const bool have_next = advance<CAUSAL>(a, nxt, c_end, wg_key0, h0, L);
@@ -689,9 +703,9 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
         uint32_t flag = 0;
         const uint32_t boff = (uint32_t)buf * (2u * TE * 2u);
         u32x4 ring[4];
-        ring[0] = opnd(0);
-        ring[1] = opnd(1);
-        ring[2] = opnd(2);
+        ring[0] = ring0[0];
+        ring[1] = ring0[1];
+        ring[2] = ring0[2];
         // product i of the stream: its A operand, with the read of product i + 3 issued
         auto next_a = [&](int i) {
           if (i + 3 < 64) ring[(i + 3) & 3] = opnd(i + 3);
@@ -867,6 +881,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       res_prev = res_cur;
       pbuf = buf;
       buf = nbuf;
+      if constexpr (SPLIT) {  // (after the last step: reads of a re-copied tile, unused)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) ring0[k] = s_opnd(lds_t[buf][0], k);
+      }
     }
     if (PIPE && have_prev) {
       residue(pbuf, rp, rd, res_prev);
