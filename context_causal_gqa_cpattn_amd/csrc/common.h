@@ -187,13 +187,15 @@ __device__ __forceinline__ void dma16_at(const char* base, uint32_t off, uint32_
                : "memory", "m0");
 }
 
-// The same copy with the LDS address given as two wave-uniform parts (M0 is formed by
-// one scalar add inside the block).
+// The same copy with the LDS address given as a wave-uniform base plus a constant
+// lds_off (known at compile time once the caller's loops are unrolled): M0 is formed by
+// one scalar add with a literal inside the block, instead of a constant materialised in
+// a scalar register and an add.
 __device__ __forceinline__ void dma16_add(const char* base, uint32_t off, uint32_t lds,
                                           uint32_t lds_off) {
   asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(off), "s"(base), "s"(lds_off)
+               : "s"(lds), "v"(off), "s"(base), "i"(lds_off)
                : "memory", "m0", "scc");
 }
 
@@ -212,6 +214,13 @@ __device__ __forceinline__ void dma16_nt_at(const char* base, uint32_t off, uint
                :
                : "s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt_add(const char* base, uint32_t off, uint32_t lds,
+                                             uint32_t lds_off) {
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(lds), "v"(off), "s"(base), "i"(lds_off)
+               : "memory", "m0", "scc");
 }
 
 // 32-bit LDS address of a shared-memory pointer that is the same in every lane.

@@ -156,13 +156,17 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   const uint32_t ls0 = lds_addr(lds_s[0]) + (uint32_t)(slot * 2 * kBlkElems * 2);
   const char* const zsrc = uniform_ptr(a.ds_zero);
   const char* const dsrc_b[2] = {uniform_ptr(dsrc[0]), uniform_ptr(dsrc[1])};
+  // LDS destinations as a wave-uniform base plus a constant (folded into the M0 write):
+  // K tile instruction i = wave + kWaves p (or wave mod KTI), dS block ti of the slot
+  const uint32_t lkw = lk0 + (uint32_t)((KTI >= kWaves ? wu : wu % KTI) * 1024);
+  const uint32_t lsw = ls0 + (uint32_t)(kSplit == 2 ? part * kBlkElems * 2 : 0);
   auto issue_one = [&](int kb_req, int p, int sb) {
     const int kb = min(kb_req, n_steps - 1);
     if (p < KI) {
-      const int i = KTI >= kWaves ? wu + kWaves * p : wu % KTI;  // instruction of the tile
       const uint32_t last = (uint32_t)min(L - kb * kBlk - 1, kBlk - 1) * rs_bytes;
       const char* b = uniform_ptr(kbase + (int64_t)kb * kBlk * kv_stride);
-      dma16_at(b, min(kroff[p], last + kgran[p]), lk0 + (uint32_t)(sb * kBlk * D * 2 + i * 1024));
+      dma16_add(b, min(kroff[p], last + kgran[p]), lkw,
+                (uint32_t)(sb * kBlk * D * 2 + (KTI >= kWaves ? kWaves * p : 0) * 1024));
     } else {
       const int q = p - KI;
       const int ti = kSplit == 2 ? part : (q >> 1);
@@ -170,8 +174,9 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
       const uint64_t blk = (uint64_t)(uintptr_t)(dsrc_b[ti] + (int64_t)kb * (kBlkElems * 2));
       const uint64_t m = 0 - (uint64_t)(kb < nkb[ti]);  // all ones when the block is stored
       const char* src = (const char*)(uintptr_t)((blk & m) | ((uint64_t)(uintptr_t)zsrc & ~m));
-      dma16_nt_at(src + half * 1024, (uint32_t)lane * 16u,
-                  ls0 + (uint32_t)(sb * kSlots * 2 * kBlkElems * 2 + ti * kBlkElems * 2 + half * 1024));
+      dma16_nt_add(src + half * 1024, (uint32_t)lane * 16u, lsw,
+                   (uint32_t)(sb * kSlots * 2 * kBlkElems * 2 + (kSplit == 2 ? 0 : (q >> 1)) * kBlkElems * 2 +
+                              half * 1024));
     }
   };
   f32x16 acc[2][NDB];

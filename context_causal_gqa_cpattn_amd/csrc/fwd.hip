@@ -268,8 +268,8 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
       CopyStep c;
       c.bk = uniform_ptr(kbase + (int64_t)tsrc * kBN * kv_stride);
       c.bv = uniform_ptr(vbase + (int64_t)tsrc * kBN * kv_stride);
-      c.lk = lds_addr(lds_k[buf_next]);
-      c.lv = lds_addr(lds_v[buf_next]);
+      c.lk = lds_addr(lds_k[buf_next]) + (uint32_t)wu * 1024u;  // this wave's first instruction
+      c.lv = lds_addr(lds_v[buf_next]) + (uint32_t)wu * 1024u;
       const uint32_t last = (uint32_t)min(L - tsrc * kBN - 1, kBN - 1) * rs_bytes;
 #pragma unroll
       for (int e = 0; e < 2; ++e) c.lim[e] = last + gran[e];
@@ -278,8 +278,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
     auto copy_one = [&](const CopyStep& c, int p) {
       const bool is_v = p >= CPW / 2;
       const int pp = is_v ? p - CPW / 2 : p;
-      const int i = wu + NW * pp;
-      dma16_at(is_v ? c.bv : c.bk, min(roff[pp], c.lim[pp & 1]), (is_v ? c.lv : c.lk) + i * 1024);
+      dma16_add(is_v ? c.bv : c.bk, min(roff[pp], c.lim[pp & 1]), is_v ? c.lv : c.lk, (uint32_t)(NW * pp * 1024));
     };
 
     // The copies are inline assembly, which the compiler's wait-count bookkeeping does
