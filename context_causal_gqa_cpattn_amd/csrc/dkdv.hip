@@ -118,8 +118,8 @@ __device__ __forceinline__ void dma_tiles(uint16_t* lqt, uint16_t* ldot, const A
 
 // The tile's row statistics (64 floats: log2(e) LSE of its 32 rows, +inf past the chunk
 // end, then Delta) into LDS, one dword per lane; issued by one wave.
-__device__ __forceinline__ void dma_stats(float* lds, const AttnArgs& a, int unit, int lane) {
-  dma4_at(uniform_ptr(a.stats + (int64_t)unit * 64), (uint32_t)lane * 4u, lds_addr(lds));
+__device__ __forceinline__ void dma_stats(uint32_t lds, const AttnArgs& a, int unit, int lane) {
+  dma4_at(uniform_ptr(a.stats + (int64_t)unit * 64), (uint32_t)lane * 4u, lds);
 }
 
 // P and dS of accumulator elements [r0, r0 + n) of a lane, in place (s -> P, dp -> dS).
@@ -164,14 +164,23 @@ __device__ __forceinline__ u32x4 residue_bf16x8(const f32x16& v, const u32x4& hi
 }
 
 // Whether any probability of the wave's tile (P in the accumulator) reaches kResidueP.
+// P is not negative (an exponential, or 0 where masked), so its bits order like its
+// value as signed integers: the maximum is integer max3 steps (no NaN quieting), and the
+// result is a wave-uniform scalar.
 __device__ __forceinline__ uint32_t wave_has_large_p(const f32x16& p) {
-  float m = fmaxf(p[0], p[1]);
+  int m = max(__float_as_int(p[0]), __float_as_int(p[1]));
 #pragma unroll
-  for (int r = 2; r < 16; ++r) m = fmaxf(m, p[r]);
-  return __builtin_amdgcn_ballot_w64(m >= kResidueP) != 0 ? 1u : 0u;
+  for (int r = 2; r < 16; ++r) m = max(m, __float_as_int(p[r]));
+  const uint64_t b = __builtin_amdgcn_ballot_w64(m >= __float_as_int(kResidueP));
+  return (uint32_t)b | (uint32_t)(b >> 32);  // nonzero iff some lane's P reaches it
 }
 
 }  // namespace
+
+// A 16-byte LDS read at a 32-bit LDS address (the dV/dK operand addresses are formed as
+// integers once per step and shared with the residue products' assembly).
+using lds_u32x4_cptr = const __attribute__((address_space(3))) u32x4*;
+__device__ __forceinline__ u32x4 lds16(uint32_t addr) { return *(lds_u32x4_cptr)(uintptr_t)addr; }
 
 // S and dP products in arch VGPRs.  At D = 256 the dK^T/dV^T accumulators fill all 256
 // accumulation registers, and the compiler places every MFMA result there, so S and dP
@@ -212,7 +221,7 @@ __device__ __forceinline__ void residue_products(f32x16 (&dvt)[NB], f32x16 (&dkt
                                                  uint32_t a1, const u32x4 (&rp)[2], const u32x4 (&rd)[2],
                                                  uint32_t flag_in) {
   static_assert(TB + (NB - 1) * 2048 < 65536, "ds_read offsets are 16 bits");
-  const uint32_t flag = __builtin_amdgcn_readfirstlane(flag_in);
+  const uint32_t flag = flag_in;  // wave-uniform (a ballot), kept in a scalar register
   u32x4 t[4], u[4];
   (void)u;
   if constexpr (NB == 1) {
@@ -405,7 +414,7 @@ template <int NB, int OFF>
 __device__ __forceinline__ void residue_half(f32x16 (&acc)[NB], uint32_t a0, uint32_t a1,
                                              const u32x4 (&r)[2], uint32_t flag_in) {
   static_assert(NB == 8 && OFF + (NB - 1) * 2048 < 65536, "ds_read offsets are 16 bits");
-  const uint32_t flag = __builtin_amdgcn_readfirstlane(flag_in);
+  const uint32_t flag = flag_in;  // wave-uniform (a ballot), kept in a scalar register
   u32x4 t[2], u[2];
   if constexpr (NB == 8) {
     asm volatile(
@@ -504,6 +513,10 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     const int key = wkey0 + n;  // this lane's key (column of S, dP, dK^T, dV^T)
     const bool key_ok = n < nk && key >= a.kv_lo && key < a.kv_hi;  // in the sequence and the window
     const bool wave_in_window = wkey0 >= a.kv_lo && wkey0 + 32 <= a.kv_hi;
+    // The same tests from a scalar copy of the wave's first key, for the per-step
+    // wave-level decisions (mask fix-up, dS store), so that they are scalar branches.
+    const int wkey0_u = wg_key0 + __builtin_amdgcn_readfirstlane(wave) * 32;
+    const bool wave_masked_u = min(32, L - wkey0_u) < 32 || wkey0_u < a.kv_lo || wkey0_u + 32 > a.kv_hi;
 
     // K and V as B operands: lane (hl, n) holds key n, dimensions 16 st + 8 hl + [0, 8).
     // Lanes past the sequence end load its last key (finite values; their P and dS are 0).
@@ -566,22 +579,26 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     const bool stats_wave = __builtin_amdgcn_readfirstlane(wave) == kWaves - 1;
     if (have) {
       dma_tiles<D>(lds_t[0][0], lds_t[0][1], a, cur, wave, lane);
-      if (stats_wave) dma_stats(lds_st[0], a, cur.unit, lane);
+      if (stats_wave) dma_stats(lds_addr(lds_st[0]), a, cur.unit, lane);
     }
     wait_vm_all();
     __syncthreads();
 
+    // Lane addresses of the dV/dK A operands, k-steps 0 / 1, in buffer 0 (the residue
+    // products and the ordinary ones share them, plus the buffer's offset).
+    const uint32_t lds_st0 = lds_addr(lds_st[0]);
+    const uint32_t res_a0 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off0;
+    const uint32_t res_a1 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off1;
     // dV/dK products of one tile: A operands from buffer pb, B = packed P / dS.  The
     // operand stream (per block: dO^T steps 0 and 1, then Q^T steps 0 and 1) is read
     // three products ahead.  Between the blocks, body(blk) issues independent work.
     auto dvdk = [&](int pb, const u32x4 (&pp)[2], const u32x4 (&pd)[2], auto&& body) {
-      const uint16_t* qtt = lds_t[pb][0];
-      const uint16_t* dtt = lds_t[pb][1];
+      const uint32_t boff = (uint32_t)pb * (2u * TE * 2u);
+      const uint32_t a0 = res_a0 + boff, a1 = res_a1 + boff;
       constexpr int NOP = 4 * NB;
       auto operand = [&](int i) {
         const int blk = i >> 2, which = i & 3;
-        const uint16_t* t = (which < 2) ? dtt : qtt;
-        return ld16(t + blk * 32 * kTq + ((which & 1) ? tr_off1 : tr_off0));
+        return lds16(((which & 1) ? a1 : a0) + (uint32_t)((which < 2 ? TE * 2 : 0) + blk * 32 * kTq * 2));
       };
       u32x4 f[4];
       f[0] = operand(0);
@@ -605,8 +622,6 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     uint32_t res_prev = 0;
     auto nop = [](int) {};
     // Residue products of the tile in buffer pb (lane addresses of its k-step 0 / 1 operands).
-    const uint32_t res_a0 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off0;
-    const uint32_t res_a1 = lds_addr(lds_t[0][0]) + 2u * (uint32_t)tr_off1;
     auto residue = [&](int pb, const u32x4 (&rp)[2], const u32x4 (&rd)[2], uint32_t flag) {
       const uint32_t boff = (uint32_t)pb * (2u * TE * 2u);
       residue_products<NB, TE * 2>(dvt, dkt, res_a0 + boff, res_a1 + boff, rp, rd, flag);
@@ -649,7 +664,9 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
         const int which = p / TI, k = p % TI;
         dma16_add(cb[which], voff[k], clw, (uint32_t)(which * TE * 2 + k * kWaves * 1024));
       };
-      if (stats_wave) dma_stats(lds_st[nbuf], a, src_unit, lane);
+      // (the LDS address as an integer: a pointer into lds_st converted per step costs
+      // 64-bit arithmetic and a null test)
+      if (stats_wave) dma_stats(lds_st0 + (uint32_t)nbuf * (2u * kTq * 4u), a, src_unit, lane);
       if (BIAS && have_next) load_bias(nxt, bias_nxt);
       if (!SPREAD && have_next) dma_tiles<D>(lds_t[nbuf][0], lds_t[nbuf][1], a, nxt, wave, lane);
 
@@ -675,11 +692,12 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
         static_assert(!BIAS, "no bias term at this head dimension");
         const uint16_t* qtt = lds_t[buf][0];
         const uint16_t* dtt = lds_t[buf][1];
+        const uint32_t a0 = res_a0 + (uint32_t)buf * (2u * TE * 2u), a1 = a0 + (res_a1 - res_a0);
         // Elements that a mask may hide this step: the causal diagonal, and keys past the
         // sequence end or outside the key window (queries past the chunk end have LSE =
         // +inf, so their P is 0 already).  Element r is visible iff c(r) >= thr, with
         // c(r) = 8 (r / 4) + r % 4 its query less 4 hl.
-        const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
+        const bool fix = (CAUSAL && tile_pos0 < wkey0_u + 31) || wave_masked_u;
         const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
         // the lane's 16 LSE / Delta values (element r: query 8 (r / 4) + 4 hl + r % 4)
         auto row16 = [&](const float* x, float (&out)[16]) {
@@ -694,7 +712,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
           if (i < NS) return tr_a(qtt, i);
           if (i < 2 * NS) return tr_a(dtt, i - NS);
           const int j = i & 15;  // (3) dO^T, (4) Q^T: block j / 2, k-step j % 2
-          return ld16((i < 48 ? dtt : qtt) + (j >> 1) * 32 * kTq + ((j & 1) ? tr_off1 : tr_off0));
+          return lds16(((j & 1) ? a1 : a0) + (uint32_t)((i < 48 ? TE * 2 : 0) + (j >> 1) * 32 * kTq * 2));
         };
         static_assert(2 * NS == 32 && 4 * NB == 32, "64 products per step");
         f32x16 s, dp;
@@ -757,7 +775,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         // (3) dV^T += dO^T P; dS two elements per product, its packing and residues
-        residue_half<NB, TE * 2>(dvt, res_a0 + boff, res_a1 + boff, sp, flag);
+        residue_half<NB, TE * 2>(dvt, a0, a1, sp, flag);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const u32x4 A = next_a(32 + j);
@@ -781,7 +799,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         // (4) dK^T += Q^T dS
-        residue_half<NB, 0>(dkt, res_a0 + boff, res_a1 + boff, sd, flag);
+        residue_half<NB, 0>(dkt, a0, a1, sd, flag);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const u32x4 A = next_a(48 + j);
@@ -822,7 +840,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
         // end or outside the key window: element r is visible iff c(r) >= thr, c(r) =
         // 8 (r / 4) + r % 4 its query less 4 hl) the hidden elements' P and dS are set to
         // 0 afterwards.  Queries past the chunk end have LSE = +inf: P = 0 already.
-        const bool fix = (CAUSAL && tile_pos0 < wkey0 + 31) || nk < 32 || !wave_in_window;
+        const bool fix = (CAUSAL && tile_pos0 < wkey0_u + 31) || wave_masked_u;
         const int thr = !key_ok ? (1 << 20) : CAUSAL ? key - tile_pos0 - 4 * hl : -(1 << 20);
         const float* lse = lds_st[buf];
         const float* dl = lds_st[buf] + kTq;
@@ -865,8 +883,8 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
       // n, granules 2 e + hl (pd[e]).  Only blocks with a visible pair are stored; they are
       // the blocks that dQ reads.  Issued after the step's wait for its copies, so that the
       // stores complete during the next step instead of extending this one.
-      if (a.ds_out != nullptr && wkey0 < L && (!CAUSAL || wkey0 <= tile_pos0 + nq - 1)) {
-        uint16_t* dst = a.ds_out + (cur.ds + (wkey0 >> 5)) * 1024 + n * 32 + hl * 8;
+      if (a.ds_out != nullptr && wkey0_u < L && (!CAUSAL || wkey0_u <= tile_pos0 + nq - 1)) {
+        uint16_t* dst = a.ds_out + (cur.ds + (wkey0_u >> 5)) * 1024 + n * 32 + hl * 8;
         // streaming stores: dS is read back only by the dQ product, long after
         __builtin_nontemporal_store(pd[0], reinterpret_cast<u32x4*>(dst));
         __builtin_nontemporal_store(pd[1], reinterpret_cast<u32x4*>(dst + 16));
