@@ -160,11 +160,20 @@ __global__ __launch_bounds__(DsCfg<D>::kThreads) void dq_ds_kernel(const AttnArg
   // K tile instruction i = wave + kWaves p (or wave mod KTI), dS block ti of the slot
   const uint32_t lkw = lk0 + (uint32_t)((KTI >= kWaves ? wu : wu % KTI) * 1024);
   const uint32_t lsw = ls0 + (uint32_t)(kSplit == 2 ? part * kBlkElems * 2 : 0);
+  // Source offsets without a multiply by a clamped step index: step kb's K rows start
+  // kb * k_stride bytes after kbase; steps past the last re-copy the last one, and only
+  // the last step can have fewer than kBlk valid keys.
+  const int64_t k_stride = (int64_t)kBlk * kv_stride * 2;
+  const int kb_last = max(n_steps - 1, 0);
+  const char* const kbase_b = uniform_ptr(kbase);
+  const uint32_t klast_full = (uint32_t)(kBlk - 1) * rs_bytes;
+  const uint32_t klast_tail = (uint32_t)min(L - kb_last * kBlk - 1, kBlk - 1) * rs_bytes;
   auto issue_one = [&](int kb_req, int p, int sb) {
-    const int kb = min(kb_req, n_steps - 1);
+    const bool past = kb_req >= kb_last;
+    const int kb = past ? kb_last : kb_req;
     if (p < KI) {
-      const uint32_t last = (uint32_t)min(L - kb * kBlk - 1, kBlk - 1) * rs_bytes;
-      const char* b = uniform_ptr(kbase + (int64_t)kb * kBlk * kv_stride);
+      const uint32_t last = past ? klast_tail : klast_full;
+      const char* b = kbase_b + (past ? (int64_t)kb_last * k_stride : (int64_t)kb_req * k_stride);
       dma16_add(b, min(kroff[p], last + kgran[p]), lkw,
                 (uint32_t)(sb * kBlk * D * 2 + (KTI >= kWaves ? kWaves * p : 0) * 1024));
     } else {

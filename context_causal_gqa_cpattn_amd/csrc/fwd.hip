@@ -156,6 +156,9 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
     const int n_tiles = (kv_end + kBN - 1) / kBN;   // one past the last tile
     const int wave_first_pos = ch.pos0 + row0;
     const int wave_last_pos = wave_first_pos + nrows - 1;
+    // A scalar copy for the per-tile mask decision, so that its two paths (vector work
+    // only) are a scalar branch instead of an exec-mask if/else.
+    const int wave_first_pos_u = rfl(wave_first_pos);
     const int qpos = wave_first_pos + col;  // this lane's query position
 
     // Q^T as B operand: lane holds query `col`, dims [16*st + 8*kg, +8).
@@ -263,14 +266,24 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
       uint32_t lk, lv;
       uint32_t lim[2];  // offset of the last valid row's granule (clamp)
     };
+    // Source offsets without a multiply per tile: tile t's K/V rows start tile_stride * t
+    // bytes after kbase / vbase; tiles past the last re-copy the last one, and only the last
+    // tile can have fewer than kBN valid rows.
+    const int64_t tile_stride = (int64_t)kBN * kv_stride * 2;
+    const int64_t last_off = (int64_t)max(n_tiles - 1, 0) * tile_stride;
+    const uint32_t last_full = (uint32_t)(kBN - 1) * rs_bytes;
+    const uint32_t last_tail = (uint32_t)min(L - max(n_tiles - 1, 0) * kBN - 1, kBN - 1) * rs_bytes;
+    const char* const kbase_b = uniform_ptr(kbase);
+    const char* const vbase_b = uniform_ptr(vbase);
     auto copy_step = [&](int t_next, int buf_next) {
-      const int tsrc = min(t_next, n_tiles - 1);
+      const bool past = t_next >= n_tiles - 1;  // the last tile (or past it: the last again)
+      const int64_t off = past ? last_off : (int64_t)t_next * tile_stride;
       CopyStep c;
-      c.bk = uniform_ptr(kbase + (int64_t)tsrc * kBN * kv_stride);
-      c.bv = uniform_ptr(vbase + (int64_t)tsrc * kBN * kv_stride);
+      c.bk = kbase_b + off;
+      c.bv = vbase_b + off;
       c.lk = lds_addr(lds_k[buf_next]) + (uint32_t)wu * 1024u;  // this wave's first instruction
       c.lv = lds_addr(lds_v[buf_next]) + (uint32_t)wu * 1024u;
-      const uint32_t last = (uint32_t)min(L - tsrc * kBN - 1, kBN - 1) * rs_bytes;
+      const uint32_t last = past ? last_tail : last_full;
 #pragma unroll
       for (int e = 0; e < 2; ++e) c.lim[e] = last + gran[e];
       return c;
@@ -346,7 +359,7 @@ __global__ __launch_bounds__(FwdShape<D>::NW * 64) void attn_fwd_kernel(const At
         // Scale to base 2, bias, mask (diagonal or tail tiles only); tile row max.  The
         // masked and unmasked tiles take separate, wave-uniform paths.
         const bool need_mask = (key0 + kBN > kv_hi) || (key0 < kv_lo) ||
-                               (CAUSAL && key0 + kBN - 1 > wave_first_pos);
+                               (CAUSAL && key0 + kBN - 1 > wave_first_pos_u);
         float mx = -INFINITY;
         if (need_mask) {
           asm volatile("" ::: "memory");
