@@ -187,7 +187,8 @@ __device__ __forceinline__ u32x4 lds16(uint32_t addr) { return *(lds_u32x4_cptr)
 // would displace one dK/dV block per step (96 register moves).  Inline assembly pins
 // their destinations to VGPRs.  A chain accumulates into the same registers (no wait
 // states needed between dependent products of one shape); xdl_fence covers the wait
-// states before VALU reads the results (at least 11 for an 8-pass product; 20 given).
+// states before VALU reads the results (at least 11 after an 8-pass product; 12 given,
+// counted from the fence alone).
 __device__ __forceinline__ f32x16 mfma32_v0(u32x4 a, u32x4 b) {
   f32x16 d;
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
@@ -197,10 +198,10 @@ __device__ __forceinline__ void mfma32_v(f32x16& c, u32x4 a, u32x4 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void xdl_fence(f32x16& x) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x));
+  asm volatile("s_nop 7\n\ts_nop 3" : "+v"(x));
 }
 __device__ __forceinline__ void xdl_fence2(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
+  asm volatile("s_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
 }
 
 // The residue products of one tile, dV^T += dO^T rp and dK^T += Q^T rd for every 32-row
