@@ -513,9 +513,9 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     const int nk = max(0, min(32, L - wkey0));
     const int key = wkey0 + n;  // this lane's key (column of S, dP, dK^T, dV^T)
     const bool key_ok = n < nk && key >= a.kv_lo && key < a.kv_hi;  // in the sequence and the window
-    const bool wave_in_window = wkey0 >= a.kv_lo && wkey0 + 32 <= a.kv_hi;
-    // The same tests from a scalar copy of the wave's first key, for the per-step
-    // wave-level decisions (mask fix-up, dS store), so that they are scalar branches.
+    // The wave-level tests (keys past the sequence end or outside the key window) from a
+    // scalar copy of the wave's first key, for the per-step decisions (mask fix-up, dS
+    // store), so that they are scalar branches.
     const int wkey0_u = wg_key0 + __builtin_amdgcn_readfirstlane(wave) * 32;
     const bool wave_masked_u = min(32, L - wkey0_u) < 32 || wkey0_u < a.kv_lo || wkey0_u + 32 > a.kv_hi;
 
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
     // into the free buffer), for smaller D all at once.  Copy k of a tensor by this wave
     // moves the tile's 1 KB piece i = wave + kWaves k: the lane offsets are fixed.
     constexpr bool SPREAD = D >= 128;
-    constexpr int TI = D * kTq * 2 / 1024 / kWaves;  // copies per wave per tensor
+    constexpr int TI = SPREAD ? D * kTq * 2 / 1024 / kWaves : 1;  // copies per wave per tensor
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     uint32_t voff[SPREAD ? TI : 1];
 #pragma unroll
@@ -720,7 +720,6 @@ __global__ __launch_bounds__(kKvThreads) void dkdv_kernel(const AttnArgs a) {
         float lv[16], dlv[16];
         u32x4 sp[2], sd[2];  // BF16 residues of P and dS (set when flag)
         uint32_t flag = 0;
-        const uint32_t boff = (uint32_t)buf * (2u * TE * 2u);
         u32x4 ring[4];
         ring[0] = ring0[0];
         ring[1] = ring0[1];
